@@ -1,0 +1,224 @@
+"""Pins for the oracle's attention functions (CPU only).
+
+Each check ties the oracle to something other than itself: torch's
+scaled_dot_product_attention (a library routine) in float64, closed forms from
+tests/golden/, and invariants of softmax attention.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _sdpa(q, k, v, G, causal=False, mask=None):
+    """Library routine: torch SDPA in float64 on CPU, KV heads expanded h -> h//G."""
+    q, k, v = (np.array(x, dtype=np.float64) for x in (q, k, v))
+    tq = torch.as_tensor(q, dtype=torch.float64)
+    tk = torch.as_tensor(k, dtype=torch.float64).repeat_interleave(G, dim=1)
+    tv = torch.as_tensor(v, dtype=torch.float64).repeat_interleave(G, dim=1)
+    m = None if mask is None else torch.as_tensor(mask)
+    return torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=m,
+                                                            is_causal=causal).numpy()
+
+
+def test_dense_decode_matches_library_sdpa():
+    B, Hq, Hkv, d, N = 2, 4, 2, 16, 37
+    q, k, v = _rand((B, Hq, d), 1), _rand((B, Hkv, N, d), 2), _rand((B, Hkv, N, d), 3)
+    out, lse, p = oracle.dense_decode(q, k, v)
+    ref = _sdpa(q[:, :, None, :], k, v, Hq // Hkv)[:, :, 0, :]
+    assert np.max(np.abs(out - ref)) < 1e-12
+    assert np.allclose(p.sum(-1), 1.0, atol=1e-13)
+
+
+def test_dense_decode_probabilities_match_library_with_identity_values():
+    # SDPA with V = identity returns the attention matrix itself.
+    B, Hq, Hkv, d, N = 1, 4, 2, 8, 19
+    q, k = _rand((B, Hq, d), 4), _rand((B, Hkv, N, d), 5)
+    eye = np.broadcast_to(np.eye(N), (B, Hkv, N, N))
+    _, _, p = oracle.dense_decode(q, k, eye)
+    ref = _sdpa(q[:, :, None, :], k, eye, Hq // Hkv)[:, :, 0, :]
+    assert np.max(np.abs(p - ref)) < 1e-13
+
+
+def test_decode_closed_form_golden():
+    g = json.load(open(os.path.join(GOLD, "decode_closed_form.json")))
+    q = np.array(g["q"])[None, None, :]
+    k = np.zeros((1, 1, 4, 4))
+    k[0, 0, :, 0] = [math.log(j + 1) for j in range(4)]
+    v = np.array(g["v"], dtype=np.float64)[None, None]
+    out, lse, p = oracle.dense_decode(q, k, v)
+    assert np.allclose(p[0, 0], g["p"], atol=1e-15)
+    assert abs(lse[0, 0] - math.log(10.0)) < 1e-14
+    assert np.allclose(out[0, 0], g["out"], atol=1e-14)
+    pooled = oracle.pool_decode(p, 1)
+    idx = oracle.topk_full_sort(pooled[0, 0], 2)
+    assert idx.tolist() == g["top2"]
+    sp, _ = oracle.sparse_decode(q, k, v, idx[None, None, :])
+    assert np.allclose(sp[0, 0], g["sparse_top2_out"], atol=1e-14)
+
+
+def test_dense_decode_special_cases():
+    q, k, v = _rand((1, 2, 8), 6), _rand((1, 1, 1, 8), 7), _rand((1, 1, 1, 8), 8)
+    out, _, _ = oracle.dense_decode(q, k, v)
+    assert np.allclose(out[0, 0], v[0, 0, 0]) and np.allclose(out[0, 1], v[0, 0, 0])
+    # equal scores (q = 0) give the mean of V
+    v2 = _rand((1, 1, 9, 8), 9)
+    out, _, p = oracle.dense_decode(np.zeros((1, 1, 8)), _rand((1, 1, 9, 8), 10), v2)
+    assert np.allclose(out[0, 0], v2[0, 0].mean(0), atol=1e-15)
+    assert np.allclose(p, 1.0 / 9)
+
+
+def test_pool_decode_mass_and_group_one():
+    B, Hq, Hkv, d, N = 2, 8, 2, 8, 50
+    q, k, v = _rand((B, Hq, d), 11), _rand((B, Hkv, N, d), 12), _rand((B, Hkv, N, d), 13)
+    _, _, p = oracle.dense_decode(q, k, v)
+    pooled = oracle.pool_decode(p, Hkv)
+    assert np.allclose(pooled.sum(-1), Hq // Hkv, atol=1e-12)
+    # group 0 collects exactly heads 0..3 (a wrong head->KV mapping fails this)
+    assert np.allclose(pooled[:, 0], p[:, 0:4].sum(1))
+    # G = 1: Top-k of P is the argsort of the raw logits (softmax is monotone)
+    q1 = _rand((1, 1, d), 14)
+    k1 = _rand((1, 1, N, d), 15)
+    _, _, p1 = oracle.dense_decode(q1, k1, k1)
+    logits = k1[0, 0] @ q1[0, 0]
+    for kk in (1, 5, 17, N):
+        want = np.sort(np.argsort(-logits, kind="stable")[:kk])
+        assert oracle.topk_full_sort(oracle.pool_decode(p1, 1)[0, 0], kk).tolist() == want.tolist()
+
+
+def test_sparse_decode_matches_masked_library_sdpa():
+    B, Hq, Hkv, d, N, K = 2, 4, 2, 8, 40, 11
+    q, k, v = _rand((B, Hq, d), 16), _rand((B, Hkv, N, d), 17), _rand((B, Hkv, N, d), 18)
+    r = np.random.default_rng(19)
+    idx = np.stack([np.stack([np.sort(r.choice(N, K, replace=False)) for _ in range(Hkv)])
+                    for _ in range(B)])
+    head_map = [1, 0]
+    out, _ = oracle.sparse_decode(q, k, v, idx, head_map)
+    mask = np.zeros((B, Hq, 1, N), dtype=bool)
+    for b in range(B):
+        for h in range(Hq):
+            mask[b, h, 0, idx[b, head_map[h // 2]]] = True
+    ref = _sdpa(q[:, :, None, :], k, v, 2, mask=mask)[:, :, 0, :]
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_sparse_decode_full_set_equals_dense_and_k1_picks_row():
+    B, Hq, Hkv, d, N = 1, 4, 2, 16, 33
+    q, k, v = _rand((B, Hq, d), 20), _rand((B, Hkv, N, d), 21), _rand((B, Hkv, N, d), 22)
+    dense, _, _ = oracle.dense_decode(q, k, v)
+    full = np.broadcast_to(np.arange(N), (B, Hkv, N))
+    sp, _ = oracle.sparse_decode(q, k, v, full)
+    assert np.max(np.abs(sp - dense)) < 1e-12
+    # permuting the list changes nothing
+    perm = np.random.default_rng(23).permutation(N)
+    sp2, _ = oracle.sparse_decode(q, k, v, full[..., perm])
+    assert np.max(np.abs(sp2 - dense)) < 1e-12
+    one = np.full((B, Hkv, 1), 7)
+    sp1, _ = oracle.sparse_decode(q, k, v, one)
+    assert np.allclose(sp1[0, 0], v[0, 0, 7]) and np.allclose(sp1[0, 3], v[0, 1, 7])
+
+
+def test_dense_prefill_matches_causal_library_sdpa():
+    B, Hq, Hkv, d, N = 1, 4, 2, 16, 45
+    q, k, v = _rand((B, Hq, N, d), 24), _rand((B, Hkv, N, d), 25), _rand((B, Hkv, N, d), 26)
+    out, lse = oracle.dense_prefill(q, k, v)
+    ref = _sdpa(q, k, v, 2, causal=True)
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_tile_pool_matches_library_probabilities():
+    # P from SDPA with V = identity and a causal mask; pooled = sums over the
+    # tile's rows and the group's heads.
+    B, Hq, Hkv, d, N, tile = 1, 4, 2, 8, 21, 8
+    q, k = _rand((B, Hq, N, d), 27), _rand((B, Hkv, N, d), 28)
+    eye = np.broadcast_to(np.eye(N), (B, Hkv, N, N))
+    P = _sdpa(q, k, eye, 2, causal=True)  # [B,Hq,N,N]
+    rows = oracle.tile_pool(q, k, tile)
+    T = -(-N // tile)
+    for t in range(T):
+        lo, hi = tile * t, min(N, tile * (t + 1))
+        for g in range(Hkv):
+            want = P[0, 2 * g:2 * g + 2, lo:hi, :hi].sum(axis=(0, 1))
+            got = rows[0][t][g]
+            assert got.shape == (hi,)
+            assert np.max(np.abs(got - want)) < 1e-12
+            # mass: every row sums to one
+            assert abs(got.sum() - 2 * (hi - lo)) < 1e-11
+
+
+def test_tile_pool_tile_one_is_per_row_probability():
+    B, Hq, Hkv, d, N = 1, 1, 1, 8, 9
+    q, k, v = _rand((B, Hq, N, d), 29), _rand((B, Hkv, N, d), 30), _rand((B, Hkv, N, d), 31)
+    rows = oracle.tile_pool(q, k, tile=1)
+    for r in range(N):
+        _, _, p = oracle.dense_prefill_rows(q, k, v, 0, 0, [r])
+        assert np.allclose(rows[0][r][0], p[0, : r + 1], atol=1e-15)
+
+
+def test_sparse_prefill_matches_masked_library_sdpa():
+    B, Hq, Hkv, d, N, tile = 1, 4, 2, 8, 37, 8
+    q, k, v = _rand((B, Hq, N, d), 32), _rand((B, Hkv, N, d), 33), _rand((B, Hkv, N, d), 34)
+    T = -(-N // tile)
+    r = np.random.default_rng(35)
+    kmax = 12
+    idx = -np.ones((B, T, Hkv, kmax), dtype=np.int64)
+    for t in range(T):
+        P_t = min(N, tile * (t + 1))
+        kt = min(P_t, kmax)
+        for g in range(Hkv):
+            sel = np.sort(r.choice(P_t, kt, replace=False))
+            # guarantee every row sees at least one key: include key 0
+            if 0 not in sel:
+                sel[0] = 0
+                sel = np.sort(sel)
+            idx[0, t, g, :kt] = sel
+    head_map = [1, 0]
+    out = oracle.sparse_prefill(q, k, v, idx, head_map, tile)
+    mask = np.zeros((B, Hq, N, N), dtype=bool)
+    for h in range(Hq):
+        for rr in range(N):
+            J = idx[0, rr // tile, head_map[h // 2]]
+            J = J[(J >= 0) & (J <= rr)]
+            mask[0, h, rr, J] = True
+    ref = _sdpa(q, k, v, 2, mask=mask)
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_sparse_prefill_full_lists_equal_dense():
+    B, Hq, Hkv, d, N, tile = 1, 2, 1, 8, 20, 8
+    q, k, v = _rand((B, Hq, N, d), 36), _rand((B, Hkv, N, d), 37), _rand((B, Hkv, N, d), 38)
+    T = -(-N // tile)
+    idx = -np.ones((B, T, Hkv, N), dtype=np.int64)
+    for t in range(T):
+        P_t = min(N, tile * (t + 1))
+        idx[0, t, 0, :P_t] = np.arange(P_t)
+    dense, _ = oracle.dense_prefill(q, k, v)
+    sp = oracle.sparse_prefill(q, k, v, idx, [0], tile)
+    assert np.max(np.abs(sp - dense)) < 1e-12
+
+
+def test_anchor_prefill_tiles_zero_and_one_are_dense():
+    # with the prefill k rule (minimum 256, tile 128) tiles 0 and 1 keep every key
+    for t, P in ((0, 128), (1, 256)):
+        assert oracle.prefill_tile_k(t, 32768) == (P, P)
+
+
+def test_oracle_rejects_non_finite():
+    q = np.zeros((1, 1, 4))
+    k = np.zeros((1, 1, 3, 4))
+    k[0, 0, 1, 2] = np.nan
+    with pytest.raises(ValueError):
+        oracle.dense_decode(q, k, k)
+    with pytest.raises(ValueError):
+        oracle.topk_full_sort(np.array([1.0, np.inf]), 1)
