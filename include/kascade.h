@@ -1,0 +1,196 @@
+/*
+ * kascade.h — C ABI of libkascade.so: Kascade cross-layer Top-k sparse
+ * attention (anchor and reuse layers, decode and prefill) on MI355X (gfx950).
+ *
+ * The method is the one described on the pages about the paper "Kascade: A
+ * Practical Sparse Attention Method for Long-Context LLM Inference"
+ * (arXiv 2512.16391).  Citations name the page and its section:
+ *   [Explainer] the 0h-n0.github.io page "論文解説: Kascade — レイヤー間スパーシティ
+ *               再利用による実用的長文脈LLM推論高速化";
+ *   [Abstract]  the paper's abstract (fugumt.com / montaan.com pages).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.   Every array argument is a DEVICE pointer, except `head_map`
+ *             (a HOST array of n_kv_heads int32, validated on the host and
+ *             passed to the kernels by value) and the shape/rule structs.
+ * Ownership.  The caller allocates and frees every buffer, including the
+ *             workspace (size from kascade_workspace_bytes).  The library
+ *             never allocates device memory, never frees, never synchronises.
+ * Streams.    Work is enqueued asynchronously on `stream` (0 = null stream).
+ * Layouts.    K and V caches are [B, Hkv, N_cap, d] addressed through the
+ *             element strides in kascade_shape (rows of d contiguous
+ *             elements).  Queries are [B, Hq, d] (decode) or [B, Hq, N, d]
+ *             (prefill) through the q strides.  Outputs are CONTIGUOUS:
+ *             out [B, Hq, d] / [B, Hq, N, d] in the input dtype, lse
+ *             [B, Hq] / [B, Hq, N] fp32 (natural log).
+ * GQA.        Query head h uses KV head h / (Hq / Hkv).
+ * Scale.      shape.scale == 0 means 1/sqrt(head_dim).
+ * Errors.     Every call returns KASCADE_OK (0) or a negative kascade_status.
+ *             Arguments are validated before anything is launched: on a
+ *             validation error nothing runs and no output is touched.  When a
+ *             launch fails the call returns KASCADE_ERR_HIP, the outputs are
+ *             undefined, and kascade_last_hip_error() (per thread) holds the
+ *             hipError_t.
+ * Determinism. No floating-point atomics: identical inputs give bitwise
+ *             identical outputs.
+ * Supported.  dtype F32 with head_dim 64, dtype BF16 with head_dim 128
+ *             (one 256-byte K/V row in both cases).  Prefill: BF16,
+ *             head_dim 128, tile 128, batch 1..65535, Hq/Hkv in {1,2,4,8}.
+ * Threads.    Calls are thread-safe on distinct streams with distinct
+ *             workspaces.
+ */
+#ifndef KASCADE_H
+#define KASCADE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KASCADE_OK = 0,
+  KASCADE_ERR_NULL = -1,       /* a required pointer is NULL                 */
+  KASCADE_ERR_SHAPE = -2,      /* sizes/strides inconsistent or unsupported  */
+  KASCADE_ERR_DTYPE = -3,      /* dtype x head_dim combination unsupported   */
+  KASCADE_ERR_TOPK = -4,       /* topk outside [1, ctx_len] or bad rule      */
+  KASCADE_ERR_HEADMAP = -5,    /* head_map entry outside [0, n_kv_heads)     */
+  KASCADE_ERR_WORKSPACE = -6,  /* workspace smaller than required            */
+  KASCADE_ERR_HIP = -7,        /* a HIP call failed (see last_hip_error)     */
+  KASCADE_ERR_ARG = -8         /* another argument is out of range           */
+} kascade_status;
+
+typedef enum { KASCADE_F32 = 0, KASCADE_BF16 = 1 } kascade_dtype;
+
+typedef struct kascade_shape {
+  int32_t batch;        /* B                                                */
+  int32_t n_q_heads;    /* Hq                                               */
+  int32_t n_kv_heads;   /* Hkv, divides Hq                                  */
+  int32_t head_dim;     /* d                                                */
+  int32_t ctx_len;      /* N: keys in the cache (decode) / prompt length    */
+  int32_t dtype;        /* kascade_dtype of q, k, v and out                 */
+  float scale;          /* softmax scale, 0 => 1/sqrt(d)                    */
+  int32_t reserved;     /* must be 0                                        */
+  int64_t q_stride_b, q_stride_h, q_stride_n;     /* in elements            */
+  int64_t kv_stride_b, kv_stride_h, kv_stride_n;  /* in elements            */
+} kascade_shape;
+
+/* Prefill per-tile k rule ([Explainer] "Top-k設定", eq. k, with the query tile
+ * of section "実装のポイント"): for tile t the causal prefix is
+ * P_t = min(N, tile*(t+1)) and
+ *   k_t = min(P_t, max(k_min, round_to * floor((P_t*pct + 50*round_to) /
+ *                                               (100*round_to)))),
+ * i.e. pct% of P_t rounded to the nearest multiple of round_to.  The
+ * 32K-prompt workload uses {tile 128, pct 10, round_to 64, k_min 256}. */
+typedef struct kascade_topk_rule {
+  int32_t tile, pct, round_to, k_min;
+} kascade_topk_rule;
+
+/* ---- the four entry points ------------------------------------------- */
+
+/* Anchor-layer decode.  [Explainer] "アンカーレイヤーと再利用レイヤー": an anchor
+ * computes full attention and the Top-k key indices of its post-softmax
+ * distribution; [Abstract]: the selection is exact and head-aware.
+ *   out      [B,Hq,d]   dense attention output (input dtype)
+ *   lse_out  [B,Hq]     fp32 logsumexp of the scaled scores, may be NULL
+ *   topk_idx [B,Hkv,topk] int32: for each KV head g, the topk positions j
+ *            with the largest pooled probability sum_{h in group g} P[b,h,j]
+ *            (ties to the lower j), in ascending order
+ *   pooled_out [B,Hkv,N] fp32 pooled probabilities, may be NULL
+ * Requires 1 <= topk <= N. */
+int kascade_anchor_decode(const kascade_shape* shape, const void* q, const void* k,
+                          const void* v, int32_t topk, void* out, float* lse_out,
+                          int32_t* topk_idx, float* pooled_out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* Reuse-layer decode.  [Explainer] "アンカーレイヤーと再利用レイヤー" (attention
+ * on the preceding anchor's selected keys only) and "ヘッドリマッピング" (each KV
+ * head g of the reuse layer uses the list of anchor KV head head_map[g]).
+ *   anchor_topk_idx [B,Hkv,topk] int32 device: the anchor's lists (any order,
+ *            entries in [0,N); the caller guarantees this)
+ *   head_map [Hkv] int32 HOST array, entries in [0,Hkv)
+ *   out      [B,Hq,d]: for query head h, softmax over the listed keys of
+ *            this layer's K (KV head h/G), renormalised over them, times V. */
+int kascade_reuse_decode(const kascade_shape* shape, const void* q, const void* k,
+                         const void* v, int32_t topk, const int32_t* anchor_topk_idx,
+                         const int32_t* head_map, void* out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/* Anchor-layer prefill (causal).  [Abstract]: tile-level operations in
+ * prefill; [Explainer] "実装のポイント": 128-query tiles.
+ *   out  [B,Hq,N,d] bf16 dense causal attention; lse_out [B,Hq,N] or NULL
+ *   tile_topk_idx [B,T,Hkv,k_max] int32, T = ceil(N/tile), k_max = k of the
+ *        last tile: row (b,t,g) holds the k_t positions j < P_t with the
+ *        largest pooled probability sum over the G heads of group g and the
+ *        rows r of tile t of P[h,r,j] (P = 0 for j > r), ascending, ties to
+ *        the lower j, then -1 up to k_max
+ *   pooled_out: NULL or packed rows, row (b,t,g) at offset
+ *        b*Hkv*S_T + Hkv*tile*t*(t+1)/2 + g*P_t (S_T = sum of all P_t), fp32 */
+int kascade_anchor_prefill(const kascade_shape* shape, const void* q, const void* k,
+                           const void* v, const kascade_topk_rule* rule, void* out,
+                           float* lse_out, int32_t* tile_topk_idx, float* pooled_out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Reuse-layer prefill (causal).  Row r of tile t, query head h attends to
+ * J = { j in anchor_tile_topk_idx[b,t,head_map[h/G], 0:k_t] : j <= r } with a
+ * softmax renormalised over J.  Lists must be ascending with -1 padding, as
+ * written by kascade_anchor_prefill, and every J non-empty (true for the
+ * rule's k_min >= tile).  head_map: HOST [Hkv]. */
+int kascade_reuse_prefill(const kascade_shape* shape, const void* q, const void* k,
+                          const void* v, const kascade_topk_rule* rule,
+                          const int32_t* anchor_tile_topk_idx, const int32_t* head_map,
+                          void* out, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* ---- helpers ----------------------------------------------------------- */
+
+/* op: 0 anchor_decode, 1 reuse_decode, 2 anchor_prefill, 3 reuse_prefill,
+ * 4 dense_decode, 5 dense_prefill.  Returns the workspace bytes the op
+ * needs for this shape (0 if none), or 0 for an invalid op/shape. */
+size_t kascade_workspace_bytes(int op, const kascade_shape* shape, int32_t topk,
+                               const kascade_topk_rule* rule);
+
+/* k_t for a prefix of n keys under `rule` (same integer formula as the
+ * kernels).  Returns -1 if the rule is invalid. */
+int32_t kascade_topk_for_len(int32_t n, const kascade_topk_rule* rule);
+
+/* Exact Top-k of fp32 rows: for each row r of `rows`, the k positions with
+ * the largest scores[r*row_stride + j], j < n, ties to the lower j, written
+ * ascending to idx[r*idx_stride + 0:k].  -0.0 equals +0.0; NaN rows give
+ * unspecified indices.  No workspace. */
+int kascade_topk_select_f32(const float* scores, int64_t row_stride, int32_t rows,
+                            int32_t n, int32_t k, int32_t* idx, int64_t idx_stride,
+                            hipStream_t stream);
+
+/* Dense baselines with the same kernels and layouts: decode = anchor decode
+ * without pooling/selection; prefill = the causal flash pass alone. */
+int kascade_dense_decode(const kascade_shape* shape, const void* q, const void* k,
+                         const void* v, void* out, float* lse_out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+int kascade_dense_prefill(const kascade_shape* shape, const void* q, const void* k,
+                          const void* v, void* out, float* lse_out, hipStream_t stream);
+
+/* Per-kernel timing with HIP events recorded on the launching stream around
+ * every launch of kernel `kernel_id` (ids below) while enabled.  enable()
+ * resets the totals; read() waits for the recorded events and returns the
+ * summed milliseconds and the launch count.  Not thread-safe; meant for
+ * benchmarks. */
+enum {
+  KASCADE_K_DECODE_SPLITK = 0, KASCADE_K_DECODE_COMBINE = 1, KASCADE_K_DECODE_POOL = 2,
+  KASCADE_K_TOPK_SELECT = 3, KASCADE_K_REUSE_DECODE = 4, KASCADE_K_PREFILL_FLASH = 5,
+  KASCADE_K_PREFILL_POOL = 6, KASCADE_K_PREFILL_SPARSE = 7, KASCADE_K_COUNT = 8
+};
+int kascade_kernel_timer_enable(int kernel_id, int enable);
+int kascade_kernel_timer_read(int kernel_id, double* total_ms, int64_t* launches);
+
+const char* kascade_status_str(int status);
+int kascade_last_hip_error(void);
+const char* kascade_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KASCADE_H */

@@ -1,0 +1,548 @@
+// C ABI of libkascade: argument validation, workspace layout, launch
+// sequencing and per-kernel event timing.  Every check happens before the
+// first launch, so a rejected call leaves all outputs untouched.
+#include <math.h>
+#include <mutex>
+#include <string.h>
+#include <vector>
+
+#include "../../include/kascade.h"
+#include "kernels.h"
+
+using namespace kc;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+struct DeviceInfo {
+  bool init = false;
+  int select_cache_cap = 0;
+};
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+int device_setup(DeviceInfo** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return KASCADE_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return KASCADE_ERR_ARG;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.init) {
+    int lds = 0;
+    e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) {
+      g_last_hip_error = (int)e;
+      return KASCADE_ERR_HIP;
+    }
+    // select kernel: 2048-bin histogram + scan scratch + row cache
+    int cap = (int)((lds - (int)topk_select_lds_bytes(0)) / 4);
+    cap = cap > 32768 ? 32768 : cap;
+    cap = cap < 0 ? 0 : (cap & ~1023);
+    e = topk_select_set_max_lds(topk_select_lds_bytes(cap));
+    if (e != hipSuccess) {
+      g_last_hip_error = (int)e;
+      return KASCADE_ERR_HIP;
+    }
+    d.select_cache_cap = cap;
+    d.init = true;
+  }
+  *out = &d;
+  return KASCADE_OK;
+}
+
+// ---- per-kernel event timing ------------------------------------------------
+struct Timer {
+  bool on = false;
+  double total_ms = 0.0;
+  int64_t launches = 0;
+  std::vector<hipEvent_t> pool;   // pairs
+  size_t used = 0;                // pairs recorded since the last drain
+};
+Timer g_timer[KASCADE_K_COUNT];
+constexpr size_t kTimerPairs = 256;
+
+hipError_t timer_drain(Timer& t) {
+  for (size_t i = 0; i < t.used; ++i) {
+    hipError_t e = hipEventSynchronize(t.pool[2 * i + 1]);
+    if (e != hipSuccess) return e;
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, t.pool[2 * i], t.pool[2 * i + 1]);
+    if (e != hipSuccess) return e;
+    t.total_ms += ms;
+    t.launches += 1;
+  }
+  t.used = 0;
+  return hipSuccess;
+}
+
+template <typename F>
+hipError_t timed(int id, hipStream_t s, F&& launch) {
+  Timer& t = g_timer[id];
+  if (!t.on) return launch();
+  if (t.used == kTimerPairs) {
+    hipError_t e = timer_drain(t);
+    if (e != hipSuccess) return e;
+  }
+  hipEvent_t b = t.pool[2 * t.used], en = t.pool[2 * t.used + 1];
+  hipError_t e = hipEventRecord(b, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(en, s);
+  if (e != hipSuccess) return e;
+  t.used += 1;
+  return hipSuccess;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return KASCADE_OK;
+  g_last_hip_error = (int)e;
+  return KASCADE_ERR_HIP;
+}
+
+// ---- validation ---------------------------------------------------------------
+size_t elem_size(int dtype) { return dtype == KASCADE_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_shape(const kascade_shape* s, bool prefill) {
+  if (!s) return KASCADE_ERR_NULL;
+  if (s->reserved != 0) return KASCADE_ERR_ARG;
+  if (s->batch < 1 || s->batch > 65535 || s->n_q_heads < 1 || s->n_kv_heads < 1 ||
+      s->ctx_len < 1)
+    return KASCADE_ERR_SHAPE;
+  if (s->n_kv_heads > kMaxKvHeads || s->n_q_heads % s->n_kv_heads != 0) return KASCADE_ERR_SHAPE;
+  const int G = s->n_q_heads / s->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KASCADE_ERR_SHAPE;
+  if (s->dtype == KASCADE_F32) {
+    if (s->head_dim != 64 || prefill) return KASCADE_ERR_DTYPE;
+  } else if (s->dtype == KASCADE_BF16) {
+    if (s->head_dim != 128) return KASCADE_ERR_DTYPE;
+  } else {
+    return KASCADE_ERR_DTYPE;
+  }
+  if (!(s->scale >= 0.f) || isinf(s->scale)) return KASCADE_ERR_ARG;
+  const int64_t es = (int64_t)elem_size(s->dtype);
+  const int64_t d = s->head_dim;
+  // every row must be 16-byte aligned and rows must not overlap
+  if (s->kv_stride_n < d || s->q_stride_h < (prefill ? 0 : d)) return KASCADE_ERR_SHAPE;
+  if ((s->kv_stride_n * es) % 16 || (s->kv_stride_h * es) % 16 || (s->kv_stride_b * es) % 16 ||
+      (s->q_stride_h * es) % 16 || (s->q_stride_b * es) % 16 || (s->q_stride_n * es) % 16)
+    return KASCADE_ERR_SHAPE;
+  if (s->kv_stride_h < 0 || s->kv_stride_b < 0 || s->q_stride_b < 0 || s->q_stride_n < 0)
+    return KASCADE_ERR_SHAPE;
+  if (s->kv_stride_h < (int64_t)s->ctx_len * s->kv_stride_n && s->n_kv_heads > 1)
+    return KASCADE_ERR_SHAPE;
+  if (prefill && s->q_stride_n < d) return KASCADE_ERR_SHAPE;
+  return KASCADE_OK;
+}
+
+float scale_log2(const kascade_shape* s) {
+  const float sc = s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim);
+  return sc * 1.4426950408889634f;
+}
+
+int check_rule(const kascade_topk_rule* r) {
+  if (!r) return KASCADE_ERR_NULL;
+  if (r->tile != 128 || r->pct < 1 || r->pct > 100 || r->round_to < 1 || r->k_min < 1)
+    return KASCADE_ERR_TOPK;
+  // every causal row must see at least one selected key (k_min >= tile)
+  if (r->k_min < r->tile) return KASCADE_ERR_TOPK;
+  return KASCADE_OK;
+}
+
+int check_head_map(const int32_t* hm, int n_kv, HeadMap* out) {
+  if (!hm) return KASCADE_ERR_NULL;
+  memset(out, 0, sizeof(*out));
+  for (int g = 0; g < n_kv; ++g) {
+    if (hm[g] < 0 || hm[g] >= n_kv) return KASCADE_ERR_HEADMAP;
+    out->m[g] = hm[g];
+  }
+  return KASCADE_OK;
+}
+
+// ---- decode workspace -----------------------------------------------------------
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct DecodePlan {
+  int kps, splits;
+  size_t off_scores, off_part, off_lse2, off_pooled, total;
+};
+
+DecodePlan plan_decode(const kascade_shape* s, int n_keys, bool spill, bool pooled_ws) {
+  DecodePlan p;
+  const int64_t rows = (int64_t)s->batch * s->n_kv_heads;
+  // about 1024 workgroups, 256..4096 keys each
+  int64_t per = (n_keys * rows + 1023) / 1024;
+  per = (per + 255) / 256 * 256;
+  per = per < 256 ? 256 : (per > 4096 ? 4096 : per);
+  p.kps = (int)per;
+  p.splits = (int)((n_keys + per - 1) / per);
+  const int64_t BH = (int64_t)s->batch * s->n_q_heads;
+  size_t off = 0;
+  p.off_scores = off;
+  if (spill) off += align256((size_t)BH * s->ctx_len * 4);
+  p.off_part = off;
+  off += align256((size_t)BH * p.splits * (s->head_dim + 2) * 4);
+  p.off_lse2 = off;
+  off += align256((size_t)BH * 4);
+  p.off_pooled = off;
+  if (pooled_ws) off += align256((size_t)rows * s->ctx_len * 4);
+  p.total = off;
+  return p;
+}
+
+DecodeArgs decode_args(const kascade_shape* s, const void* q, const void* k, const void* v,
+                       int n_keys, const DecodePlan& p, char* ws) {
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.q_sb = s->q_stride_b;
+  a.q_sh = s->q_stride_h;
+  a.kv_sb = s->kv_stride_b;
+  a.kv_sh = s->kv_stride_h;
+  a.kv_sn = s->kv_stride_n;
+  a.B = s->batch;
+  a.Hq = s->n_q_heads;
+  a.Hkv = s->n_kv_heads;
+  a.n_keys = n_keys;
+  a.n_ctx = s->ctx_len;
+  a.scale_log2 = scale_log2(s);
+  a.keys_per_split = p.kps;
+  a.n_splits = p.splits;
+  a.part = reinterpret_cast<float*>(ws + p.off_part);
+  return a;
+}
+
+// ---- prefill workspace -----------------------------------------------------------
+int64_t packed_per_batch(const kascade_shape* s, int tile) {
+  const int T = (s->ctx_len + tile - 1) / tile;
+  return packed_row_offset(T, 0, s->n_kv_heads, tile, s->ctx_len);
+}
+
+struct PrefillPlan {
+  size_t off_lse2, off_pooled, total;
+};
+
+PrefillPlan plan_prefill(const kascade_shape* s, const kascade_topk_rule* r, bool pooled_ws) {
+  PrefillPlan p;
+  size_t off = 0;
+  p.off_lse2 = off;
+  off += align256((size_t)s->batch * s->n_q_heads * s->ctx_len * 4);
+  p.off_pooled = off;
+  if (pooled_ws) off += align256((size_t)s->batch * packed_per_batch(s, r->tile) * 4);
+  p.total = off;
+  return p;
+}
+
+PrefillArgs prefill_args(const kascade_shape* s, const void* q, const void* k, const void* v,
+                         void* out) {
+  PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.q_sb = s->q_stride_b;
+  a.q_sh = s->q_stride_h;
+  a.q_sn = s->q_stride_n;
+  a.kv_sb = s->kv_stride_b;
+  a.kv_sh = s->kv_stride_h;
+  a.kv_sn = s->kv_stride_n;
+  a.B = s->batch;
+  a.Hq = s->n_q_heads;
+  a.Hkv = s->n_kv_heads;
+  a.N = s->ctx_len;
+  a.T = (s->ctx_len + 127) / 128;
+  a.scale_log2 = scale_log2(s);
+  a.out = out;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kascade_version(void) { return "kascade-mi355x 0.1"; }
+
+int kascade_last_hip_error(void) { return g_last_hip_error; }
+
+const char* kascade_status_str(int st) {
+  switch (st) {
+    case KASCADE_OK: return "ok";
+    case KASCADE_ERR_NULL: return "null pointer";
+    case KASCADE_ERR_SHAPE: return "unsupported or inconsistent shape/strides";
+    case KASCADE_ERR_DTYPE: return "unsupported dtype/head_dim";
+    case KASCADE_ERR_TOPK: return "topk out of range or invalid rule";
+    case KASCADE_ERR_HEADMAP: return "head_map entry out of range";
+    case KASCADE_ERR_WORKSPACE: return "workspace too small";
+    case KASCADE_ERR_HIP: return "HIP error";
+    case KASCADE_ERR_ARG: return "invalid argument";
+  }
+  return "unknown status";
+}
+
+int32_t kascade_topk_for_len(int32_t n, const kascade_topk_rule* rule) {
+  if (!rule || rule->pct < 1 || rule->pct > 100 || rule->round_to < 1 || rule->k_min < 1 || n < 0)
+    return -1;
+  return tile_k_for_len(n, rule->pct, rule->round_to, rule->k_min);
+}
+
+size_t kascade_workspace_bytes(int op, const kascade_shape* s, int32_t topk,
+                               const kascade_topk_rule* rule) {
+  const bool prefill = op == 2 || op == 3 || op == 5;
+  if (check_shape(s, prefill) != KASCADE_OK) return 0;
+  switch (op) {
+    case 0: return plan_decode(s, s->ctx_len, true, true).total;
+    case 1: return topk >= 1 ? plan_decode(s, topk, false, false).total : 0;
+    case 4: return plan_decode(s, s->ctx_len, false, false).total;
+    case 2: return check_rule(rule) == KASCADE_OK ? plan_prefill(s, rule, true).total : 0;
+    case 3: return 0;
+    case 5: return 0;
+  }
+  return 0;
+}
+
+int kascade_anchor_decode(const kascade_shape* s, const void* q, const void* k, const void* v,
+                          int32_t topk, void* out, float* lse_out, int32_t* topk_idx,
+                          float* pooled_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(s, false);
+  if (st) return st;
+  if (!q || !k || !v || !out || !topk_idx) return KASCADE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return KASCADE_ERR_ARG;
+  if (topk < 1 || topk > s->ctx_len) return KASCADE_ERR_TOPK;
+  const DecodePlan p = plan_decode(s, s->ctx_len, true, true);
+  if (!ws || ws_bytes < p.total) return KASCADE_ERR_WORKSPACE;
+  DeviceInfo* dev = nullptr;
+  if ((st = device_setup(&dev))) return st;
+  char* w = reinterpret_cast<char*>(ws);
+  DecodeArgs a = decode_args(s, q, k, v, s->ctx_len, p, w);
+  a.scores = reinterpret_cast<float*>(w + p.off_scores);
+  float* lse2 = reinterpret_cast<float*>(w + p.off_lse2);
+  float* pooled = pooled_out ? pooled_out : reinterpret_cast<float*>(w + p.off_pooled);
+  hipError_t e = timed(KASCADE_K_DECODE_SPLITK, stream,
+                       [&] { return launch_decode_splitk(a, s->dtype, false, stream); });
+  if (e != hipSuccess) return hip_status(e);
+  CombineArgs c = {a.part, p.splits, s->batch * s->n_q_heads, out, lse2, lse_out};
+  e = timed(KASCADE_K_DECODE_COMBINE, stream,
+            [&] { return launch_decode_combine(c, s->dtype, stream); });
+  if (e != hipSuccess) return hip_status(e);
+  PoolDecodeArgs pa = {a.scores, lse2, pooled, s->batch, s->n_q_heads, s->n_kv_heads, s->ctx_len};
+  e = timed(KASCADE_K_DECODE_POOL, stream, [&] { return launch_decode_pool(pa, stream); });
+  if (e != hipSuccess) return hip_status(e);
+  SelectArgs sa;
+  memset(&sa, 0, sizeof(sa));
+  sa.src = pooled;
+  sa.row_stride = s->ctx_len;
+  sa.rows = s->batch * s->n_kv_heads;
+  sa.n = s->ctx_len;
+  sa.k = topk;
+  sa.idx = topk_idx;
+  sa.idx_stride = topk;
+  sa.mode = 0;
+  sa.cache_cap = dev->select_cache_cap;
+  e = timed(KASCADE_K_TOPK_SELECT, stream, [&] { return launch_topk_select(sa, stream); });
+  return hip_status(e);
+}
+
+int kascade_reuse_decode(const kascade_shape* s, const void* q, const void* k, const void* v,
+                         int32_t topk, const int32_t* idx, const int32_t* head_map, void* out,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(s, false);
+  if (st) return st;
+  if (!q || !k || !v || !out || !idx) return KASCADE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return KASCADE_ERR_ARG;
+  if (topk < 1 || topk > s->ctx_len) return KASCADE_ERR_TOPK;
+  HeadMap hm;
+  if ((st = check_head_map(head_map, s->n_kv_heads, &hm))) return st;
+  const DecodePlan p = plan_decode(s, topk, false, false);
+  if (!ws || ws_bytes < p.total) return KASCADE_ERR_WORKSPACE;
+  DeviceInfo* dev = nullptr;
+  if ((st = device_setup(&dev))) return st;
+  char* w = reinterpret_cast<char*>(ws);
+  DecodeArgs a = decode_args(s, q, k, v, topk, p, w);
+  a.idx = idx;
+  a.idx_sg = topk;
+  a.idx_sb = (int64_t)s->n_kv_heads * topk;
+  a.hm = hm;
+  hipError_t e = timed(KASCADE_K_REUSE_DECODE, stream,
+                       [&] { return launch_decode_splitk(a, s->dtype, true, stream); });
+  if (e != hipSuccess) return hip_status(e);
+  CombineArgs c = {a.part, p.splits, s->batch * s->n_q_heads, out,
+                   reinterpret_cast<float*>(w + p.off_lse2), nullptr};
+  e = timed(KASCADE_K_DECODE_COMBINE, stream,
+            [&] { return launch_decode_combine(c, s->dtype, stream); });
+  return hip_status(e);
+}
+
+int kascade_dense_decode(const kascade_shape* s, const void* q, const void* k, const void* v,
+                         void* out, float* lse_out, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  int st = check_shape(s, false);
+  if (st) return st;
+  if (!q || !k || !v || !out) return KASCADE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return KASCADE_ERR_ARG;
+  const DecodePlan p = plan_decode(s, s->ctx_len, false, false);
+  if (!ws || ws_bytes < p.total) return KASCADE_ERR_WORKSPACE;
+  DeviceInfo* dev = nullptr;
+  if ((st = device_setup(&dev))) return st;
+  char* w = reinterpret_cast<char*>(ws);
+  DecodeArgs a = decode_args(s, q, k, v, s->ctx_len, p, w);
+  hipError_t e = timed(KASCADE_K_DECODE_SPLITK, stream,
+                       [&] { return launch_decode_splitk(a, s->dtype, false, stream); });
+  if (e != hipSuccess) return hip_status(e);
+  CombineArgs c = {a.part, p.splits, s->batch * s->n_q_heads, out,
+                   reinterpret_cast<float*>(w + p.off_lse2), lse_out};
+  e = timed(KASCADE_K_DECODE_COMBINE, stream,
+            [&] { return launch_decode_combine(c, s->dtype, stream); });
+  return hip_status(e);
+}
+
+int kascade_topk_select_f32(const float* scores, int64_t row_stride, int32_t rows, int32_t n,
+                            int32_t k, int32_t* idx, int64_t idx_stride, hipStream_t stream) {
+  if (!scores || !idx) return KASCADE_ERR_NULL;
+  if (rows < 0 || rows > 2147483647 / 2 || n < 1 || row_stride < n) return KASCADE_ERR_SHAPE;
+  if (k < 1 || k > n || idx_stride < k) return KASCADE_ERR_TOPK;
+  if (rows == 0) return KASCADE_OK;
+  DeviceInfo* dev = nullptr;
+  int st = device_setup(&dev);
+  if (st) return st;
+  SelectArgs sa;
+  memset(&sa, 0, sizeof(sa));
+  sa.src = scores;
+  sa.row_stride = row_stride;
+  sa.rows = rows;
+  sa.n = n;
+  sa.k = k;
+  sa.idx = idx;
+  sa.idx_stride = idx_stride;
+  sa.mode = 0;
+  sa.cache_cap = dev->select_cache_cap;
+  return hip_status(timed(KASCADE_K_TOPK_SELECT, stream,
+                          [&] { return launch_topk_select(sa, stream); }));
+}
+
+int kascade_anchor_prefill(const kascade_shape* s, const void* q, const void* k, const void* v,
+                           const kascade_topk_rule* rule, void* out, float* lse_out,
+                           int32_t* tile_idx, float* pooled_out, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  int st = check_shape(s, true);
+  if (st) return st;
+  if ((st = check_rule(rule))) return st;
+  if (!q || !k || !v || !out || !tile_idx) return KASCADE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return KASCADE_ERR_ARG;
+  const PrefillPlan p = plan_prefill(s, rule, pooled_out == nullptr);
+  if (!ws || ws_bytes < p.total) return KASCADE_ERR_WORKSPACE;
+  DeviceInfo* dev = nullptr;
+  if ((st = device_setup(&dev))) return st;
+  char* w = reinterpret_cast<char*>(ws);
+  PrefillArgs a = prefill_args(s, q, k, v, out);
+  a.lse2 = reinterpret_cast<float*>(w + p.off_lse2);
+  a.lse_out = lse_out;
+  a.pooled = pooled_out ? pooled_out : reinterpret_cast<float*>(w + p.off_pooled);
+  a.packed_per_batch = packed_per_batch(s, rule->tile);
+  hipError_t e = timed(KASCADE_K_PREFILL_FLASH, stream, [&] { return launch_prefill_flash(a, stream); });
+  if (e != hipSuccess) return hip_status(e);
+  e = timed(KASCADE_K_PREFILL_POOL, stream, [&] { return launch_prefill_pool(a, stream); });
+  if (e != hipSuccess) return hip_status(e);
+  SelectArgs sa;
+  memset(&sa, 0, sizeof(sa));
+  sa.src = a.pooled;
+  sa.rows = s->batch * a.T * s->n_kv_heads;
+  sa.idx = tile_idx;
+  sa.idx_stride = tile_k_for_len(s->ctx_len, rule->pct, rule->round_to, rule->k_min);
+  sa.mode = 1;
+  sa.T = a.T;
+  sa.Hkv = s->n_kv_heads;
+  sa.N = s->ctx_len;
+  sa.tile = rule->tile;
+  sa.pct = rule->pct;
+  sa.round_to = rule->round_to;
+  sa.k_min = rule->k_min;
+  sa.packed_per_batch = a.packed_per_batch;
+  sa.cache_cap = dev->select_cache_cap;
+  e = timed(KASCADE_K_TOPK_SELECT, stream, [&] { return launch_topk_select(sa, stream); });
+  return hip_status(e);
+}
+
+int kascade_reuse_prefill(const kascade_shape* s, const void* q, const void* k, const void* v,
+                          const kascade_topk_rule* rule, const int32_t* idx,
+                          const int32_t* head_map, void* out, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int st = check_shape(s, true);
+  if (st) return st;
+  if ((st = check_rule(rule))) return st;
+  if (!q || !k || !v || !out || !idx) return KASCADE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return KASCADE_ERR_ARG;
+  HeadMap hm;
+  if ((st = check_head_map(head_map, s->n_kv_heads, &hm))) return st;
+  DeviceInfo* dev = nullptr;
+  if ((st = device_setup(&dev))) return st;
+  PrefillArgs a = prefill_args(s, q, k, v, out);
+  a.idx = idx;
+  a.k_max = tile_k_for_len(s->ctx_len, rule->pct, rule->round_to, rule->k_min);
+  a.pct = rule->pct;
+  a.round_to = rule->round_to;
+  a.k_min = rule->k_min;
+  a.hm = hm;
+  return hip_status(timed(KASCADE_K_PREFILL_SPARSE, stream,
+                          [&] { return launch_prefill_sparse(a, stream); }));
+}
+
+int kascade_dense_prefill(const kascade_shape* s, const void* q, const void* k, const void* v,
+                          void* out, float* lse_out, hipStream_t stream) {
+  int st = check_shape(s, true);
+  if (st) return st;
+  if (!q || !k || !v || !out) return KASCADE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return KASCADE_ERR_ARG;
+  DeviceInfo* dev = nullptr;
+  if ((st = device_setup(&dev))) return st;
+  PrefillArgs a = prefill_args(s, q, k, v, out);
+  a.lse_out = lse_out;
+  return hip_status(timed(KASCADE_K_PREFILL_FLASH, stream,
+                          [&] { return launch_prefill_flash(a, stream); }));
+}
+
+int kascade_kernel_timer_enable(int id, int enable) {
+  if (id < 0 || id >= KASCADE_K_COUNT) return KASCADE_ERR_ARG;
+  Timer& t = g_timer[id];
+  if (enable) {
+    if (t.pool.empty()) {
+      t.pool.resize(2 * kTimerPairs);
+      for (auto& ev : t.pool) {
+        hipError_t e = hipEventCreate(&ev);
+        if (e != hipSuccess) {
+          t.pool.clear();
+          return hip_status(e);
+        }
+      }
+    }
+    t.used = 0;
+    t.total_ms = 0.0;
+    t.launches = 0;
+  }
+  t.on = enable != 0;
+  return KASCADE_OK;
+}
+
+int kascade_kernel_timer_read(int id, double* total_ms, int64_t* launches) {
+  if (id < 0 || id >= KASCADE_K_COUNT) return KASCADE_ERR_ARG;
+  if (!total_ms || !launches) return KASCADE_ERR_NULL;
+  Timer& t = g_timer[id];
+  hipError_t e = timer_drain(t);
+  if (e != hipSuccess) return hip_status(e);
+  *total_ms = t.total_ms;
+  *launches = t.launches;
+  return KASCADE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Launch-side declarations of the libkascade kernels (host code).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kc {
+
+constexpr int kMaxKvHeads = 64;
+
+struct HeadMap {
+  int32_t m[kMaxKvHeads];
+};
+
+// Split-K decode (dense anchor pass, or gathered reuse pass).
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t q_sb, q_sh;            // query strides (elements)
+  int64_t kv_sb, kv_sh, kv_sn;   // cache strides (elements)
+  int32_t B, Hq, Hkv;
+  int32_t n_keys;                // dense: N; gather: list length (topk)
+  int32_t n_ctx;                 // keys in the cache (gather positions are clamped below it)
+  float scale_log2;              // softmax scale * log2(e)
+  int32_t keys_per_split, n_splits;
+  float* scores;                 // [B,Hq,N] scaled log2-domain scores (anchor) or null
+  float* part;                   // [B,Hq,n_splits,D+2]: m, l, o[D]
+  const int32_t* idx;            // gather: anchor lists [B,Hkv_a,topk]
+  int64_t idx_sb, idx_sg;
+  HeadMap hm;
+};
+
+struct CombineArgs {
+  const float* part;
+  int32_t n_splits, BH;
+  void* out;                     // [B*Hq, D] input dtype
+  float* lse2;                   // [B*Hq] log2-domain lse (workspace), may be null
+  float* lse_out;                // [B*Hq] natural-log lse, may be null
+};
+
+struct PoolDecodeArgs {
+  const float* scores;           // [B,Hq,N]
+  const float* lse2;             // [B,Hq]
+  float* pooled;                 // [B,Hkv,N]
+  int32_t B, Hq, Hkv, N;
+};
+
+// Exact Top-k over rows.  mode 0: fixed n, k per row.  mode 1: prefill tile
+// rows enumerated (b, t, g) with n = P_t, k = k_t from the rule.
+struct SelectArgs {
+  const float* src;
+  int64_t row_stride;            // mode 0
+  int32_t rows;
+  int32_t n, k;                  // mode 0
+  int32_t* idx;
+  int64_t idx_stride;            // mode 0: row stride; mode 1: k_max
+  int32_t mode;
+  int32_t T, Hkv, N, tile, pct, round_to, k_min;   // mode 1
+  int64_t packed_per_batch;      // mode 1: elements of one batch's packed rows
+  int32_t cache_cap;             // rows up to this length are cached in LDS
+};
+
+// Prefill kernels (bf16, d = 128, tile = 128).
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t q_sb, q_sh, q_sn;
+  int64_t kv_sb, kv_sh, kv_sn;
+  int32_t B, Hq, Hkv, N, T;
+  float scale_log2;
+  void* out;                     // [B,Hq,N,128] bf16
+  float* lse2;                   // [B,Hq,N] log2-domain lse (flash writes, pool reads)
+  float* lse_out;                // [B,Hq,N] natural log, may be null
+  float* pooled;                 // packed pooled rows
+  int64_t packed_per_batch;
+  const int32_t* idx;            // sparse: anchor tile lists [B,T,Hkv,k_max]
+  int32_t k_max;
+  int32_t pct, round_to, k_min;  // tile k rule
+  HeadMap hm;
+};
+
+// Launchers: return hipSuccess or the launch error.
+hipError_t launch_decode_splitk(const DecodeArgs& a, int dtype, bool gather, hipStream_t s);
+hipError_t launch_decode_combine(const CombineArgs& a, int dtype, hipStream_t s);
+hipError_t launch_decode_pool(const PoolDecodeArgs& a, hipStream_t s);
+hipError_t launch_topk_select(const SelectArgs& a, hipStream_t s);
+size_t topk_select_lds_bytes(int cache_cap);
+hipError_t topk_select_set_max_lds(size_t bytes);
+hipError_t launch_prefill_flash(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_pool(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_sparse(const PrefillArgs& a, hipStream_t s);
+
+// The per-tile k rule, identical on host and device.
+__host__ __device__ inline int32_t tile_k_for_len(int32_t n, int32_t pct, int32_t round_to,
+                                                  int32_t k_min) {
+  int64_t r = round_to;
+  int64_t tenth = r * (((int64_t)n * pct + 50 * r) / (100 * r));
+  int64_t kk = tenth > k_min ? tenth : k_min;
+  return (int32_t)(kk < n ? kk : n);
+}
+
+// Offset (elements) of packed pooled row (t, g) inside one batch.
+__host__ __device__ inline int64_t packed_row_offset(int32_t t, int32_t g, int32_t Hkv,
+                                                     int32_t tile, int32_t N) {
+  // rows of tiles 0..t-1: Hkv * sum_{u<t} P_u ; P_u = min(N, tile*(u+1))
+  int64_t full = (int64_t)(N / tile);   // tiles whose prefix is tile*(u+1)
+  int64_t tt = t < full ? t : full;
+  int64_t sum = (int64_t)tile * tt * (tt + 1) / 2 + (int64_t)(t - tt) * N;
+  int64_t Pt = (int64_t)tile * (t + 1) < N ? (int64_t)tile * (t + 1) : N;
+  return (int64_t)Hkv * sum + (int64_t)g * Pt;
+}
+
+}  // namespace kc

@@ -1,0 +1,332 @@
+"""ctypes binding of libkascade.so (argument marshalling only).
+
+The functions named ``kascade_*`` mirror the C entry points of
+``include/kascade.h`` one to one: tensors are passed as device pointers
+(``tensor.data_ptr()``), the stream as torch's current HIP stream.  The
+small helpers below them (``anchor_decode`` etc.) only allocate outputs and
+workspace with torch and call those entry points; every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if the
+library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkascade.so")
+
+KASCADE_F32, KASCADE_BF16 = 0, 1
+OP_ANCHOR_DECODE, OP_REUSE_DECODE, OP_ANCHOR_PREFILL, OP_REUSE_PREFILL = 0, 1, 2, 3
+OP_DENSE_DECODE, OP_DENSE_PREFILL = 4, 5
+K_DECODE_SPLITK, K_DECODE_COMBINE, K_DECODE_POOL, K_TOPK_SELECT = 0, 1, 2, 3
+K_REUSE_DECODE, K_PREFILL_FLASH, K_PREFILL_POOL, K_PREFILL_SPARSE = 4, 5, 6, 7
+
+EXPORTS = [
+    "kascade_anchor_decode", "kascade_reuse_decode", "kascade_anchor_prefill",
+    "kascade_reuse_prefill", "kascade_workspace_bytes", "kascade_topk_for_len",
+    "kascade_topk_select_f32", "kascade_dense_decode", "kascade_dense_prefill",
+    "kascade_kernel_timer_enable", "kascade_kernel_timer_read", "kascade_status_str",
+    "kascade_last_hip_error", "kascade_version",
+]
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("ctx_len", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+        ("q_stride_b", ctypes.c_int64), ("q_stride_h", ctypes.c_int64), ("q_stride_n", ctypes.c_int64),
+        ("kv_stride_b", ctypes.c_int64), ("kv_stride_h", ctypes.c_int64), ("kv_stride_n", ctypes.c_int64),
+    ]
+
+
+class TopkRule(ctypes.Structure):
+    _fields_ = [("tile", ctypes.c_int32), ("pct", ctypes.c_int32),
+                ("round_to", ctypes.c_int32), ("k_min", ctypes.c_int32)]
+
+
+PREFILL_RULE = TopkRule(128, 10, 64, 256)
+
+
+class KascadeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = _LIB
+        msg = lib.kascade_status_str(status).decode() if lib else str(status)
+        hip = lib.kascade_last_hip_error() if lib else 0
+        super().__init__("%s failed: %s (status %d, hip error %d)" % (where, msg, status, hip))
+        self.status = status
+
+
+_LIB: Optional[ctypes.CDLL] = None
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_SIGS = {
+    "kascade_anchor_decode": (_i32, [ctypes.POINTER(Shape), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kascade_reuse_decode": (_i32, [ctypes.POINTER(Shape), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kascade_anchor_prefill": (_i32, [ctypes.POINTER(Shape), _vp, _vp, _vp, ctypes.POINTER(TopkRule), _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kascade_reuse_prefill": (_i32, [ctypes.POINTER(Shape), _vp, _vp, _vp, ctypes.POINTER(TopkRule), _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kascade_workspace_bytes": (_sz, [_i32, ctypes.POINTER(Shape), _i32, ctypes.POINTER(TopkRule)]),
+    "kascade_topk_for_len": (_i32, [_i32, ctypes.POINTER(TopkRule)]),
+    "kascade_topk_select_f32": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _i64, _vp]),
+    "kascade_dense_decode": (_i32, [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kascade_dense_prefill": (_i32, [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _vp, _vp]),
+    "kascade_kernel_timer_enable": (_i32, [_i32, _i32]),
+    "kascade_kernel_timer_read": (_i32, [_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
+    "kascade_status_str": (ctypes.c_char_p, [_i32]),
+    "kascade_last_hip_error": (_i32, []),
+    "kascade_version": (ctypes.c_char_p, []),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkascade.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libkascade.so is not built (run __graft_entry__.build() or "
+                               "python -m long_context_anchor_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+# ---------------------------------------------------------------------------
+# raw entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def _p(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream
+
+
+def kascade_anchor_decode(shape, q, k, v, topk, out, lse_out, topk_idx, pooled_out, workspace,
+                          workspace_bytes, stream=None) -> int:
+    return lib().kascade_anchor_decode(ctypes.byref(shape), _p(q), _p(k), _p(v), topk, _p(out),
+                                       _p(lse_out), _p(topk_idx), _p(pooled_out), _p(workspace),
+                                       workspace_bytes, _stream(stream))
+
+
+def kascade_reuse_decode(shape, q, k, v, topk, anchor_topk_idx, head_map, out, workspace,
+                         workspace_bytes, stream=None) -> int:
+    hm = (ctypes.c_int32 * len(head_map))(*[int(x) for x in head_map]) if head_map is not None else None
+    return lib().kascade_reuse_decode(ctypes.byref(shape), _p(q), _p(k), _p(v), topk,
+                                      _p(anchor_topk_idx), ctypes.cast(hm, _vp) if hm is not None else None,
+                                      _p(out), _p(workspace), workspace_bytes, _stream(stream))
+
+
+def kascade_anchor_prefill(shape, q, k, v, rule, out, lse_out, tile_topk_idx, pooled_out,
+                           workspace, workspace_bytes, stream=None) -> int:
+    return lib().kascade_anchor_prefill(ctypes.byref(shape), _p(q), _p(k), _p(v), ctypes.byref(rule),
+                                        _p(out), _p(lse_out), _p(tile_topk_idx), _p(pooled_out),
+                                        _p(workspace), workspace_bytes, _stream(stream))
+
+
+def kascade_reuse_prefill(shape, q, k, v, rule, anchor_tile_topk_idx, head_map, out, workspace,
+                          workspace_bytes, stream=None) -> int:
+    hm = (ctypes.c_int32 * len(head_map))(*[int(x) for x in head_map]) if head_map is not None else None
+    return lib().kascade_reuse_prefill(ctypes.byref(shape), _p(q), _p(k), _p(v), ctypes.byref(rule),
+                                       _p(anchor_tile_topk_idx),
+                                       ctypes.cast(hm, _vp) if hm is not None else None,
+                                       _p(out), _p(workspace), workspace_bytes, _stream(stream))
+
+
+def kascade_workspace_bytes(op, shape, topk=0, rule=None) -> int:
+    return lib().kascade_workspace_bytes(op, ctypes.byref(shape), topk,
+                                         ctypes.byref(rule) if rule is not None else None)
+
+
+def kascade_topk_for_len(n, rule) -> int:
+    return lib().kascade_topk_for_len(n, ctypes.byref(rule))
+
+
+def kascade_topk_select_f32(scores, row_stride, rows, n, k, idx, idx_stride, stream=None) -> int:
+    return lib().kascade_topk_select_f32(_p(scores), row_stride, rows, n, k, _p(idx), idx_stride,
+                                         _stream(stream))
+
+
+def kascade_dense_decode(shape, q, k, v, out, lse_out, workspace, workspace_bytes, stream=None) -> int:
+    return lib().kascade_dense_decode(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(out), _p(lse_out),
+                                      _p(workspace), workspace_bytes, _stream(stream))
+
+
+def kascade_dense_prefill(shape, q, k, v, out, lse_out, stream=None) -> int:
+    return lib().kascade_dense_prefill(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(out), _p(lse_out),
+                                       _stream(stream))
+
+
+def kascade_kernel_timer_enable(kernel_id: int, enable: bool) -> int:
+    return lib().kascade_kernel_timer_enable(kernel_id, 1 if enable else 0)
+
+
+def kascade_kernel_timer_read(kernel_id: int):
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    st = lib().kascade_kernel_timer_read(kernel_id, ctypes.byref(ms), ctypes.byref(n))
+    if st:
+        raise KascadeError(st, "kascade_kernel_timer_read")
+    return ms.value, n.value
+
+
+def kascade_status_str(status: int) -> str:
+    return lib().kascade_status_str(status).decode()
+
+
+def kascade_last_hip_error() -> int:
+    return lib().kascade_last_hip_error()
+
+
+def kascade_version() -> str:
+    return lib().kascade_version().decode()
+
+
+# ---------------------------------------------------------------------------
+# shape marshalling and allocating helpers
+# ---------------------------------------------------------------------------
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return KASCADE_F32
+    if t.dtype == torch.bfloat16:
+        return KASCADE_BF16
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+def make_shape(q: torch.Tensor, k: torch.Tensor, ctx_len: int, scale: float = 0.0) -> Shape:
+    """Shape from q ([B,Hq,d] decode or [B,Hq,N,d] prefill) and the cache k
+    ([B,Hkv,N_cap,d]); strides in elements."""
+    if q.dim() == 3:
+        qsb, qsh, qsn = q.stride(0), q.stride(1), 0
+    else:
+        qsb, qsh, qsn = q.stride(0), q.stride(1), q.stride(2)
+    if q.stride(-1) != 1 or k.stride(-1) != 1:
+        raise ValueError("the head_dim axis must be contiguous")
+    return Shape(q.shape[0], q.shape[1], k.shape[1], q.shape[-1], ctx_len, _dtype_code(q), scale, 0,
+                 qsb, qsh, qsn, k.stride(0), k.stride(1), k.stride(2))
+
+
+def check(status: int, where: str) -> None:
+    if status != 0:
+        raise KascadeError(status, where)
+
+
+def workspace(op: int, shape: Shape, topk: int = 0, rule: Optional[TopkRule] = None,
+              device="cuda") -> torch.Tensor:
+    n = kascade_workspace_bytes(op, shape, topk, rule)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def anchor_decode(q, k, v, topk: int, ctx_len: Optional[int] = None, want_pooled=False, ws=None):
+    """Returns (out [B,Hq,d], lse [B,Hq], idx int32 [B,Hkv,topk], pooled or None)."""
+    N = ctx_len or k.shape[2]
+    sh = make_shape(q, k, N)
+    B, Hq, d = q.shape
+    Hkv = k.shape[1]
+    out = torch.empty((B, Hq, d), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    idx = torch.empty((B, Hkv, topk), dtype=torch.int32, device=q.device)
+    pooled = torch.empty((B, Hkv, N), dtype=torch.float32, device=q.device) if want_pooled else None
+    ws = ws if ws is not None else workspace(OP_ANCHOR_DECODE, sh, topk)
+    check(kascade_anchor_decode(sh, q, k, v, topk, out, lse, idx, pooled, ws, ws.numel()),
+          "kascade_anchor_decode")
+    return out, lse, idx, pooled
+
+
+def reuse_decode(q, k, v, anchor_idx, head_map: Sequence[int], ctx_len: Optional[int] = None, ws=None):
+    N = ctx_len or k.shape[2]
+    sh = make_shape(q, k, N)
+    topk = anchor_idx.shape[-1]
+    out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    ws = ws if ws is not None else workspace(OP_REUSE_DECODE, sh, topk)
+    check(kascade_reuse_decode(sh, q, k, v, topk, anchor_idx, head_map, out, ws, ws.numel()),
+          "kascade_reuse_decode")
+    return out
+
+
+def dense_decode(q, k, v, ctx_len: Optional[int] = None, ws=None):
+    N = ctx_len or k.shape[2]
+    sh = make_shape(q, k, N)
+    out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    ws = ws if ws is not None else workspace(OP_DENSE_DECODE, sh)
+    check(kascade_dense_decode(sh, q, k, v, out, lse, ws, ws.numel()), "kascade_dense_decode")
+    return out, lse
+
+
+def topk_select(scores: torch.Tensor, k: int) -> torch.Tensor:
+    rows, n = scores.shape
+    idx = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+    check(kascade_topk_select_f32(scores, scores.stride(0), rows, n, k, idx, k),
+          "kascade_topk_select_f32")
+    return idx
+
+
+def prefill_k_max(n: int, rule: TopkRule = PREFILL_RULE) -> int:
+    return kascade_topk_for_len(n, rule)
+
+
+def anchor_prefill(q, k, v, rule: TopkRule = PREFILL_RULE, want_pooled=False, ws=None):
+    """Returns (out [B,Hq,N,d], lse [B,Hq,N], tile idx [B,T,Hkv,k_max], pooled or None)."""
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    sh = make_shape(q, k, N)
+    T = -(-N // rule.tile)
+    kmax = prefill_k_max(N, rule)
+    out = torch.empty((B, Hq, N, d), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    idx = torch.empty((B, T, Hkv, kmax), dtype=torch.int32, device=q.device)
+    pooled = None
+    if want_pooled:
+        per_batch = packed_size(N, Hkv, rule.tile)
+        pooled = torch.empty((B, per_batch), dtype=torch.float32, device=q.device)
+    ws = ws if ws is not None else workspace(OP_ANCHOR_PREFILL, sh, 0, rule)
+    check(kascade_anchor_prefill(sh, q, k, v, rule, out, lse, idx, pooled, ws, ws.numel()),
+          "kascade_anchor_prefill")
+    return out, lse, idx, pooled
+
+
+def reuse_prefill(q, k, v, anchor_tile_idx, head_map: Sequence[int], rule: TopkRule = PREFILL_RULE):
+    N = q.shape[2]
+    sh = make_shape(q, k, N)
+    out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    check(kascade_reuse_prefill(sh, q, k, v, rule, anchor_tile_idx, head_map, out, None, 0),
+          "kascade_reuse_prefill")
+    return out
+
+
+def dense_prefill(q, k, v):
+    N = q.shape[2]
+    sh = make_shape(q, k, N)
+    out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    check(kascade_dense_prefill(sh, q, k, v, out, lse), "kascade_dense_prefill")
+    return out, lse
+
+
+def packed_size(n: int, n_kv: int, tile: int = 128) -> int:
+    """Elements of one batch's packed pooled rows: n_kv * sum_t P_t."""
+    T = -(-n // tile)
+    return n_kv * sum(min(n, tile * (t + 1)) for t in range(T))
+
+
+def packed_row(pooled_b: torch.Tensor, t: int, g: int, n: int, n_kv: int, tile: int = 128):
+    """View of packed row (t, g) of one batch's pooled buffer."""
+    off = n_kv * sum(min(n, tile * (u + 1)) for u in range(t))
+    P = min(n, tile * (t + 1))
+    off += g * P
+    return pooled_b[off:off + P]

@@ -1,0 +1,254 @@
+"""GPU parity of the decode path (anchor and reuse layers) and of the exact
+Top-k select, against the fp64 oracle, through the C ABI.
+
+Tolerances: outputs max-abs 1e-4 (fp32 inputs) and 2e-2 (bf16 inputs);
+indices bit-exact when the select sees the same fp32 scores, otherwise every
+element of the symmetric difference must have an oracle pooled score within
+1e-5 (relative) of the oracle's k-th value.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_anchor_amd import configs, synth
+from long_context_anchor_amd import kascade as K
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def np64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def tol_of(dtype):
+    return 1e-4 if dtype == torch.float32 else 2e-2
+
+
+# ---------------------------------------------------------------------------
+# exact select: bit-exact against the full-sort oracle on identical scores
+# ---------------------------------------------------------------------------
+
+SELECT_CASES = [
+    ("normal", 1, 1, 1), ("normal", 3, 7, 3), ("normal", 4, 100, 1), ("normal", 4, 100, 99),
+    ("normal", 2, 1000, 128), ("ties", 3, 1000, 333), ("const", 2, 4097, 100),
+    ("signed", 3, 5000, 2500), ("pooled", 8, 32768, 3264), ("ties", 2, 32768, 3264),
+    ("normal", 2, 40000, 4000), ("pooled", 2, 131072, 13120), ("ties", 1, 131072, 65536),
+    ("normal", 5, 8193, 8192),
+]
+
+
+@pytest.mark.parametrize("kind,rows,n,k", SELECT_CASES)
+def test_select_bit_exact(kind, rows, n, k):
+    say("select", kind, rows, n, k)
+    s = synth.score_rows(seed=n + k, rows=rows, n=n, kind=kind, device=DEV)
+    idx = K.topk_select(s, k)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    host = s.cpu().numpy()
+    for r in range(rows):
+        want = oracle.topk_full_sort(host[r].astype(np.float64), k)
+        assert np.array_equal(got[r], want), (kind, r)
+
+
+def test_select_strided_rows():
+    s = synth.score_rows(seed=3, rows=4, n=3000, kind="ties", device=DEV)
+    view = s[:, :2500]
+    idx = torch.full((4, 300), -7, dtype=torch.int32, device=DEV)
+    K.check(K.kascade_topk_select_f32(view, view.stride(0), 4, 2500, 250, idx, 300), "select")
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for r in range(4):
+        want = oracle.topk_full_sort(s[r, :2500].cpu().numpy().astype(np.float64), 250)
+        assert np.array_equal(got[r, :250], want)
+        assert np.all(got[r, 250:] == -7)   # beyond k untouched
+
+
+# ---------------------------------------------------------------------------
+# dense decode (the anchor's attention pass) on ragged shapes
+# ---------------------------------------------------------------------------
+
+DENSE_CASES = [
+    (torch.float32, 1, 4, 2, 64, 1024), (torch.float32, 2, 8, 8, 64, 257),
+    (torch.float32, 1, 8, 1, 64, 1), (torch.bfloat16, 1, 32, 8, 128, 4099),
+    (torch.bfloat16, 3, 16, 2, 128, 700), (torch.bfloat16, 1, 8, 1, 128, 70000),
+]
+
+
+@pytest.mark.parametrize("dtype,B,Hq,Hkv,d,N", DENSE_CASES)
+def test_dense_decode_parity(dtype, B, Hq, Hkv, d, N):
+    say("dense decode", dtype, B, Hq, Hkv, d, N)
+    g = torch.Generator(device=DEV).manual_seed(N)
+    q = torch.randn((B, Hq, d), generator=g, device=DEV).to(dtype)
+    k = torch.randn((B, Hkv, N, d), generator=g, device=DEV).to(dtype)
+    v = torch.randn((B, Hkv, N, d), generator=g, device=DEV).to(dtype)
+    out, lse = K.dense_decode(q, k, v)
+    torch.cuda.synchronize()
+    ro, rl, _ = oracle.dense_decode(np64(q), np64(k), np64(v))
+    assert np.max(np.abs(np64(out) - ro)) <= tol_of(dtype)
+    assert np.max(np.abs(np64(lse) - rl)) <= 1e-4
+
+
+# ---------------------------------------------------------------------------
+# anchor decode: output, pooled scores, indices
+# ---------------------------------------------------------------------------
+
+def _decode_layer(cfg, layer, n=None, batch=None, n_kv=None):
+    n = n or cfg.ctx_len
+    B = batch or cfg.batch
+    Hkv = n_kv or cfg.n_kv_heads
+    lin = synth.heavy_lineages(cfg.seed, max(layer + 1, 2), Hkv, n,
+                               cfg.n_heavy or int(round(cfg.heavy_frac * n)), cfg.drift)
+    maps = synth.head_maps(cfg.seed, max(layer + 1, 2), cfg.anchors, Hkv, cfg.head_map_kind)
+    heavy = synth.layer_heavy_sets(lin, layer, cfg.anchors, maps)
+    q, k, v = synth.decode_layer(cfg.seed, layer, B, cfg.group * Hkv, Hkv, cfg.head_dim, n, heavy,
+                                 cfg.alpha, cfg.dtype, device=DEV)
+    return q, k, v, maps
+
+
+def _check_anchor(q, k, v, topk, tol):
+    out, lse, idx, pooled = K.anchor_decode(q, k, v, topk, want_pooled=True)
+    torch.cuda.synchronize()
+    ro, rl, rpool, ridx = oracle.anchor_decode(np64(q), np64(k), np64(v), topk)
+    assert np.max(np.abs(np64(out) - ro)) <= tol
+    assert np.max(np.abs(np64(lse) - rl)) <= 1e-4
+    gp = np64(pooled)
+    assert np.max(np.abs(gp - rpool) / np.maximum(rpool, 1e-30)) < 1e-4 or \
+        np.max(np.abs(gp - rpool)) < 1e-6
+    gi = idx.cpu().numpy()
+    B, Hkv = gi.shape[:2]
+    ndiff = 0
+    for b in range(B):
+        for g in range(Hkv):
+            assert np.all(np.diff(gi[b, g]) > 0), "indices ascending and distinct"
+            # bit-exact against a full sort of the GPU's own fp32 pooled row
+            assert np.array_equal(gi[b, g], oracle.topk_full_sort(gp[b, g], topk))
+            ok, nd = oracle.index_sets_agree(gi[b, g], ridx[b, g], rpool[b, g])
+            assert ok, (b, g, nd)
+            ndiff += nd
+    return out, idx, ridx, ndiff
+
+
+def test_anchor_decode_tiny_fp32():
+    cfg = configs.CONFIGS[1]
+    say("anchor decode tiny fp32")
+    q, k, v, _ = _decode_layer(cfg, 0)
+    _check_anchor(q, k, v, cfg.topk, cfg.tol)
+
+
+@pytest.mark.parametrize("N,topk", [(1, 1), (130, 129), (1000, 128), (5000, 4999), (20000, 2048)])
+def test_anchor_decode_ragged_bf16(N, topk):
+    cfg = configs.CONFIGS[2]
+    say("anchor decode ragged", N, topk)
+    q, k, v, _ = _decode_layer(cfg, 0, n=N, batch=2, n_kv=2)
+    _check_anchor(q, k, v, topk, cfg.tol)
+
+
+# ---------------------------------------------------------------------------
+# reuse decode
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,G,N,topk,hm", [
+    (torch.float32, 2, 1024, 128, [0, 1]), (torch.float32, 2, 1024, 128, [1, 0]),
+    (torch.bfloat16, 4, 4096, 3, [2, 2, 0, 1]), (torch.bfloat16, 4, 3000, 3000, [3, 0, 1, 2]),
+    (torch.bfloat16, 1, 777, 333, [0, 0]), (torch.bfloat16, 8, 10000, 1000, [1, 1]),
+])
+def test_reuse_decode_parity(dtype, G, N, topk, hm):
+    say("reuse decode", dtype, G, N, topk, hm)
+    Hkv = len(hm)
+    B = 2
+    d = 64 if dtype == torch.float32 else 128
+    g = torch.Generator(device=DEV).manual_seed(N + topk)
+    q = torch.randn((B, G * Hkv, d), generator=g, device=DEV).to(dtype)
+    k = torch.randn((B, Hkv, N, d), generator=g, device=DEV).to(dtype)
+    v = torch.randn((B, Hkv, N, d), generator=g, device=DEV).to(dtype)
+    idx = synth.random_index_lists(N + topk, B, Hkv, N, topk, device=DEV)
+    out = K.reuse_decode(q, k, v, idx, hm)
+    torch.cuda.synchronize()
+    ref, _ = oracle.sparse_decode(np64(q), np64(k), np64(v), idx.cpu().numpy(), hm)
+    assert np.max(np.abs(np64(out) - ref)) <= tol_of(dtype)
+
+
+def test_reuse_full_list_equals_dense():
+    g = torch.Generator(device=DEV).manual_seed(5)
+    q = torch.randn((1, 8, 128), generator=g, device=DEV).bfloat16()
+    k = torch.randn((1, 2, 2000, 128), generator=g, device=DEV).bfloat16()
+    v = torch.randn((1, 2, 2000, 128), generator=g, device=DEV).bfloat16()
+    full = torch.arange(2000, device=DEV, dtype=torch.int32).expand(1, 2, 2000).contiguous()
+    sp = K.reuse_decode(q, k, v, full, [0, 1])
+    dense, _ = K.dense_decode(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.max(torch.abs(sp.float() - dense.float())).item() <= 1e-2
+
+
+# ---------------------------------------------------------------------------
+# full-size layers of the Llama-shaped 32K workload and the 128K workload
+# ---------------------------------------------------------------------------
+
+def test_llama_32k_anchor_and_reuse_layer():
+    cfg = configs.CONFIGS[2]
+    say("32K anchor layer 0 + reuse layer 1")
+    q, k, v, maps = _decode_layer(cfg, 0)
+    out, idx, ridx, ndiff = _check_anchor(q, k, v, cfg.topk, cfg.tol)
+    say("  index symmetric-difference total", ndiff)
+    q1, k1, v1, _ = _decode_layer(cfg, 1)
+    hm = maps[1]
+    out1 = K.reuse_decode(q1, k1, v1, idx, hm)
+    torch.cuda.synchronize()
+    ref1, _ = oracle.sparse_decode(np64(q1), np64(k1), np64(v1), ridx, hm)
+    assert np.max(np.abs(np64(out1) - ref1)) <= cfg.tol
+
+
+def test_llama_128k_sampled():
+    # full-size launch (B=4, N=131072); the oracle checks batch row 3 and KV heads 0 and 5
+    cfg = configs.CONFIGS[3]
+    say("128K anchor + reuse, sampled rows")
+    q, k, v, maps = _decode_layer(cfg, 0)
+    out, lse, idx, pooled = K.anchor_decode(q, k, v, cfg.topk, want_pooled=True)
+    q1, k1, v1, _ = _decode_layer(cfg, 1)
+    hm = maps[1]
+    out1 = K.reuse_decode(q1, k1, v1, idx, hm)
+    torch.cuda.synchronize()
+    b, G = 3, cfg.group
+    for g in (0, 5):
+        hs = slice(g * G, (g + 1) * G)
+        ro, rl, p = oracle.dense_decode(np64(q[b:b + 1, hs]), np64(k[b:b + 1, g:g + 1]),
+                                        np64(v[b:b + 1, g:g + 1]))
+        assert np.max(np.abs(np64(out[b:b + 1, hs]) - ro)) <= cfg.tol
+        rpool = oracle.pool_decode(p, 1)[0, 0]
+        ridx = oracle.topk_full_sort(rpool, cfg.topk)
+        ok, nd = oracle.index_sets_agree(idx[b, g].cpu().numpy(), ridx, rpool)
+        assert ok, nd
+        # reuse head g2 of layer 1 whose list comes from anchor head g
+        for g2 in [x for x in range(cfg.n_kv_heads) if hm[x] == g]:
+            hs2 = slice(g2 * G, (g2 + 1) * G)
+            lists = ridx[None, None, :]
+            r1, _ = oracle.sparse_decode(np64(q1[b:b + 1, hs2]), np64(k1[b:b + 1, g2:g2 + 1]),
+                                         np64(v1[b:b + 1, g2:g2 + 1]), lists, [0])
+            assert np.max(np.abs(np64(out1[b:b + 1, hs2]) - r1)) <= cfg.tol
+
+
+# ---------------------------------------------------------------------------
+# determinism and workspace independence
+# ---------------------------------------------------------------------------
+
+def test_decode_deterministic_and_workspace_poison_proof():
+    cfg = configs.CONFIGS[2]
+    q, k, v, _ = _decode_layer(cfg, 0, n=20000, batch=1, n_kv=8)
+    sh = K.make_shape(q, k, 20000)
+    ws = K.workspace(K.OP_ANCHOR_DECODE, sh, 2048)
+    o1, l1, i1, p1 = K.anchor_decode(q, k, v, 2048, want_pooled=True, ws=ws)
+    ws.view(torch.float32)[: ws.numel() // 4].fill_(float("nan"))
+    o2, l2, i2, p2 = K.anchor_decode(q, k, v, 2048, want_pooled=True, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2) and torch.equal(i1, i2) and torch.equal(p1, p2)
