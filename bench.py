@@ -1,0 +1,355 @@
+#!/usr/bin/env python3
+"""Benchmark of the Kascade anchor/reuse Top-k attention hot path on one GPU.
+
+One step = one pass of the whole hot path over the Llama-3.1-8B-shaped
+synthetic workloads (32 layers, 32 query / 8 KV heads, head_dim 128, bf16,
+anchors [0, 2, 8, 13, 14], random permutation head maps):
+  * decode at context 32768, batch 1, k = 3264   (anchor + reuse decode)
+  * decode at context 131072, batch 4, k = 13120 (anchor + reuse decode)
+  * prefill of a 32768-token prompt, 128-query tiles, per-tile k (min 256)
+All inputs are resident in HBM before timing starts; every layer has its own
+KV buffers so the 256 MB last-level cache cannot serve them across layers.
+
+Prints ONE JSON line.  `value` is the decode attention time per layer at the
+32K context (the first quantity of the metric); `components` carries the
+128K decode figures (us/layer, GB/s) and the prefill TFLOP/s; `roofline`
+describes the kernel with the largest share of the step time, measured with
+HIP events on its launch stream inside the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attn µs/layer + HBM GB/s at 32k/128k ctx; prefill attn TFLOP/s"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# workload construction (synthetic, seeded)
+# ---------------------------------------------------------------------------
+
+def build_decode(cfg_id, torch, K, synth, configs):
+    cfg = configs.CONFIGS[cfg_id]
+    N, L = cfg.ctx_len, cfg.n_layers
+    lin = synth.heavy_lineages(cfg.seed, L, cfg.n_kv_heads, N, cfg.heavy, cfg.drift)
+    maps = synth.head_maps(cfg.seed, L, cfg.anchors, cfg.n_kv_heads, cfg.head_map_kind)
+    layers = []
+    for l in range(L):
+        q, k, v = synth.decode_layer(cfg.seed, l, cfg.batch, cfg.n_q_heads, cfg.n_kv_heads,
+                                     cfg.head_dim, N, synth.layer_heavy_sets(lin, l, cfg.anchors, maps),
+                                     cfg.alpha, cfg.dtype, device="cuda")
+        layers.append((q, k, v))
+    sh = K.make_shape(layers[0][0], layers[0][1], N)
+    ws_a = K.workspace(K.OP_ANCHOR_DECODE, sh, cfg.topk)
+    ws_r = K.workspace(K.OP_REUSE_DECODE, sh, cfg.topk)
+    idx = {a: torch.empty((cfg.batch, cfg.n_kv_heads, cfg.topk), dtype=torch.int32, device="cuda")
+           for a in cfg.anchors}
+    out = torch.empty_like(layers[0][0])
+    anchor_of = {l: max(a for a in cfg.anchors if a <= l) for l in range(L)}
+
+    def run(kind=None):
+        for l, (q, k, v) in enumerate(layers):
+            if l in cfg.anchors:
+                if kind in (None, "anchor"):
+                    K.check(K.kascade_anchor_decode(sh, q, k, v, cfg.topk, out, None, idx[l], None,
+                                                    ws_a, ws_a.numel()), "anchor_decode")
+            elif kind in (None, "reuse"):
+                K.check(K.kascade_reuse_decode(sh, q, k, v, cfg.topk, idx[anchor_of[l]], maps[l], out,
+                                               ws_r, ws_r.numel()), "reuse_decode")
+
+    e = 2
+    n_anchor = len(cfg.anchors)
+    n_reuse = L - n_anchor
+    io = cfg.batch * cfg.n_q_heads * cfg.head_dim * e * 2 + cfg.batch * cfg.n_kv_heads * cfg.topk * 4
+    bytes_anchor = 2 * cfg.batch * cfg.n_kv_heads * N * cfg.head_dim * e + io
+    bytes_reuse = 2 * cfg.batch * cfg.n_kv_heads * cfg.topk * cfg.head_dim * e + io
+    return dict(cfg=cfg, run=run, n_anchor=n_anchor, n_reuse=n_reuse, bytes_anchor=bytes_anchor,
+                bytes_reuse=bytes_reuse, layers=layers, maps=maps)
+
+
+def build_prefill(torch, K, synth, configs):
+    cfg = configs.CONFIGS[4]
+    N, L = cfg.ctx_len, cfg.n_layers
+    lin = synth.heavy_lineages(cfg.seed, L, cfg.n_kv_heads, N, cfg.heavy, cfg.drift)
+    maps = synth.head_maps(cfg.seed, L, cfg.anchors, cfg.n_kv_heads, cfg.head_map_kind)
+    layers = []
+    for l in range(L):
+        layers.append(synth.prefill_layer(cfg.seed, l, 1, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, N,
+                                          synth.layer_heavy_sets(lin, l, cfg.anchors, maps),
+                                          cfg.alpha, cfg.gamma, cfg.dtype, device="cuda"))
+    rule = K.PREFILL_RULE
+    sh = K.make_shape(layers[0][0], layers[0][1], N)
+    ws = K.workspace(K.OP_ANCHOR_PREFILL, sh, 0, rule)
+    T = N // rule.tile
+    kmax = K.kascade_topk_for_len(N, rule)
+    idx = {a: torch.empty((1, T, cfg.n_kv_heads, kmax), dtype=torch.int32, device="cuda")
+           for a in cfg.anchors}
+    out = torch.empty_like(layers[0][0])
+    anchor_of = {l: max(a for a in cfg.anchors if a <= l) for l in range(L)}
+
+    def run(kind=None):
+        for l, (q, k, v) in enumerate(layers):
+            if l in cfg.anchors:
+                if kind in (None, "anchor"):
+                    K.check(K.kascade_anchor_prefill(sh, q, k, v, rule, out, None, idx[l], None, ws,
+                                                     ws.numel()), "anchor_prefill")
+            elif kind in (None, "reuse"):
+                K.check(K.kascade_reuse_prefill(sh, q, k, v, rule, idx[anchor_of[l]], maps[l], out,
+                                                None, 0), "reuse_prefill")
+
+    d, Hq = cfg.head_dim, cfg.n_q_heads
+    flops_flash = 4.0 * d * Hq * N * (N + 1) / 2
+    flops_pool = 2.0 * d * Hq * N * (N + 1) / 2
+
+    def reuse_flops():
+        # 4*d*sum_{h,r} |J_{h,r}|, counted from the anchors' lists
+        total = 0.0
+        rows = torch.arange(N, device="cuda", dtype=torch.int64).view(T, rule.tile)
+        per_anchor = {}
+        for a, ix in idx.items():
+            cnt = torch.zeros(cfg.n_kv_heads, dtype=torch.float64, device="cuda")
+            for t in range(T):
+                P = min(N, rule.tile * (t + 1))
+                kt = K.kascade_topk_for_len(P, rule)
+                lst = ix[0, t, :, :kt].to(torch.int64).contiguous()        # [Hkv, kt]
+                c = torch.searchsorted(lst, rows[t].expand(cfg.n_kv_heads, -1).contiguous(), right=True)
+                cnt += c.sum(dim=1).double()
+            per_anchor[a] = cnt.cpu().numpy()
+        for l in range(L):
+            if l in cfg.anchors:
+                continue
+            c = per_anchor[anchor_of[l]]
+            total += sum(c[int(maps[l][g])] for g in range(cfg.n_kv_heads)) * cfg.group
+        return 4.0 * d * total
+
+    return dict(cfg=cfg, run=run, n_anchor=len(cfg.anchors), n_reuse=L - len(cfg.anchors),
+                flops_flash=flops_flash, flops_pool=flops_pool, reuse_flops=reuse_flops)
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline on a bounded sample of the 32K decode workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(dec, torch):
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    cfg = dec["cfg"]
+    a = cfg.anchors[0]
+    r = a + 1
+    qa, ka, va = (x.float().cpu().numpy() for x in dec["layers"][a])
+    qr, kr, vr = (x.float().cpu().numpy() for x in dec["layers"][r])
+    t0 = time.perf_counter()
+    reps_a = 0
+    while True:
+        _, _, _, ridx = oracle.anchor_decode(qa, ka, va, cfg.topk)
+        reps_a += 1
+        if time.perf_counter() - t0 > 6.0:
+            break
+    t_anchor = (time.perf_counter() - t0) / reps_a
+    t1 = time.perf_counter()
+    reps_r = 0
+    while True:
+        oracle.reuse_decode(qr, kr, vr, ridx, dec["maps"][r])
+        reps_r += 1
+        if time.perf_counter() - t1 > 4.0:
+            break
+    t_reuse = (time.perf_counter() - t1) / reps_r
+    L = cfg.n_layers
+    per_layer = (dec["n_anchor"] * t_anchor + dec["n_reuse"] * t_reuse) / L
+    return {"value": per_layer * 1e6, "unit": "us/layer", "cores": int(threads), "kind": "oracle",
+            "sample": "32K-context decode: one anchor layer (%d reps) and one reuse layer (%d reps), "
+                      "weighted %d anchor : %d reuse layers; host %s, %d logical cpus" % (
+                          reps_a, reps_r, dec["n_anchor"], dec["n_reuse"], platform.processor() or
+                          platform.machine(), os.cpu_count() or 0),
+            "anchor_s": t_anchor, "reuse_s": t_reuse}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["decode32k", "decode128k", "prefill"], default=None,
+                    help="run one section only (profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_anchor_amd import configs, synth
+    from long_context_anchor_amd import kascade as K
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+    K.lib()  # fails loudly when the HIP library is missing
+    torch.cuda.set_device(0)
+
+    sections = ["decode32k", "decode128k", "prefill"] if args.only is None else [args.only]
+    log("building workloads", sections)
+    t_build = time.perf_counter()
+    work = {}
+    if "decode32k" in sections or not args.no_cpu_baseline:
+        work["decode32k"] = build_decode(2, torch, K, synth, configs)
+    if "decode128k" in sections:
+        work["decode128k"] = build_decode(3, torch, K, synth, configs)
+    if "prefill" in sections:
+        work["prefill"] = build_prefill(torch, K, synth, configs)
+    torch.cuda.synchronize()
+    log("built in %.1f s" % (time.perf_counter() - t_build))
+
+    def step():
+        marks = {}
+        for s in sections:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            work[s]["run"]()
+            e1.record()
+            marks[s] = (e0, e1)
+        return marks
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log("warmup step %d done" % i)
+
+    # pick the kernel with the largest share of one step, then time it live
+    for kid in range(8):
+        K.kascade_kernel_timer_enable(kid, True)
+    step()
+    torch.cuda.synchronize()
+    shares = {kid: K.kascade_kernel_timer_read(kid) for kid in range(8)}
+    for kid in range(8):
+        K.kascade_kernel_timer_enable(kid, False)
+    dom = max(shares, key=lambda k: shares[k][0])
+    log("kernel shares (ms, launches):", {k: (round(v[0], 3), v[1]) for k, v in shares.items()})
+    K.kascade_kernel_timer_enable(dom, True)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    all_marks = [step() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dom_ms, dom_n = K.kascade_kernel_timer_read(dom)
+    K.kascade_kernel_timer_enable(dom, False)
+    log("timed %d steps in %.3f s" % (args.steps, wall))
+
+    sec_ms = {s: float(np.mean([m[s][0].elapsed_time(m[s][1]) for m in all_marks])) for s in sections}
+
+    comps = {}
+    for s in ("decode32k", "decode128k"):
+        if s not in sections:
+            continue
+        w = work[s]
+        L = w["cfg"].n_layers
+        by = w["n_anchor"] * w["bytes_anchor"] + w["n_reuse"] * w["bytes_reuse"]
+        # per-kind breakdown outside the timed steps
+        per = {}
+        for kind, n in (("anchor", w["n_anchor"]), ("reuse", w["n_reuse"])):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 5
+            e0.record()
+            for _ in range(reps):
+                w["run"](kind)
+            e1.record()
+            torch.cuda.synchronize()
+            per[kind] = e0.elapsed_time(e1) / reps / n * 1e3
+        comps[s] = {
+            "us_per_layer": sec_ms[s] * 1e3 / L,
+            "GBps": by / (sec_ms[s] * 1e-3) / 1e9,
+            "hbm_frac": by / (sec_ms[s] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "anchor_us": per["anchor"], "reuse_us": per["reuse"],
+            "anchor_GBps": w["bytes_anchor"] / (per["anchor"] * 1e-6) / 1e9,
+            "reuse_GBps": w["bytes_reuse"] / (per["reuse"] * 1e-6) / 1e9,
+            "context": w["cfg"].ctx_len, "batch": w["cfg"].batch, "topk": w["cfg"].topk,
+        }
+    if "prefill" in sections:
+        w = work["prefill"]
+        rf = w["reuse_flops"]()
+        fl = w["n_anchor"] * (w["flops_flash"] + w["flops_pool"]) + rf
+        per = {}
+        for kind, n in (("anchor", w["n_anchor"]), ("reuse", w["n_reuse"])):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            w["run"](kind)
+            e1.record()
+            torch.cuda.synchronize()
+            per[kind] = e0.elapsed_time(e1) / n
+        comps["prefill32k"] = {
+            "ms": sec_ms["prefill"], "TFLOPs": fl / (sec_ms["prefill"] * 1e-3) / 1e12,
+            "anchor_ms": per["anchor"], "reuse_ms": per["reuse"],
+            "anchor_TFLOPs": (w["flops_flash"] + w["flops_pool"]) / (per["anchor"] * 1e-3) / 1e12,
+            "reuse_TFLOPs": rf / w["n_reuse"] / (per["reuse"] * 1e-3) / 1e12,
+            "mfma_frac": fl / (sec_ms["prefill"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        }
+
+    # roofline of the dominant kernel
+    names = {0: "decode_splitk", 1: "decode_combine", 2: "decode_pool", 3: "topk_select",
+             4: "reuse_decode", 5: "prefill_flash", 6: "prefill_pool", 7: "prefill_sparse"}
+    avg_ms = dom_ms / max(dom_n, 1)
+    roof = {"kernel": names[dom], "launches": dom_n, "avg_ms": avg_ms, "traffic": None}
+    if dom in (5, 6, 7) and "prefill" in sections:
+        w = work["prefill"]
+        if dom == 5:
+            per_launch = w["flops_flash"]
+        elif dom == 6:
+            per_launch = w["flops_pool"]
+        else:
+            per_launch = w["reuse_flops"]() / w["n_reuse"]
+        ach = per_launch / (avg_ms * 1e-3) / 1e12
+        roof.update({"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ach / BF16_PEAK_TFLOPS, "algorithmic_per_launch": per_launch})
+    else:
+        # decode kernels: algorithmic bytes of the launch (cache K+V or gathered rows)
+        s = "decode128k" if "decode128k" in sections else "decode32k"
+        w = work[s]
+        per_launch = w["bytes_reuse"] if dom == 4 else w["bytes_anchor"]
+        ach = per_launch / (avg_ms * 1e-3) / 1e9
+        roof.update({"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "algorithmic_per_launch": per_launch})
+
+    ms_per_step = wall * 1e3 / args.steps
+    value = comps.get("decode32k", {}).get("us_per_layer")
+    line = {
+        "metric": METRIC, "value": value, "unit": "us/layer", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Llama-3.1-8B-shaped attention, 32 layers, 32q/8kv heads, d=128, "
+                               "anchors [0,2,8,13,14]: decode 32K ctx B=1 k=3264 + decode 128K ctx "
+                               "B=4 k=13120 + prefill 32K tokens (tile 128, k_t min 256)",
+                   "sections": sections},
+        "components": comps, "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        line["cpu_baseline"] = cpu_baseline(work["decode32k"], torch)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -52,14 +52,6 @@ KC_INLINE f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& 
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Key position of block row kr: dense keys are kb + kr; gathered keys come
-// from the list.  Returns -1 for rows past the end.
-struct KeySrc {
-  const int32_t* list;   // gather
-  int nkeys;
-  int n_ctx;
-};
-
 // Stage one block of 64 K rows ([key][d], padded) and V^T ([d][key],
 // permuted within 16-key chunks) into LDS.  pos[] holds the block's key
 // positions (-1 = none).  NT threads.
@@ -260,7 +252,8 @@ __global__ __launch_bounds__(256) void k_prefill_attn(const PrefillArgs a) {
 }
 
 // One workgroup = one (query tile, KV head, batch): 4*WH waves; wave w takes
-// the 32-row slice w%4 of the tile for heads (w/4) + WH*i of the group.
+// the 32-row slice w%4 of the tile for heads (w/4) + WH*i of the group, one
+// head at a time (i outer), so a wave holds one head's queries.
 template <int G>
 __global__ __launch_bounds__(256 * (G < 4 ? G : 4)) void k_prefill_pool(const PrefillArgs a) {
   constexpr int WH = G < 4 ? G : 4;          // head lanes of waves
@@ -280,71 +273,67 @@ __global__ __launch_bounds__(256 * (G < 4 ? G : 4)) void k_prefill_pool(const Pr
   const int row0 = t * kTileQ + slice * 32;
   const float c = a.scale_log2;
   const int P = min(N, kTileQ * (t + 1));
-
-  bf16x8_t qf[HPW][8];
-  float lse[HPW][16];
-#pragma unroll
-  for (int hi = 0; hi < HPW; ++hi) {
-    const int h = g * G + hw + WH * hi;
-    const int r = row0 + l32;
-    const char* qp = reinterpret_cast<const char*>(a.q) +
-                     ((int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)min(r, N - 1) * a.q_sn) * 2;
-#pragma unroll
-    for (int ds = 0; ds < 8; ++ds) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (r < N) u = ld16(qp + (ds * 16 + hf * 8) * 2);
-      qf[hi][ds] = as_bf16x8(u);
-    }
-    const float* lp = a.lse2 + ((int64_t)b * a.Hq + h) * N;
-#pragma unroll
-    for (int ri = 0; ri < 16; ++ri) {
-      const int rr = row0 + 8 * (ri >> 2) + 4 * hf + (ri & 3);
-      lse[hi][ri] = rr < N ? lp[rr] : 0.f;
-    }
-  }
   const int64_t row_bytes = a.kv_sn * 2;
   const char* kbase = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh) * 2;
   float* prow = a.pooled + (int64_t)b * a.packed_per_batch + packed_row_offset(t, g, a.Hkv, kTileQ, N);
 
-  for (int kb = 0; kb < P; kb += kKB) {
-    __syncthreads();
-    if (tid < kKB) spos[tid] = (kb + tid < P) ? kb + tid : -1;
-    __syncthreads();
-    stage_kv<NT>(sk, nullptr, spos, kbase, nullptr, row_bytes, false);
-    __syncthreads();
-    const bool need_mask = (kb + kKB - 1 > row0) || (kb + kKB > P) || (row0 + 32 > N);
+  for (int hi = 0; hi < HPW; ++hi) {
+    bf16x8_t qf[8];
+    float lse[16];
+    {
+      const int h = g * G + hw + WH * hi;
+      const int r = row0 + l32;
+      const char* qp = reinterpret_cast<const char*>(a.q) +
+                       ((int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)min(r, N - 1) * a.q_sn) * 2;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      bf16x8_t kf[8];
+      for (int ds = 0; ds < 8; ++ds) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (r < N) u = ld16(qp + (ds * 16 + hf * 8) * 2);
+        qf[ds] = as_bf16x8(u);
+      }
+      const float* lp = a.lse2 + ((int64_t)b * a.Hq + h) * N;
 #pragma unroll
-      for (int ds = 0; ds < 8; ++ds)
-        kf[ds] = as_bf16x8(lds16(sk + (kt * 32 + l32) * kKStride + ds * 16 + hf * 8));
-      const int j = kb + kt * 32 + l32;
-      float cs = 0.f;
+      for (int ri = 0; ri < 16; ++ri) {
+        const int rr = row0 + 8 * (ri >> 2) + 4 * hf + (ri & 3);
+        lse[ri] = rr < N ? lp[rr] : 0.f;
+      }
+    }
+    for (int kb = 0; kb < P; kb += kKB) {
+      __syncthreads();
+      if (tid < kKB) spos[tid] = (kb + tid < P) ? kb + tid : -1;
+      __syncthreads();
+      stage_kv<NT>(sk, nullptr, spos, kbase, nullptr, row_bytes, false);
+      __syncthreads();
+      const bool need_mask = (kb + kKB - 1 > row0) || (kb + kKB > P) || (row0 + 32 > N);
 #pragma unroll
-      for (int hi = 0; hi < HPW; ++hi) {
+      for (int kt = 0; kt < 2; ++kt) {
         f32x16_t acc = f32x16_t{};
 #pragma unroll
-        for (int ds = 0; ds < 8; ++ds) acc = mfma32(qf[hi][ds], kf[ds], acc);
+        for (int ds = 0; ds < 8; ++ds) {
+          const bf16x8_t kf = as_bf16x8(lds16(sk + (kt * 32 + l32) * kKStride + ds * 16 + hf * 8));
+          acc = mfma32(qf[ds], kf, acc);
+        }
+        const int j = kb + kt * 32 + l32;
+        float cs = 0.f;
 #pragma unroll
         for (int ri = 0; ri < 16; ++ri) {
-          float p = exp2f_fast(fmaf(acc[ri], c, -lse[hi][ri]));
+          float p = exp2f_fast(fmaf(acc[ri], c, -lse[ri]));
           if (need_mask) {
             const int rr = row0 + 8 * (ri >> 2) + 4 * hf + (ri & 3);
             p = (j <= rr && rr < N && j < P) ? p : 0.f;
           }
           cs += p;
         }
+        cs += __shfl_xor(cs, 32, 64);
+        if (hf == 0) red[wave][kt * 32 + l32] = cs;
       }
-      cs += __shfl_xor(cs, 32, 64);
-      if (hf == 0) red[wave][kt * 32 + l32] = cs;
-    }
-    __syncthreads();
-    if (tid < kKB && kb + tid < P) {
-      float sum = 0.f;
+      __syncthreads();
+      if (tid < kKB && kb + tid < P) {
+        float sum = hi == 0 ? 0.f : prow[kb + tid];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) sum += red[w][tid];
-      prow[kb + tid] = sum;
+        for (int w = 0; w < NW; ++w) sum += red[w][tid];
+        prow[kb + tid] = sum;
+      }
     }
   }
 }
