@@ -50,6 +50,11 @@ int device_setup(DeviceInfo** out) {
       return KASCADE_ERR_HIP;
     }
     d.select_cache_cap = cap;
+    e = prefill_set_max_lds();
+    if (e != hipSuccess) {
+      g_last_hip_error = (int)e;
+      return KASCADE_ERR_HIP;
+    }
     d.init = true;
   }
   *out = &d;
@@ -182,6 +187,9 @@ DecodePlan plan_decode(const kascade_shape* s, int n_keys, bool spill, bool pool
   int64_t per = (n_keys * rows + 1023) / 1024;
   per = (per + 255) / 256 * 256;
   per = per < 256 ? 256 : (per > 4096 ? 4096 : per);
+  // at most 2048 splits per row (the combine keeps one weight per split in LDS)
+  const int64_t min_per = ((n_keys + 2047) / 2048 + 255) / 256 * 256;
+  per = per < min_per ? min_per : per;
   p.kps = (int)per;
   p.splits = (int)((n_keys + per - 1) / per);
   const int64_t BH = (int64_t)s->batch * s->n_q_heads;
@@ -485,6 +493,9 @@ int kascade_reuse_prefill(const kascade_shape* s, const void* q, const void* k, 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return KASCADE_ERR_ARG;
   HeadMap hm;
   if ((st = check_head_map(head_map, s->n_kv_heads, &hm))) return st;
+  if ((size_t)tile_k_for_len(s->ctx_len, rule->pct, rule->round_to, rule->k_min) >
+      prefill_sparse_max_list())
+    return KASCADE_ERR_SHAPE;
   DeviceInfo* dev = nullptr;
   if ((st = device_setup(&dev))) return st;
   PrefillArgs a = prefill_args(s, q, k, v, out);

@@ -233,32 +233,68 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk(const DecodeArgs a) 
   }
 }
 
-// One workgroup per (batch, query head): merge the splits.
+// One workgroup per (batch, query head): merge the splits.  The split
+// weights 2^(m_s - M) are formed once in LDS; every thread then sums a
+// strided share of the splits for one output column (independent loads).
+constexpr int kCombineThreads = 256;
+constexpr int kMaxSplits = 2048;
+
 template <typename T>
-__global__ __launch_bounds__(128) void k_decode_combine(const CombineArgs a) {
+__global__ __launch_bounds__(kCombineThreads) void k_decode_combine(const CombineArgs a) {
   constexpr int D = Elem<T>::D;
-  const int bh = blockIdx.x, dd = threadIdx.x;
-  if (dd >= D) return;
-  const float* p = a.part + (int64_t)bh * a.n_splits * (D + 2);
-  float M = kNegInf;
-  for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, p[(int64_t)s * (D + 2)]);
-  float L = 0.f, O = 0.f;
-  for (int s = 0; s < a.n_splits; ++s) {
+  constexpr int PARTS = kCombineThreads / D;
+  __shared__ float sw[kMaxSplits];
+  __shared__ float sred[kCombineThreads];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int S = a.n_splits;
+  const float* p = a.part + (int64_t)bh * S * (D + 2);
+
+  float mx = kNegInf;
+  for (int s = tid; s < S; s += kCombineThreads) mx = fmaxf(mx, p[(int64_t)s * (D + 2)]);
+  sred[tid] = mx;
+  __syncthreads();
+  for (int o = kCombineThreads / 2; o > 0; o >>= 1) {
+    if (tid < o) sred[tid] = fmaxf(sred[tid], sred[tid + o]);
+    __syncthreads();
+  }
+  const float M = sred[0];
+  __syncthreads();
+  float lp = 0.f;
+  for (int s = tid; s < S; s += kCombineThreads) {
     const float* ps = p + (int64_t)s * (D + 2);
     const float w = exp2f_fast(ps[0] - M);
-    L = fmaf(ps[1], w, L);
-    O = fmaf(ps[2 + dd], w, O);
+    sw[s] = w;
+    lp = fmaf(ps[1], w, lp);
   }
-  const float r = O / L;
-  if constexpr (sizeof(T) == 2) {
-    reinterpret_cast<uint16_t*>(a.out)[(int64_t)bh * D + dd] = (uint16_t)f32_to_bf16_bits(r);
-  } else {
-    reinterpret_cast<float*>(a.out)[(int64_t)bh * D + dd] = r;
+  sred[tid] = lp;
+  __syncthreads();
+  for (int o = kCombineThreads / 2; o > 0; o >>= 1) {
+    if (tid < o) sred[tid] += sred[tid + o];
+    __syncthreads();
   }
-  if (dd == 0) {
-    const float lse2 = M + log2f_fast(L);
-    if (a.lse2) a.lse2[bh] = lse2;
-    if (a.lse_out) a.lse_out[bh] = lse2 * kLn2;
+  const float L = sred[0];
+  __syncthreads();
+  const int dd = tid % D, part = tid / D;
+  float O = 0.f;
+#pragma unroll 8
+  for (int s = part; s < S; s += PARTS) O = fmaf(p[(int64_t)s * (D + 2) + 2 + dd], sw[s], O);
+  sred[tid] = O;
+  __syncthreads();
+  if (tid < D) {
+    float acc = 0.f;
+#pragma unroll
+    for (int q = 0; q < PARTS; ++q) acc += sred[q * D + tid];
+    const float r = acc / L;
+    if constexpr (sizeof(T) == 2) {
+      reinterpret_cast<uint16_t*>(a.out)[(int64_t)bh * D + tid] = (uint16_t)f32_to_bf16_bits(r);
+    } else {
+      reinterpret_cast<float*>(a.out)[(int64_t)bh * D + tid] = r;
+    }
+    if (tid == 0) {
+      const float lse2 = M + log2f_fast(L);
+      if (a.lse2) a.lse2[bh] = lse2;
+      if (a.lse_out) a.lse_out[bh] = lse2 * kLn2;
+    }
   }
 }
 
@@ -330,10 +366,11 @@ hipError_t launch_decode_splitk(const DecodeArgs& a, int dtype, bool gather, hip
 }
 
 hipError_t launch_decode_combine(const CombineArgs& a, int dtype, hipStream_t s) {
+  if (a.n_splits > kMaxSplits) return hipErrorInvalidValue;
   if (dtype == 1)
-    hipLaunchKernelGGL(k_decode_combine<uint16_t>, dim3(a.BH), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(k_decode_combine<uint16_t>, dim3(a.BH), dim3(kCombineThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(k_decode_combine<float>, dim3(a.BH), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(k_decode_combine<float>, dim3(a.BH), dim3(kCombineThreads), 0, s, a);
   return hipGetLastError();
 }
 

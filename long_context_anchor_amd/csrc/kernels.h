@@ -90,6 +90,8 @@ hipError_t topk_select_set_max_lds(size_t bytes);
 hipError_t launch_prefill_flash(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_pool(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_sparse(const PrefillArgs& a, hipStream_t s);
+size_t prefill_sparse_max_list();
+hipError_t prefill_set_max_lds();
 
 // The per-tile k rule, identical on host and device.
 __host__ __device__ inline int32_t tile_k_for_len(int32_t n, int32_t pct, int32_t round_to,

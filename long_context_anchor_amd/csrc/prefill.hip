@@ -52,63 +52,83 @@ KC_INLINE f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& 
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Stage one block of 64 K rows ([key][d], padded) and V^T ([d][key],
-// permuted within 16-key chunks) into LDS.  pos[] holds the block's key
-// positions (-1 = none).  NT threads.
-template <int NT>
-KC_INLINE void stage_kv(uint16_t* sk, uint16_t* svt, const int32_t* pos, const char* kbase,
-                        const char* vbase, int64_t row_bytes, bool with_v) {
-  const int tid = threadIdx.x;
-  // K: 64 rows x 16 chunks of 16 bytes
+// One block of 64 keys held in registers between its global loads and its
+// LDS store, so the loads of block i+1 are in flight while block i is used.
+// K units: 64 rows x 16 chunks of 16 bytes, (kKB*16)/NT per thread.  V^T
+// units: (16-key chunk, half, 4 d columns): 8 keys x 4 d, 256/NT per thread.
+template <int NT, bool WITH_V>
+struct KvRegs {
+  static constexpr int KU = kKB * 16 / NT;
+  static constexpr int VU = WITH_V ? 256 / NT : 0;
+  uint4 k[KU];
+  uint2 v[VU > 0 ? VU : 1][8];
+
+  // pos(kr) gives the cache row of block row kr, or -1 for none.
+  template <typename PosF>
+  KC_INLINE void load(PosF pos, const char* kbase, const char* vbase, int64_t row_bytes) {
+    const int tid = threadIdx.x;
 #pragma unroll
-  for (int u = tid; u < kKB * 16; u += NT) {
-    const int kr = u >> 4, ch = u & 15;
-    const int p = pos[kr];
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (p >= 0) val = ld16(kbase + (int64_t)p * row_bytes + ch * 16);
-    sts16(sk + kr * kKStride + ch * 8, val);
-  }
-  if (!with_v) return;
-  // V^T: unit = (16-key chunk c4, half hp, 4 d columns dg); 8 keys x 4 d each
-#pragma unroll
-  for (int u = tid; u < 256; u += NT) {
-    const int c4 = u >> 6, hp = (u >> 5) & 1, dg = u & 31;
-    uint2 w[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int kr = c4 * 16 + 4 * hp + (s & 3) + 8 * (s >> 2);
-      const int p = pos[kr];
-      w[s] = make_uint2(0, 0);
-      if (p >= 0) w[s] = *reinterpret_cast<const uint2*>(vbase + (int64_t)p * row_bytes + dg * 8);
+    for (int i = 0; i < KU; ++i) {
+      const int u = tid + i * NT;
+      const int p = pos(u >> 4);
+      k[i] = make_uint4(0, 0, 0, 0);
+      if (p >= 0) k[i] = ld16(kbase + (int64_t)p * row_bytes + (u & 15) * 16);
     }
-    // column e of the 4: element e of every key, packed two keys per word
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      uint4 o;
-      const uint32_t a0 = (e < 2) ? w[0].x : w[0].y, a1 = (e < 2) ? w[1].x : w[1].y;
-      const uint32_t a2 = (e < 2) ? w[2].x : w[2].y, a3 = (e < 2) ? w[3].x : w[3].y;
-      const uint32_t a4 = (e < 2) ? w[4].x : w[4].y, a5 = (e < 2) ? w[5].x : w[5].y;
-      const uint32_t a6 = (e < 2) ? w[6].x : w[6].y, a7 = (e < 2) ? w[7].x : w[7].y;
-      o.x = __builtin_amdgcn_perm(a1, a0, sel);
-      o.y = __builtin_amdgcn_perm(a3, a2, sel);
-      o.z = __builtin_amdgcn_perm(a5, a4, sel);
-      o.w = __builtin_amdgcn_perm(a7, a6, sel);
-      sts16(svt + (dg * 4 + e) * kVStride + c4 * 16 + 8 * hp, o);
+    for (int i = 0; i < VU; ++i) {
+      const int u = tid + i * NT;
+      const int c4 = u >> 6, hp = (u >> 5) & 1, dg = u & 31;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int p = pos(c4 * 16 + 4 * hp + (s & 3) + 8 * (s >> 2));
+        v[i][s] = make_uint2(0, 0);
+        if (p >= 0) v[i][s] = *reinterpret_cast<const uint2*>(vbase + (int64_t)p * row_bytes + dg * 8);
+      }
     }
   }
-}
+
+  // K rows as [key][d] (padded); V^T as [d][key] with the keys of each
+  // 16-key chunk in MFMA B-operand order (see the file comment).
+  KC_INLINE void store(uint16_t* sk, uint16_t* svt) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < KU; ++i) {
+      const int u = tid + i * NT;
+      sts16(sk + (u >> 4) * kKStride + (u & 15) * 8, k[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < VU; ++i) {
+      const int u = tid + i * NT;
+      const int c4 = u >> 6, hp = (u >> 5) & 1, dg = u & 31;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t a[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) a[s] = (e < 2) ? v[i][s].x : v[i][s].y;
+        uint4 o;
+        o.x = __builtin_amdgcn_perm(a[1], a[0], sel);
+        o.y = __builtin_amdgcn_perm(a[3], a[2], sel);
+        o.z = __builtin_amdgcn_perm(a[5], a[4], sel);
+        o.w = __builtin_amdgcn_perm(a[7], a[6], sel);
+        sts16(svt + (dg * 4 + e) * kVStride + c4 * 16 + 8 * hp, o);
+      }
+    }
+  }
+};
 
 struct __align__(16) AttnSmem {
   uint16_t k[kKB * kKStride];
   uint16_t vt[kD * kVStride];
-  int32_t pos[kKB];
 };
 
 // One workgroup = one (query tile, query head, batch); 4 waves x 32 rows.
+// GATHER: the keys are the tile's list for KV head head_map[g] (ascending,
+// staged in LDS once), masked per row by position <= row.
 template <bool GATHER>
-__global__ __launch_bounds__(256) void k_prefill_attn(const PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void k_prefill_attn(const PrefillArgs a) {
   __shared__ AttnSmem sm;
+  extern __shared__ int32_t slist[];
   const int t = a.T - 1 - (int)blockIdx.x;   // longest causal tiles first
   const int h = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.Hkv, g = h / G;
@@ -133,33 +153,36 @@ __global__ __launch_bounds__(256) void k_prefill_attn(const PrefillArgs a) {
   }
   const int P = min(N, kTileQ * (t + 1));
   int nkeys = P;
-  const int32_t* list = nullptr;
   if (GATHER) {
     nkeys = tile_k_for_len(P, a.pct, a.round_to, a.k_min);
-    list = a.idx + ((int64_t)(b * a.T + t) * a.Hkv + a.hm.m[g]) * a.k_max;
+    const int32_t* list = a.idx + ((int64_t)(b * a.T + t) * a.Hkv + a.hm.m[g]) * a.k_max;
+    for (int i = tid; i < nkeys; i += 256) {
+      const int p = list[i];
+      slist[i] = (p >= 0 && p < N) ? p : -1;
+    }
+    __syncthreads();
   }
   const int64_t row_bytes = a.kv_sn * 2;
   const char* kbase = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh) * 2;
   const char* vbase = reinterpret_cast<const char*>(a.v) + ((int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh) * 2;
+  auto pos_of = [&](int kb, int kr) -> int {
+    const int i = kb + kr;
+    if (i >= nkeys) return -1;
+    return GATHER ? slist[i] : i;
+  };
 
   f32x16_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16_t{};
   float m = kNegInf, l = 0.f;
 
+  KvRegs<256, true> regs;
+  regs.load([&](int kr) { return pos_of(0, kr); }, kbase, vbase, row_bytes);
   for (int kb = 0; kb < nkeys; kb += kKB) {
     __syncthreads();   // the previous block's LDS reads are done
-    if (tid < kKB) {
-      int p = -1;
-      if (kb + tid < nkeys) {
-        p = GATHER ? list[kb + tid] : kb + tid;
-        p = (p >= 0 && p < N) ? p : -1;
-      }
-      sm.pos[tid] = p;
-    }
+    regs.store(sm.k, sm.vt);
     __syncthreads();
-    stage_kv<256>(sm.k, sm.vt, sm.pos, kbase, vbase, row_bytes, true);
-    __syncthreads();
+    if (kb + kKB < nkeys) regs.load([&](int kr) { return pos_of(kb + kKB, kr); }, kbase, vbase, row_bytes);
 
     f32x16_t s[2];
 #pragma unroll
@@ -174,7 +197,8 @@ __global__ __launch_bounds__(256) void k_prefill_attn(const PrefillArgs a) {
     // causal mask inside the block (key position > query row) and empty slots
     bool need_mask;
     if (GATHER) {
-      need_mask = (kb + kKB > nkeys) || (sm.pos[kKB - 1] > row0) || (sm.pos[kKB - 1] < 0);
+      const int last = min(nkeys, kb + kKB) - 1;
+      need_mask = (kb + kKB > nkeys) || (slist[last] > row0) || (slist[last] < 0);
     } else {
       need_mask = (kb + kKB - 1 > row0) || (kb + kKB > nkeys);
     }
@@ -184,8 +208,7 @@ __global__ __launch_bounds__(256) void k_prefill_attn(const PrefillArgs a) {
 #pragma unroll
       for (int ri = 0; ri < 16; ++ri) {
         if (need_mask) {
-          const int kr = kt * 32 + 8 * (ri >> 2) + 4 * hf + (ri & 3);
-          const int p = sm.pos[kr];
+          const int p = pos_of(kb, kt * 32 + 8 * (ri >> 2) + 4 * hf + (ri & 3));
           if (p < 0 || p > r) s[kt][ri] = kNegInf;
         }
         mx = fmaxf(mx, s[kt][ri]);
@@ -261,7 +284,6 @@ __global__ __launch_bounds__(256 * (G < 4 ? G : 4)) void k_prefill_pool(const Pr
   constexpr int NT = 256 * WH;
   constexpr int NW = NT / 64;
   __shared__ __align__(16) uint16_t sk[kKB * kKStride];
-  __shared__ int32_t spos[kKB];
   __shared__ float red[NW][kKB];
 
   const int t = a.T - 1 - (int)blockIdx.x;
@@ -298,12 +320,15 @@ __global__ __launch_bounds__(256 * (G < 4 ? G : 4)) void k_prefill_pool(const Pr
         lse[ri] = rr < N ? lp[rr] : 0.f;
       }
     }
+    KvRegs<NT, false> regs;
+    regs.load([&](int kr) { return kr < P ? kr : -1; }, kbase, nullptr, row_bytes);
     for (int kb = 0; kb < P; kb += kKB) {
       __syncthreads();
-      if (tid < kKB) spos[tid] = (kb + tid < P) ? kb + tid : -1;
+      regs.store(sk, nullptr);
       __syncthreads();
-      stage_kv<NT>(sk, nullptr, spos, kbase, nullptr, row_bytes, false);
-      __syncthreads();
+      if (kb + kKB < P)
+        regs.load([&](int kr) { return kb + kKB + kr < P ? kb + kKB + kr : -1; }, kbase, nullptr,
+                  row_bytes);
       const bool need_mask = (kb + kKB - 1 > row0) || (kb + kKB > P) || (row0 + 32 > N);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -345,8 +370,18 @@ hipError_t launch_prefill_flash(const PrefillArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The reuse prefill keeps the tile's key list in dynamic LDS (k_max int32).
+size_t prefill_sparse_max_list() { return 24576; }
+
+hipError_t prefill_set_max_lds() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill_attn<true>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)(prefill_sparse_max_list() * sizeof(int32_t)));
+}
+
 hipError_t launch_prefill_sparse(const PrefillArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_prefill_attn<true>, dim3(a.T, a.Hq, a.B), dim3(256), 0, s, a);
+  const size_t lds = (size_t)a.k_max * sizeof(int32_t);
+  hipLaunchKernelGGL(k_prefill_attn<true>, dim3(a.T, a.Hq, a.B), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 

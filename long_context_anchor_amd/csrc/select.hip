@@ -24,6 +24,7 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kHistBins = 2048;
 constexpr int kRun = 8;   // contiguous elements per thread in the compaction pass
+constexpr int kBatch = 8; // independent loads in flight per thread in the scans
 
 struct RowGeom {
   const float* src;
@@ -105,7 +106,20 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const SelectArgs a)
   }
   const bool cached = n <= a.cache_cap;
   if (cached) {
-    for (int j = tid; j < n; j += kSelThreads) cache[j] = f32_order_key(g.src[j]);
+    // kBatch independent loads in flight per thread
+    for (int base = 0; base < n; base += kSelThreads * kBatch) {
+      float v[kBatch];
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        const int j = base + e * kSelThreads + tid;
+        v[e] = j < n ? g.src[j] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        const int j = base + e * kSelThreads + tid;
+        if (j < n) cache[j] = f32_order_key(v[e]);
+      }
+    }
   }
 
   uint32_t prefix = 0;
@@ -118,10 +132,19 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const SelectArgs a)
     const int hs = sh + nbits;                 // bits above this digit
     for (int i = tid; i < kHistBins; i += kSelThreads) hist[i] = 0;
     __syncthreads();
-    for (int j = tid; j < n; j += kSelThreads) {
-      const uint32_t key = cached ? cache[j] : f32_order_key(g.src[j]);
-      const bool match = (pass == 0) || ((key >> hs) == prefix);
-      if (match) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1u);
+    for (int base = 0; base < n; base += kSelThreads * kBatch) {
+      uint32_t kk[kBatch];
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        const int j = base + e * kSelThreads + tid;
+        kk[e] = j < n ? (cached ? cache[j] : f32_order_key(g.src[j])) : 0u;
+      }
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        const int j = base + e * kSelThreads + tid;
+        const bool match = j < n && ((pass == 0) || ((kk[e] >> hs) == prefix));
+        if (match) atomicAdd(&hist[(kk[e] >> sh) & (nb - 1)], 1u);
+      }
     }
     __syncthreads();
     // thread tid owns bins (from the top) 2*tid and 2*tid+1 of the reversed order
