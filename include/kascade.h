@@ -34,6 +34,8 @@
  *             hipError_t.
  * Determinism. No floating-point atomics: identical inputs give bitwise
  *             identical outputs.
+ * Workspace.  Scratch only: no contents carry over between calls, any
+ *             initial contents are fine.
  * Supported.  dtype F32 with head_dim 64, dtype BF16 with head_dim 128
  *             (one 256-byte K/V row in both cases).  Prefill: BF16,
  *             head_dim 128, tile 128, batch 1..65535, Hq/Hkv in {1,2,4,8}.

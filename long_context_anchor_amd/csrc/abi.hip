@@ -15,6 +15,7 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
+
 constexpr int kMaxDevices = 64;
 struct DeviceInfo {
   bool init = false;
@@ -177,7 +178,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct DecodePlan {
   int kps, splits;
-  size_t off_scores, off_part, off_lse2, off_pooled, total;
+  size_t off_hist, off_scores, off_part, off_lse2, off_pooled, total;
 };
 
 DecodePlan plan_decode(const kascade_shape* s, int n_keys, bool spill, bool pooled_ws) {
@@ -194,6 +195,8 @@ DecodePlan plan_decode(const kascade_shape* s, int n_keys, bool spill, bool pool
   p.splits = (int)((n_keys + per - 1) / per);
   const int64_t BH = (int64_t)s->batch * s->n_q_heads;
   size_t off = 0;
+  p.off_hist = off;
+  if (spill) off += align256((size_t)rows * 2048 * 4);
   p.off_scores = off;
   if (spill) off += align256((size_t)BH * s->ctx_len * 4);
   p.off_part = off;
@@ -333,6 +336,7 @@ int kascade_anchor_decode(const kascade_shape* s, const void* q, const void* k, 
   char* w = reinterpret_cast<char*>(ws);
   DecodeArgs a = decode_args(s, q, k, v, s->ctx_len, p, w);
   a.scores = reinterpret_cast<float*>(w + p.off_scores);
+  a.hist0 = reinterpret_cast<uint32_t*>(w + p.off_hist);
   float* lse2 = reinterpret_cast<float*>(w + p.off_lse2);
   float* pooled = pooled_out ? pooled_out : reinterpret_cast<float*>(w + p.off_pooled);
   hipError_t e = timed(KASCADE_K_DECODE_SPLITK, stream,
@@ -342,7 +346,8 @@ int kascade_anchor_decode(const kascade_shape* s, const void* q, const void* k, 
   e = timed(KASCADE_K_DECODE_COMBINE, stream,
             [&] { return launch_decode_combine(c, s->dtype, stream); });
   if (e != hipSuccess) return hip_status(e);
-  PoolDecodeArgs pa = {a.scores, lse2, pooled, s->batch, s->n_q_heads, s->n_kv_heads, s->ctx_len};
+  PoolDecodeArgs pa = {a.scores, lse2, pooled, a.hist0, s->batch, s->n_q_heads, s->n_kv_heads,
+                       s->ctx_len};
   e = timed(KASCADE_K_DECODE_POOL, stream, [&] { return launch_decode_pool(pa, stream); });
   if (e != hipSuccess) return hip_status(e);
   SelectArgs sa;
@@ -356,6 +361,7 @@ int kascade_anchor_decode(const kascade_shape* s, const void* q, const void* k, 
   sa.idx_stride = topk;
   sa.mode = 0;
   sa.cache_cap = dev->select_cache_cap;
+  sa.hist0 = a.hist0;
   e = timed(KASCADE_K_TOPK_SELECT, stream, [&] { return launch_topk_select(sa, stream); });
   return hip_status(e);
 }

@@ -24,16 +24,14 @@ KC_INLINE float log2f_fast(float x) { return __builtin_amdgcn_logf(x); }
 // bf16 <-> fp32.  bf16 is the high half of an fp32 word.
 KC_INLINE float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 KC_INLINE float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-// fp32 -> bf16 round to nearest even (NaN kept quiet).
-KC_INLINE uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// fp32 -> bf16, round to nearest even, on the hardware converter
+// (v_cvt_pk_bf16_f32).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 KC_INLINE uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const f32x2_t x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
 }
+KC_INLINE uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.f) & 0xFFFFu; }
 
 // dot of two bf16 pairs accumulated in fp32 (v_dot2c_f32_bf16).
 KC_INLINE float dot2_bf16(uint32_t a, uint32_t b, float c) {

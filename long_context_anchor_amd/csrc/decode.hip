@@ -87,6 +87,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk(const DecodeArgs a) 
   const int k0 = split * a.keys_per_split;
   const int k1 = min(a.n_keys, k0 + a.keys_per_split);
 
+  if (a.hist0 && split == 0) {
+    uint32_t* h0 = a.hist0 + ((int64_t)b * a.Hkv + g) * 2048;
+    for (int i = tid; i < 2048; i += kThreads) h0[i] = 0u;
+  }
   if (GATHER) {
     const int32_t* list = a.idx + (int64_t)b * a.idx_sb + (int64_t)a.hm.m[g] * a.idx_sg;
     for (int i = tid; i < k1 - k0; i += kThreads) s_list[i] = list[k0 + i];
@@ -298,12 +302,16 @@ __global__ __launch_bounds__(kCombineThreads) void k_decode_combine(const Combin
   }
 }
 
-// pooled[b,g,j] = sum over the G heads h of group g of 2^(s[b,h,j] - lse2[b,h]).
+// pooled[b,g,j] = sum over the G heads h of group g of 2^(s[b,h,j] - lse2[b,h]),
+// plus the row's histogram of key bits 31..21 (the select kernel's first
+// digit), counted in LDS and added to the row's global histogram.
 template <int G>
 __global__ __launch_bounds__(256) void k_decode_pool(const PoolDecodeArgs a) {
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int j = (blockIdx.x * 256 + threadIdx.x) * 4;
-  if (j >= a.N) return;
+  __shared__ uint32_t sh[2048];
+  const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  for (int i = tid; i < 2048; i += 256) sh[i] = 0u;
+  __syncthreads();
+  const int j = (blockIdx.x * 256 + tid) * 4;
   float lse[G];
   const float* sp[G];
 #pragma unroll
@@ -313,29 +321,45 @@ __global__ __launch_bounds__(256) void k_decode_pool(const PoolDecodeArgs a) {
     sp[hh] = a.scores + bh * a.N;
   }
   float* out = a.pooled + ((int64_t)b * a.Hkv + g) * a.N;
-  if (j + 4 <= a.N && (a.N & 3) == 0) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (j < a.N) {
+    if (j + 4 <= a.N && (a.N & 3) == 0) {
+      float4 s4[G];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float4 s = *reinterpret_cast<const float4*>(sp[hh] + j);
-      acc.x += exp2f_fast(s.x - lse[hh]);
-      acc.y += exp2f_fast(s.y - lse[hh]);
-      acc.z += exp2f_fast(s.z - lse[hh]);
-      acc.w += exp2f_fast(s.w - lse[hh]);
-    }
-    *reinterpret_cast<float4*>(out + j) = acc;
-  } else {
-    for (int jj = j; jj < min(a.N, j + 4); ++jj) {
-      float acc = 0.f;
+      for (int hh = 0; hh < G; ++hh) s4[hh] = *reinterpret_cast<const float4*>(sp[hh] + j);
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) acc += exp2f_fast(sp[hh][jj] - lse[hh]);
-      out[jj] = acc;
+      for (int hh = 0; hh < G; ++hh) {
+        acc.x += exp2f_fast(s4[hh].x - lse[hh]);
+        acc.y += exp2f_fast(s4[hh].y - lse[hh]);
+        acc.z += exp2f_fast(s4[hh].z - lse[hh]);
+        acc.w += exp2f_fast(s4[hh].w - lse[hh]);
+      }
+      *reinterpret_cast<float4*>(out + j) = acc;
+      atomicAdd(&sh[f32_order_key(acc.x) >> 21], 1u);
+      atomicAdd(&sh[f32_order_key(acc.y) >> 21], 1u);
+      atomicAdd(&sh[f32_order_key(acc.z) >> 21], 1u);
+      atomicAdd(&sh[f32_order_key(acc.w) >> 21], 1u);
+    } else {
+      for (int jj = j; jj < min(a.N, j + 4); ++jj) {
+        float acc = 0.f;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) acc += exp2f_fast(sp[hh][jj] - lse[hh]);
+        out[jj] = acc;
+        atomicAdd(&sh[f32_order_key(acc) >> 21], 1u);
+      }
     }
+  }
+  __syncthreads();
+  uint32_t* h0 = a.hist0 + ((int64_t)b * a.Hkv + g) * 2048;
+  for (int i = tid; i < 2048; i += 256) {
+    const uint32_t c = sh[i];
+    if (c) atomicAdd(&h0[i], c);
   }
 }
 
 template <typename T, int G>
 hipError_t launch_splitk_t(const DecodeArgs& a, bool gather, hipStream_t s) {
+  if (a.n_splits > kMaxSplits || a.n_splits < 1) return hipErrorInvalidValue;
   dim3 grid(a.n_splits, a.Hkv, a.B);
   if (gather) {
     size_t lds = (size_t)a.keys_per_split * sizeof(int32_t);

@@ -28,6 +28,7 @@ struct DecodeArgs {
   const int32_t* idx;            // gather: anchor lists [B,Hkv_a,topk]
   int64_t idx_sb, idx_sg;
   HeadMap hm;
+  uint32_t* hist0;               // [B*Hkv][2048] zeroed here for the pooling kernel, or null
 };
 
 struct CombineArgs {
@@ -42,6 +43,7 @@ struct PoolDecodeArgs {
   const float* scores;           // [B,Hq,N]
   const float* lse2;             // [B,Hq]
   float* pooled;                 // [B,Hkv,N]
+  uint32_t* hist0;               // [B*Hkv][2048]: counts of key bits 31..21 of pooled
   int32_t B, Hq, Hkv, N;
 };
 
@@ -58,6 +60,7 @@ struct SelectArgs {
   int32_t T, Hkv, N, tile, pct, round_to, k_min;   // mode 1
   int64_t packed_per_batch;      // mode 1: elements of one batch's packed rows
   int32_t cache_cap;             // rows up to this length are cached in LDS
+  const uint32_t* hist0;         // [rows][2048] digit-0 histograms, or null
 };
 
 // Prefill kernels (bf16, d = 128, tile = 128).

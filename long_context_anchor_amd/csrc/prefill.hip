@@ -71,8 +71,9 @@ struct KvRegs {
     for (int i = 0; i < KU; ++i) {
       const int u = tid + i * NT;
       const int p = pos(u >> 4);
-      k[i] = make_uint4(0, 0, 0, 0);
-      if (p >= 0) k[i] = ld16(kbase + (int64_t)p * row_bytes + (u & 15) * 16);
+      // always load (row 0 stands in for a missing row), then zero: no branch
+      const uint4 x = ld16(kbase + (int64_t)(p < 0 ? 0 : p) * row_bytes + (u & 15) * 16);
+      k[i] = p < 0 ? make_uint4(0, 0, 0, 0) : x;
     }
 #pragma unroll
     for (int i = 0; i < VU; ++i) {
@@ -81,8 +82,9 @@ struct KvRegs {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int p = pos(c4 * 16 + 4 * hp + (s & 3) + 8 * (s >> 2));
-        v[i][s] = make_uint2(0, 0);
-        if (p >= 0) v[i][s] = *reinterpret_cast<const uint2*>(vbase + (int64_t)p * row_bytes + dg * 8);
+        const uint2 x =
+            *reinterpret_cast<const uint2*>(vbase + (int64_t)(p < 0 ? 0 : p) * row_bytes + dg * 8);
+        v[i][s] = p < 0 ? make_uint2(0, 0) : x;
       }
     }
   }
@@ -132,7 +134,8 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(const PrefillArgs a) {
   const int t = a.T - 1 - (int)blockIdx.x;   // longest causal tiles first
   const int h = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.Hkv, g = h / G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int l32 = lane & 31, hf = lane >> 5;
   const int N = a.N;
   const int row0 = t * kTileQ + wave * 32;
@@ -195,33 +198,46 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(const PrefillArgs a) {
       }
     }
     // causal mask inside the block (key position > query row) and empty slots
+    // (a scalar, wave-uniform decision; the masked path is branch-free)
     bool need_mask;
     if (GATHER) {
-      const int last = min(nkeys, kb + kKB) - 1;
-      need_mask = (kb + kKB > nkeys) || (slist[last] > row0) || (slist[last] < 0);
+      const int last = __builtin_amdgcn_readfirstlane(slist[min(nkeys, kb + kKB) - 1]);
+      need_mask = (kb + kKB > nkeys) || (last > row0) || (last < 0);
     } else {
       need_mask = (kb + kKB - 1 > row0) || (kb + kKB > nkeys);
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int ri = 0; ri < 16; ++ri) {
+          const int kk = kb + kt * 32 + 8 * (ri >> 2) + 4 * hf + (ri & 3);
+          int p = GATHER ? slist[min(kk, nkeys - 1)] : kk;
+          p = kk < nkeys ? p : -1;
+          s[kt][ri] = (p < 0 || p > r) ? kNegInf : s[kt][ri];
+        }
+      }
     }
     float mx = kNegInf;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int ri = 0; ri < 16; ++ri) {
-        if (need_mask) {
-          const int p = pos_of(kb, kt * 32 + 8 * (ri >> 2) + 4 * hf + (ri & 3));
-          if (p < 0 || p > r) s[kt][ri] = kNegInf;
-        }
-        mx = fmaxf(mx, s[kt][ri]);
-      }
+      for (int ri = 0; ri < 16; ++ri) mx = fmaxf(mx, s[kt][ri]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m, mx * c);
-    const bool live = mn != kNegInf;
-    const float alpha = live ? exp2f_fast(m - mn) : 1.f;
-    l *= alpha;
+    // Lazy rescaling: the reference max m moves only when some row's block
+    // max exceeds it by more than 2^8 (then every row of the wave updates
+    // exactly), so p <= 2^8 and O, l stay well inside fp32 range.
+    if (__any(mx * c > m + 8.f)) {
+      const float mn = fmaxf(m, mx * c);
+      const float alpha = mn == kNegInf ? 1.f : exp2f_fast(m - mn);
+      l *= alpha;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] *= alpha;
-    m = mn;
+      for (int i = 0; i < 4; ++i) o[i] *= alpha;
+      m = mn;
+    }
+    const float mn = m;
+    const bool live = mn != kNegInf;
     // P^T (bf16) as the B operand of O^T += V^T P^T, 16 keys per MFMA
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -288,7 +304,8 @@ __global__ __launch_bounds__(256 * (G < 4 ? G : 4)) void k_prefill_pool(const Pr
 
   const int t = a.T - 1 - (int)blockIdx.x;
   const int g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int l32 = lane & 31, hf = lane >> 5;
   const int slice = wave & 3, hw = wave >> 2;
   const int N = a.N;
@@ -340,14 +357,16 @@ __global__ __launch_bounds__(256 * (G < 4 ? G : 4)) void k_prefill_pool(const Pr
         }
         const int j = kb + kt * 32 + l32;
         float cs = 0.f;
+        if (need_mask) {
 #pragma unroll
-        for (int ri = 0; ri < 16; ++ri) {
-          float p = exp2f_fast(fmaf(acc[ri], c, -lse[ri]));
-          if (need_mask) {
+          for (int ri = 0; ri < 16; ++ri) {
             const int rr = row0 + 8 * (ri >> 2) + 4 * hf + (ri & 3);
-            p = (j <= rr && rr < N && j < P) ? p : 0.f;
+            const float p = exp2f_fast(fmaf(acc[ri], c, -lse[ri]));
+            cs += (j <= rr && rr < N && j < P) ? p : 0.f;
           }
-          cs += p;
+        } else {
+#pragma unroll
+          for (int ri = 0; ri < 16; ++ri) cs += exp2f_fast(fmaf(acc[ri], c, -lse[ri]));
         }
         cs += __shfl_xor(cs, 32, 64);
         if (hf == 0) red[wave][kt * 32 + l32] = cs;

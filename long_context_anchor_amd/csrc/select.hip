@@ -6,13 +6,21 @@
 // "アンカーレイヤーと再利用レイヤー").  Ties go to the lower index; the list is
 // written in ascending index order.
 //
-// One workgroup (1024 threads, 16 waves) per row.  Three histogram passes
-// over 11/11/10-bit digits (MSB first) fix the k-th largest key T exactly and
-// how many elements equal to T are taken (the lowest-index ones).  A final
-// pass in index order writes every key > T and the first `need` keys == T,
-// using block prefix sums, so the output is ascending and deterministic.  The
-// histograms are integer LDS atomics: order-independent.  Rows that fit are
-// cached as keys in LDS so the four passes read the row from HBM once.
+// One workgroup (1024 threads, 16 waves) per row.
+//   digit 0 (key bits 31..21): a 2048-bin histogram, either handed in (the
+//     decode pooling kernel builds it while it writes the row) or counted
+//     here;
+//   digit 1 (bits 20..10): one sweep counts the keys whose digit 0 matches
+//     and appends them to an LDS candidate buffer (wave-aggregated slots);
+//   digit 2 (bits 9..0): counted over the candidates only (a full sweep if
+//     the buffer overflowed).
+// Each digit's bin is found with a block prefix sum from the top, which fixes
+// the k-th largest key T exactly and how many keys equal to T are taken (the
+// lowest-index ones).  The compaction walks the row in index order in tiles
+// of 32768 keys (32 contiguous keys per thread) with a block prefix sum of
+// (greater, equal) counts, so the output is ascending and deterministic.
+// Histograms are integer LDS atomics: order-independent.  Rows up to the
+// cache capacity are held in LDS as keys (one HBM read per row).
 #include "common.h"
 #include "kernels.h"
 
@@ -23,8 +31,9 @@ namespace {
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kHistBins = 2048;
-constexpr int kRun = 8;   // contiguous elements per thread in the compaction pass
-constexpr int kBatch = 8; // independent loads in flight per thread in the scans
+constexpr int kRun = 32;          // contiguous keys per thread in a compaction tile
+constexpr int kTileKeys = kSelThreads * kRun;
+constexpr int kCandCap = 4096;    // digit-2 candidates kept in LDS
 
 struct RowGeom {
   const float* src;
@@ -85,15 +94,86 @@ KC_INLINE uint32_t block_excl_scan(uint32_t x, uint32_t* sh, uint32_t& total) {
   return r;
 }
 
+// Given a histogram (nb bins) of the keys still in play, find the bin that
+// holds the need-th largest key.  Returns the bin; `above_out` receives the
+// count of keys in higher bins.  Thread tid owns bins 2*rev+1 and 2*rev,
+// rev = 1023 - tid, so the prefix sum runs from the top bin down.
+KC_INLINE uint32_t find_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* scan,
+                            uint32_t* s_sel, uint32_t& above_out) {
+  const int tid = threadIdx.x;
+  const int rev = kSelThreads - 1 - tid;
+  const int bh = 2 * rev + 1, bl = 2 * rev;
+  const uint32_t ch = bh < nb ? hist[bh] : 0u;
+  const uint32_t cl = bl < nb ? hist[bl] : 0u;
+  uint32_t total;
+  const uint32_t above = block_excl_scan(ch + cl, scan, total);
+  if (bh < nb && above < need && above + ch >= need) {
+    s_sel[0] = (uint32_t)bh;
+    s_sel[1] = above;
+  } else if (bl < nb && above + ch < need && above + ch + cl >= need) {
+    s_sel[0] = (uint32_t)bl;
+    s_sel[1] = above + ch;
+  }
+  __syncthreads();
+  const uint32_t bin = s_sel[0];
+  above_out = s_sel[1];
+  __syncthreads();
+  return bin;
+}
+
+// Sweep the row's keys: 4 keys per step per thread (16-byte LDS reads when
+// cached, 16-byte global loads when the row is aligned), f(j, key) per key.
+template <typename F>
+KC_INLINE void sweep(const RowGeom& g, const uint32_t* cache, bool cached, F&& f) {
+  const int tid = threadIdx.x, n = g.n;
+  const bool vec = cached || ((reinterpret_cast<uintptr_t>(g.src) & 15) == 0);
+  const int nv = vec ? (n & ~3) : 0;
+  constexpr int kB = 4;   // 16-byte loads in flight per thread
+  for (int base = 0; base < nv; base += kSelThreads * 4 * kB) {
+    uint4 w[kB];
+#pragma unroll
+    for (int e = 0; e < kB; ++e) {
+      const int j = base + (e * kSelThreads + tid) * 4;
+      w[e] = make_uint4(0, 0, 0, 0);
+      if (j < nv) {
+        if (cached) {
+          w[e] = *reinterpret_cast<const uint4*>(cache + j);
+        } else {
+          const float4 v = *reinterpret_cast<const float4*>(g.src + j);
+          w[e] = make_uint4(f32_order_key(v.x), f32_order_key(v.y), f32_order_key(v.z),
+                            f32_order_key(v.w));
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kB; ++e) {
+      const int j = base + (e * kSelThreads + tid) * 4;
+      const bool in = j < nv;
+      f(in, w[e].x);
+      f(in, w[e].y);
+      f(in, w[e].z);
+      f(in, w[e].w);
+    }
+  }
+  // tail (and unaligned rows): whole waves step together so ballots stay uniform
+  for (int j0 = nv; j0 < n; j0 += kSelThreads) {
+    const int j = j0 + tid;
+    const bool in = j < n;
+    f(in, in ? (cached ? cache[j] : f32_order_key(g.src[j])) : 0u);
+  }
+}
+
 __global__ __launch_bounds__(kSelThreads) void k_topk_select(const SelectArgs a) {
-  extern __shared__ uint32_t smem[];
+  extern __shared__ __align__(16) uint32_t smem[];
   uint32_t* hist = smem;                       // kHistBins
   uint32_t* scan = smem + kHistBins;           // 32 words
-  uint32_t* cache = smem + kHistBins + 32;     // row keys when cached
+  uint32_t* cand = smem + kHistBins + 32;      // kCandCap candidate keys
+  uint32_t* cache = cand + kCandCap;           // row keys when cached
   __shared__ uint32_t s_sel[2];
+  __shared__ uint32_t s_ncand;
 
   const RowGeom g = row_geom(a, blockIdx.x);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int n = g.n, k = g.k;
 
   if (k >= n) {   // every index is selected
@@ -105,83 +185,116 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const SelectArgs a)
     return;
   }
   const bool cached = n <= a.cache_cap;
+  const uint32_t* hist0 = a.hist0 ? a.hist0 + (int64_t)blockIdx.x * kHistBins : nullptr;
+  for (int i = tid; i < kHistBins; i += kSelThreads) hist[i] = hist0 ? hist0[i] : 0u;
+  if (tid == 0) s_ncand = 0;
   if (cached) {
-    // kBatch independent loads in flight per thread
-    for (int base = 0; base < n; base += kSelThreads * kBatch) {
-      float v[kBatch];
+    // one pass over HBM: keys into LDS (16-byte loads when the row is aligned)
+    const bool vec = (reinterpret_cast<uintptr_t>(g.src) & 15) == 0;
+    const int nv = vec ? (n & ~3) : 0;
+    for (int base = 0; base < nv; base += kSelThreads * 16) {
+      float4 v[4];
 #pragma unroll
-      for (int e = 0; e < kBatch; ++e) {
-        const int j = base + e * kSelThreads + tid;
-        v[e] = j < n ? g.src[j] : 0.f;
+      for (int e = 0; e < 4; ++e) {
+        const int j = base + (e * kSelThreads + tid) * 4;
+        v[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j < nv) v[e] = *reinterpret_cast<const float4*>(g.src + j);
       }
 #pragma unroll
-      for (int e = 0; e < kBatch; ++e) {
-        const int j = base + e * kSelThreads + tid;
-        if (j < n) cache[j] = f32_order_key(v[e]);
+      for (int e = 0; e < 4; ++e) {
+        const int j = base + (e * kSelThreads + tid) * 4;
+        if (j < nv)
+          *reinterpret_cast<uint4*>(cache + j) = make_uint4(
+              f32_order_key(v[e].x), f32_order_key(v[e].y), f32_order_key(v[e].z),
+              f32_order_key(v[e].w));
       }
     }
+    for (int j = nv + tid; j < n; j += kSelThreads) cache[j] = f32_order_key(g.src[j]);
   }
+  __syncthreads();
 
-  uint32_t prefix = 0;
-  uint32_t need = (uint32_t)k;   // how many still to take among keys matching prefix
-#pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int nbits = pass == 2 ? 10 : 11;
-    const int sh = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int nb = 1 << nbits;
-    const int hs = sh + nbits;                 // bits above this digit
-    for (int i = tid; i < kHistBins; i += kSelThreads) hist[i] = 0;
-    __syncthreads();
-    for (int base = 0; base < n; base += kSelThreads * kBatch) {
-      uint32_t kk[kBatch];
-#pragma unroll
-      for (int e = 0; e < kBatch; ++e) {
-        const int j = base + e * kSelThreads + tid;
-        kk[e] = j < n ? (cached ? cache[j] : f32_order_key(g.src[j])) : 0u;
-      }
-#pragma unroll
-      for (int e = 0; e < kBatch; ++e) {
-        const int j = base + e * kSelThreads + tid;
-        const bool match = j < n && ((pass == 0) || ((kk[e] >> hs) == prefix));
-        if (match) atomicAdd(&hist[(kk[e] >> sh) & (nb - 1)], 1u);
-      }
-    }
-    __syncthreads();
-    // thread tid owns bins (from the top) 2*tid and 2*tid+1 of the reversed order
-    const int rev = kSelThreads - 1 - tid;
-    const int bh = 2 * rev + 1, bl = 2 * rev;
-    const uint32_t ch = bh < nb ? hist[bh] : 0u;
-    const uint32_t cl = bl < nb ? hist[bl] : 0u;
-    uint32_t total;
-    const uint32_t above = block_excl_scan(ch + cl, scan, total);
-    if (bh < nb && above < need && above + ch >= need) {
-      s_sel[0] = (uint32_t)bh;
-      s_sel[1] = above;
-    } else if (bl < nb && above + ch < need && above + ch + cl >= need) {
-      s_sel[0] = (uint32_t)bl;
-      s_sel[1] = above + ch;
-    }
-    __syncthreads();
-    prefix = (prefix << nbits) | s_sel[0];
-    need -= s_sel[1];
+  // digit 0
+  if (!hist0) {
+    sweep(g, cache, cached, [&](bool in, uint32_t key) {
+      if (in) atomicAdd(&hist[key >> 21], 1u);
+    });
     __syncthreads();
   }
-  const uint32_t T = prefix;   // the k-th largest key; take `need` of the keys == T
+  uint32_t need = (uint32_t)k, above;
+  const uint32_t b0 = find_bin(hist, 2048, need, scan, s_sel, above);
+  need -= above;
+
+  // digit 1, collecting the digit-0 matches as candidates
+  for (int i = tid; i < kHistBins; i += kSelThreads) hist[i] = 0;
+  __syncthreads();
+  sweep(g, cache, cached, [&](bool in, uint32_t key) {
+    const bool m = in && (key >> 21) == b0;
+    if (m) atomicAdd(&hist[(key >> 10) & 2047u], 1u);
+    const uint64_t bal = __ballot(m);
+    if (bal) {
+      uint32_t base = 0;
+      const int leader = __ffsll((unsigned long long)bal) - 1;
+      if (lane == leader) base = atomicAdd(&s_ncand, (uint32_t)__popcll(bal));
+      base = __shfl(base, leader, 64);
+      const uint32_t slot = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+      if (m && slot < (uint32_t)kCandCap) cand[slot] = key;
+    }
+  });
+  __syncthreads();
+  const uint32_t b1 = find_bin(hist, 2048, need, scan, s_sel, above);
+  need -= above;
+  const uint32_t p01 = (b0 << 11) | b1;   // bits 31..10 of T
+
+  // digit 2
+  for (int i = tid; i < kHistBins; i += kSelThreads) hist[i] = 0;
+  __syncthreads();
+  const uint32_t ncand = s_ncand;
+  if (ncand <= (uint32_t)kCandCap) {
+    for (uint32_t i = tid; i < ncand; i += kSelThreads) {
+      const uint32_t key = cand[i];
+      if ((key >> 10) == p01) atomicAdd(&hist[key & 1023u], 1u);
+    }
+  } else {
+    sweep(g, cache, cached, [&](bool in, uint32_t key) {
+      if (in && (key >> 10) == p01) atomicAdd(&hist[key & 1023u], 1u);
+    });
+  }
+  __syncthreads();
+  const uint32_t b2 = find_bin(hist, 1024, need, scan, s_sel, above);
+  need -= above;
+  const uint32_t T = (p01 << 10) | b2;   // the k-th largest key; take `need` of the keys == T
 
   // compaction in index order
+  const bool vec = cached || ((reinterpret_cast<uintptr_t>(g.src) & 15) == 0);
   uint32_t run_gt = 0, run_eq = 0;
-  for (int base = 0; base < n; base += kSelThreads * kRun) {
+  for (int base = 0; base < n; base += kTileKeys) {
     const int j0 = base + tid * kRun;
     uint32_t keys[kRun];
+#pragma unroll
+    for (int e = 0; e < kRun; e += 4) {
+      const int j = j0 + e;
+      if (vec && j + 4 <= n) {
+        uint4 w;
+        if (cached) {
+          w = *reinterpret_cast<const uint4*>(cache + j);
+        } else {
+          const float4 v = *reinterpret_cast<const float4*>(g.src + j);
+          w = make_uint4(f32_order_key(v.x), f32_order_key(v.y), f32_order_key(v.z),
+                         f32_order_key(v.w));
+        }
+        keys[e] = w.x; keys[e + 1] = w.y; keys[e + 2] = w.z; keys[e + 3] = w.w;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          keys[e + q] = (j + q < n) ? (cached ? cache[j + q] : f32_order_key(g.src[j + q])) : 0u;
+      }
+    }
     uint32_t cgt = 0, ceq = 0;
 #pragma unroll
     for (int e = 0; e < kRun; ++e) {
-      const int j = j0 + e;
-      uint32_t key = 0;
-      if (j < n) key = cached ? cache[j] : f32_order_key(g.src[j]);
-      keys[e] = key;
-      cgt += (j < n && key > T) ? 1u : 0u;
-      ceq += (j < n && key == T) ? 1u : 0u;
+      const bool in = j0 + e < n;
+      cgt += (in && keys[e] > T) ? 1u : 0u;
+      ceq += (in && keys[e] == T) ? 1u : 0u;
     }
     uint32_t tot;
     const uint32_t ex = block_excl_scan((cgt << 16) | ceq, scan, tot);
@@ -189,13 +302,14 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const SelectArgs a)
 #pragma unroll
     for (int e = 0; e < kRun; ++e) {
       const int j = j0 + e;
-      if (j >= n) break;
-      if (keys[e] > T) {
-        g.out[gt + min(eq, need)] = j;
-        ++gt;
-      } else if (keys[e] == T) {
-        if (eq < need) g.out[gt + eq] = j;
-        ++eq;
+      if (j < n) {
+        if (keys[e] > T) {
+          g.out[gt + min(eq, need)] = j;
+          ++gt;
+        } else if (keys[e] == T) {
+          if (eq < need) g.out[gt + eq] = j;
+          ++eq;
+        }
       }
     }
     run_gt += tot >> 16;
@@ -208,7 +322,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const SelectArgs a)
 
 // LDS bytes of the select kernel for a given row cache capacity.
 size_t topk_select_lds_bytes(int cache_cap) {
-  return (size_t)(kHistBins + 32 + cache_cap) * sizeof(uint32_t);
+  return (size_t)(kHistBins + 32 + kCandCap + cache_cap) * sizeof(uint32_t);
 }
 
 hipError_t topk_select_set_max_lds(size_t bytes) {

@@ -228,7 +228,7 @@ def check(status: int, where: str) -> None:
 def workspace(op: int, shape: Shape, topk: int = 0, rule: Optional[TopkRule] = None,
               device="cuda") -> torch.Tensor:
     n = kascade_workspace_bytes(op, shape, topk, rule)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def anchor_decode(q, k, v, topk: int, ctx_len: Optional[int] = None, want_pooled=False, ws=None):
