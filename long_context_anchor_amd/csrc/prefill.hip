@@ -21,9 +21,10 @@
 //   attention: S^T = K Q^T (A = K rows from LDS, B = Q rows in registers),
 //     so each lane owns one query and its softmax row statistics stay in
 //     the lane (plus its partner lane l^32).  P^T in that C layout is
-//     already the B operand of O^T = V^T P^T once the key order of a
-//     16-key chunk is permuted; V is written to LDS transposed in that
-//     permuted order so the A operand is one 16-byte LDS read.
+//     already the B operand of O^T = V^T P^T for a permuted key order of
+//     each 16-key chunk; V stays [key][d] in LDS and its A operand is read
+//     with the gfx950 transposing LDS load (ds_read_b64_tr_b16) in that
+//     order.
 //   pooling: S = Q K^T (A = Q registers, B = K from LDS), so each lane owns
 //     one key column and the pooled column sum is an in-lane sum.
 #include "common.h"
@@ -36,8 +37,8 @@ namespace {
 constexpr int kD = 128;
 constexpr int kTileQ = 128;            // query rows per tile (4 waves x 32)
 constexpr int kKB = 64;                // keys per block
-constexpr int kKStride = kD + 8;       // bf16 per K row in LDS (272 B: conflict-free reads)
-constexpr int kVStride = kKB + 8;      // bf16 per V^T row in LDS (144 B)
+constexpr int kKStride = kD + 8;       // bf16 per K row in LDS (272 B: conflict-free 16-byte reads)
+constexpr int kVStride = kD + 32;      // bf16 per V row in LDS (320 B: conflict-free transposed reads)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -52,93 +53,150 @@ KC_INLINE f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& 
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// One block of 64 keys held in registers between its global loads and its
-// LDS store, so the loads of block i+1 are in flight while block i is used.
-// K units: 64 rows x 16 chunks of 16 bytes, (kKB*16)/NT per thread.  V^T
-// units: (16-key chunk, half, 4 d columns): 8 keys x 4 d, 256/NT per thread.
-template <int NT, bool WITH_V>
-struct KvRegs {
-  static constexpr int KU = kKB * 16 / NT;
-  static constexpr int VU = WITH_V ? 256 / NT : 0;
-  uint4 k[KU];
-  uint2 v[VU > 0 ? VU : 1][8];
+// Register staging of one block of 64 key rows between their global loads
+// and their LDS store, so the loads of a later block are in flight while the
+// current one is used.  A block is 64 rows x 16 chunks of 16 bytes; thread
+// tid owns chunks tid + i*NT.  Per-thread row offsets are fixed, so a dense
+// block needs only its (scalar) base address.
+template <int NT, int STRIDE = kKStride>
+struct RowStager {
+  static constexpr int U = kKB * 16 / NT;
+  uint4 k[U];
 
-  // pos(kr) gives the cache row of block row kr, or -1 for none.
-  template <typename PosF>
-  KC_INLINE void load(PosF pos, const char* kbase, const char* vbase, int64_t row_bytes) {
-    const int tid = threadIdx.x;
+  KC_INLINE static int row(int i) { return (threadIdx.x + i * NT) >> 4; }
+  KC_INLINE static int chunk(int i) { return (threadIdx.x + i * NT) & 15; }
+
+  // Rows kb .. kb+63 of a dense cache.  Block rows >= nvalid load the last
+  // valid row instead (real, finite cache data): their scores are masked to
+  // -inf and their probabilities are 0, so nothing is zeroed here and the
+  // loads stay in flight until the LDS store one step later.
+  KC_INLINE void load_dense(const char* blk, int64_t row_bytes, int nvalid) {
 #pragma unroll
-    for (int i = 0; i < KU; ++i) {
-      const int u = tid + i * NT;
-      const int p = pos(u >> 4);
-      // always load (row 0 stands in for a missing row), then zero: no branch
-      const uint4 x = ld16(kbase + (int64_t)(p < 0 ? 0 : p) * row_bytes + (u & 15) * 16);
-      k[i] = p < 0 ? make_uint4(0, 0, 0, 0) : x;
-    }
-#pragma unroll
-    for (int i = 0; i < VU; ++i) {
-      const int u = tid + i * NT;
-      const int c4 = u >> 6, hp = (u >> 5) & 1, dg = u & 31;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int p = pos(c4 * 16 + 4 * hp + (s & 3) + 8 * (s >> 2));
-        const uint2 x =
-            *reinterpret_cast<const uint2*>(vbase + (int64_t)(p < 0 ? 0 : p) * row_bytes + dg * 8);
-        v[i][s] = p < 0 ? make_uint2(0, 0) : x;
-      }
+    for (int i = 0; i < U; ++i) {
+      const int rr = min(row(i), max(nvalid - 1, 0));
+      k[i] = ld16(blk + (int32_t)(rr * (int32_t)row_bytes) + chunk(i) * 16);
     }
   }
-
-  // K rows as [key][d] (padded); V^T as [d][key] with the keys of each
-  // 16-key chunk in MFMA B-operand order (see the file comment).
-  KC_INLINE void store(uint16_t* sk, uint16_t* svt) const {
-    const int tid = threadIdx.x;
+  // Gathered rows pos[rr] (block-relative rows rr < nvalid); missing rows
+  // (-1 or past the list) load cache row 0 and are masked the same way.
+  KC_INLINE void load_gather(const char* base, int64_t row_bytes, const int32_t* pos, int nvalid) {
 #pragma unroll
-    for (int i = 0; i < KU; ++i) {
-      const int u = tid + i * NT;
-      sts16(sk + (u >> 4) * kKStride + (u & 15) * 8, k[i]);
+    for (int i = 0; i < U; ++i) {
+      const int rr = row(i);
+      const int p = rr < nvalid ? pos[rr] : -1;
+      k[i] = ld16(base + (int64_t)(p < 0 ? 0 : p) * row_bytes + chunk(i) * 16);
     }
+  }
+  // rows as [key][d] (padded rows of STRIDE bf16)
+  KC_INLINE void store(uint16_t* sk) const {
 #pragma unroll
-    for (int i = 0; i < VU; ++i) {
-      const int u = tid + i * NT;
-      const int c4 = u >> 6, hp = (u >> 5) & 1, dg = u & 31;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t a[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) a[s] = (e < 2) ? v[i][s].x : v[i][s].y;
-        uint4 o;
-        o.x = __builtin_amdgcn_perm(a[1], a[0], sel);
-        o.y = __builtin_amdgcn_perm(a[3], a[2], sel);
-        o.z = __builtin_amdgcn_perm(a[5], a[4], sel);
-        o.w = __builtin_amdgcn_perm(a[7], a[6], sel);
-        sts16(svt + (dg * 4 + e) * kVStride + c4 * 16 + 8 * hp, o);
-      }
-    }
+    for (int i = 0; i < U; ++i) sts16(sk + row(i) * STRIDE + chunk(i) * 8, k[i]);
   }
 };
 
-struct __align__(16) AttnSmem {
-  uint16_t k[kKB * kKStride];
-  uint16_t vt[kD * kVStride];
-};
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// V^T fragment (MFMA A operand, 32 d rows x 16 keys) read transposed from V
+// stored as [key][d]: ds_read_b64_tr_b16 hands lane i of each 16-lane group
+// element (i & 3) of the 8-byte row addressed by lane 4e + (i >> 2), as its
+// element e.  Lane l (half h = l/32, group g16 = (l/16)&1, j = l&15)
+// addresses keys kc + 4h + (j>>2) (and +8) at d = d0 + 16*g16 + 4*(j&3), so
+// it receives d = d0 + l%32 for keys kc + 4h + {0..3, 8..11}: the order of
+// the B operand P^T taken from the S^T accumulator layout.
+KC_INLINE bf16x8_t v_frag(const uint16_t* sv, int kc, int d0, int lane) {
+  const int h = lane >> 5, g16 = (lane >> 4) & 1, j = lane & 15;
+  const uint16_t* p0 = sv + (kc + 4 * h + (j >> 2)) * kVStride + d0 + 16 * g16 + 4 * (j & 3);
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+  const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 8 * kVStride));
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x8_t v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// XCD-aware work order.  Workgroups are dispatched round-robin over the 8
+// XCDs (each with its own L2), so launch id L runs on XCD L % 8.  Work items
+// are ordered (batch, KV head, tile from the longest causal prefix down,
+// query head of the group fastest) and each XCD takes one contiguous eighth:
+// the query heads sharing a KV head and the tiles streaming the same keys
+// run on the same L2.  Returns false for the padding ids of the last eighth.
+constexpr int kXcds = 8;
+KC_INLINE bool xcd_work_item(int total, int G, int T, int Hkv, int& t, int& h, int& b) {
+  const int L = blockIdx.x;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int w = (L % kXcds) * per + L / kXcds;
+  if (w >= total) return false;
+  const int hh = w % G;
+  int rest = w / G;
+  t = T - 1 - rest % T;
+  rest /= T;
+  const int g = rest % Hkv;
+  b = rest / Hkv;
+  h = g * G + hh;
+  return true;
+}
+inline int xcd_grid(int total) { return (total + kXcds - 1) / kXcds * kXcds; }
+
+// S^T = K_block Q^T for the wave's 32 queries: two 32-key tiles.
+// The two key tiles are independent accumulation chains; alternating them
+// keeps a dependent MFMA one issue away from its predecessor.
+KC_INLINE void qk_block(const uint16_t* sk, const bf16x8_t* qf, int l32, int hf, f32x16_t* s) {
+  s[0] = f32x16_t{};
+  s[1] = f32x16_t{};
+#pragma unroll
+  for (int ds = 0; ds < 8; ++ds) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const bf16x8_t kf = as_bf16x8(lds16(sk + (kt * 32 + l32) * kKStride + ds * 16 + hf * 8));
+      s[kt] = mfma32(kf, qf[ds], s[kt]);
+    }
+  }
+}
 
 // One workgroup = one (query tile, query head, batch); 4 waves x 32 rows.
 // GATHER: the keys are the tile's list for KV head head_map[g] (ascending,
 // staged in LDS once), masked per row by position <= row.
-template <bool GATHER>
-__global__ __launch_bounds__(256, 2) void k_prefill_attn(const PrefillArgs a) {
-  __shared__ AttnSmem sm;
+//
+// Software pipeline over 64-key blocks j: while the MFMAs of S_{j+1} =
+// K_{j+1} Q^T run, the VALU does the softmax of S_j, then O^T += V_j^T P_j^T.
+// K is double-buffered in LDS (K_{j+1} is written one block ahead), V is
+// single-buffered (V_j is written at the start of step j); global loads of
+// K_{j+2} and V_{j+1} are in flight during step j.
+template <bool GATHER, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const PrefillArgs a) {
+  constexpr int NT = 64 * WAVES;
+  __shared__ __align__(16) uint16_t sk[2][kKB * kKStride];
+  __shared__ __align__(16) uint16_t sv[kKB * kVStride];
   extern __shared__ int32_t slist[];
-  const int t = a.T - 1 - (int)blockIdx.x;   // longest causal tiles first
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int G = a.Hq / a.Hkv, g = h / G;
+  const int G = a.Hq / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int l32 = lane & 31, hf = lane >> 5;
   const int N = a.N;
-  const int row0 = t * kTileQ + wave * 32;
+  // Work item and this wave's (query head, 32-row slice):
+  //   dense, 8 waves : 256 consecutive rows (two tiles) of one query head;
+  //   gather, 8 waves: one tile of two query heads of the group (same list);
+  //   4 waves        : one tile of one query head.
+  int t, h, b, row0, kend;
+  if (WAVES == 8 && !GATHER) {
+    const int Tp = (a.T + 1) / 2;
+    int pr;
+    if (!xcd_work_item(Tp * a.Hq * a.B, G, Tp, a.Hkv, pr, h, b)) return;
+    row0 = pr * 2 * kTileQ + wave * 32;
+    t = pr * 2 + (wave >> 2);
+    kend = min(N, 2 * kTileQ * (pr + 1));
+  } else if (WAVES == 8) {
+    int hp;
+    if (!xcd_work_item(a.T * (a.Hq / 2) * a.B, G / 2, a.T, a.Hkv, t, hp, b)) return;
+    h = 2 * hp + (wave >> 2);
+    row0 = t * kTileQ + (wave & 3) * 32;
+    kend = min(N, kTileQ * (t + 1));
+  } else {
+    if (!xcd_work_item(a.T * a.Hq * a.B, G, a.T, a.Hkv, t, h, b)) return;
+    row0 = t * kTileQ + wave * 32;
+    kend = min(N, kTileQ * (t + 1));
+  }
+  const int g = h / G;
   const int r = row0 + l32;
   const float c = a.scale_log2;
 
@@ -149,17 +207,15 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(const PrefillArgs a) {
                      ((int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)min(r, N - 1) * a.q_sn) * 2;
 #pragma unroll
     for (int ds = 0; ds < 8; ++ds) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (r < N) u = ld16(qp + (ds * 16 + hf * 8) * 2);
-      qf[ds] = as_bf16x8(u);
+      const uint4 u = ld16(qp + (ds * 16 + hf * 8) * 2);
+      qf[ds] = as_bf16x8(r < N ? u : make_uint4(0, 0, 0, 0));
     }
   }
-  const int P = min(N, kTileQ * (t + 1));
-  int nkeys = P;
+  int nkeys = kend;
   if (GATHER) {
-    nkeys = tile_k_for_len(P, a.pct, a.round_to, a.k_min);
+    nkeys = tile_k_for_len(kend, a.pct, a.round_to, a.k_min);
     const int32_t* list = a.idx + ((int64_t)(b * a.T + t) * a.Hkv + a.hm.m[g]) * a.k_max;
-    for (int i = tid; i < nkeys; i += 256) {
+    for (int i = tid; i < nkeys; i += NT) {
       const int p = list[i];
       slist[i] = (p >= 0 && p < N) ? p : -1;
     }
@@ -168,10 +224,20 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(const PrefillArgs a) {
   const int64_t row_bytes = a.kv_sn * 2;
   const char* kbase = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh) * 2;
   const char* vbase = reinterpret_cast<const char*>(a.v) + ((int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh) * 2;
-  auto pos_of = [&](int kb, int kr) -> int {
-    const int i = kb + kr;
-    if (i >= nkeys) return -1;
-    return GATHER ? slist[i] : i;
+  const int nb = (nkeys + kKB - 1) / kKB;
+
+  RowStager<NT> kr;
+  RowStager<NT, kVStride> vr;
+  // loads of block jb (K or V) into a stager
+  auto load_blk = [&](RowStager<NT>& st, int jb) {
+    const int kb = jb * kKB;
+    if (GATHER) st.load_gather(kbase, row_bytes, slist + kb, nkeys - kb);
+    else st.load_dense(kbase + (int64_t)kb * row_bytes, row_bytes, nkeys - kb);
+  };
+  auto load_vblk = [&](RowStager<NT, kVStride>& st, int jb) {
+    const int kb = jb * kKB;
+    if (GATHER) st.load_gather(vbase, row_bytes, slist + kb, nkeys - kb);
+    else st.load_dense(vbase + (int64_t)kb * row_bytes, row_bytes, nkeys - kb);
   };
 
   f32x16_t o[4];
@@ -179,24 +245,24 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(const PrefillArgs a) {
   for (int i = 0; i < 4; ++i) o[i] = f32x16_t{};
   float m = kNegInf, l = 0.f;
 
-  KvRegs<256, true> regs;
-  regs.load([&](int kr) { return pos_of(0, kr); }, kbase, vbase, row_bytes);
-  for (int kb = 0; kb < nkeys; kb += kKB) {
-    __syncthreads();   // the previous block's LDS reads are done
-    regs.store(sm.k, sm.vt);
-    __syncthreads();
-    if (kb + kKB < nkeys) regs.load([&](int kr) { return pos_of(kb + kKB, kr); }, kbase, vbase, row_bytes);
+  load_blk(kr, 0);
+  load_vblk(vr, 0);
+  kr.store(sk[0]);
+  if (nb > 1) load_blk(kr, 1);
+  __syncthreads();
+  f32x16_t sA[2], sB[2];
+  qk_block(sk[0], qf, l32, hf, sA);
 
-    f32x16_t s[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      s[kt] = f32x16_t{};
-#pragma unroll
-      for (int ds = 0; ds < 8; ++ds) {
-        const bf16x8_t kf = as_bf16x8(lds16(sm.k + (kt * 32 + l32) * kKStride + ds * 16 + hf * 8));
-        s[kt] = mfma32(kf, qf[ds], s[kt]);
-      }
-    }
+  // One pipeline step on block j: s_cur holds S_j; S_{j+1} goes to s_next.
+  auto step = [&](int j, f32x16_t* s_cur, f32x16_t* s_next) {
+    const int kb = j * kKB;
+    __syncthreads();   // every wave is done with V_{j-1} and K_j's LDS reads
+    if (j + 1 < nb) kr.store(sk[(j + 1) & 1]);
+    vr.store(sv);
+    __syncthreads();
+    if (j + 2 < nb) load_blk(kr, j + 2);
+    if (j + 1 < nb) load_vblk(vr, j + 1);
+
     // causal mask inside the block (key position > query row) and empty slots
     // (a scalar, wave-uniform decision; the masked path is branch-free)
     bool need_mask;
@@ -214,7 +280,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(const PrefillArgs a) {
           const int kk = kb + kt * 32 + 8 * (ri >> 2) + 4 * hf + (ri & 3);
           int p = GATHER ? slist[min(kk, nkeys - 1)] : kk;
           p = kk < nkeys ? p : -1;
-          s[kt][ri] = (p < 0 || p > r) ? kNegInf : s[kt][ri];
+          s_cur[kt][ri] = (p < 0 || p > r) ? kNegInf : s_cur[kt][ri];
         }
       }
     }
@@ -222,7 +288,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(const PrefillArgs a) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int ri = 0; ri < 16; ++ri) mx = fmaxf(mx, s[kt][ri]);
+      for (int ri = 0; ri < 16; ++ri) mx = fmaxf(mx, s_cur[kt][ri]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     // Lazy rescaling: the reference max m moves only when some row's block
@@ -236,34 +302,40 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(const PrefillArgs a) {
       for (int i = 0; i < 4; ++i) o[i] *= alpha;
       m = mn;
     }
-    const float mn = m;
-    const bool live = mn != kNegInf;
-    // P^T (bf16) as the B operand of O^T += V^T P^T, 16 keys per MFMA
+    // a row whose max is still -inf has only masked scores in this block:
+    // any finite reference gives them p = 2^-inf = 0
+    const float mn = m == kNegInf ? 0.f : m;
+
+    // One straight-line region: the MFMAs of S_{j+1} (issued unconditionally;
+    // after the last block they read a stale buffer and are discarded), the
+    // softmax of S_j, and O^T += V_j^T P_j^T, so the scheduler can interleave
+    // VALU work with the matrix pipe.  Row sums stay fp32 on the unrounded P
+    // (the log-sum-exp feeds the pooling pass).
+    qk_block(sk[(j + 1) & 1], qf, l32, hf, s_next);
+    bf16x8_t pb[4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int kt = q4 >> 1, c2 = q4 & 1;
+      float p[8];
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = live ? exp2f_fast(fmaf(s[kt][8 * c2 + e], c, -mn)) : 0.f;
-          l += p[e];
-        }
-        uint4 pk;
-        pk.x = pack_bf16x2(p[0], p[1]);
-        pk.y = pack_bf16x2(p[2], p[3]);
-        pk.z = pack_bf16x2(p[4], p[5]);
-        pk.w = pack_bf16x2(p[6], p[7]);
-        const bf16x8_t pb = as_bf16x8(pk);
-        const int chunk = kt * 2 + c2;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const bf16x8_t vf =
-              as_bf16x8(lds16(sm.vt + (db * 32 + l32) * kVStride + chunk * 16 + hf * 8));
-          o[db] = mfma32(vf, pb, o[db]);
-        }
-      }
+      for (int e = 0; e < 8; ++e) p[e] = exp2f_fast(fmaf(s_cur[kt][8 * c2 + e], c, -mn));
+      l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      uint4 pk;
+      pk.x = pack_bf16x2(p[0], p[1]);
+      pk.y = pack_bf16x2(p[2], p[3]);
+      pk.z = pack_bf16x2(p[4], p[5]);
+      pk.w = pack_bf16x2(p[6], p[7]);
+      pb[q4] = as_bf16x8(pk);
     }
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] = mfma32(v_frag(sv, ch * 16, db * 32, lane), pb[ch], o[db]);
+    }
+  };
+  for (int j = 0; j < nb; j += 2) {
+    step(j, sA, sB);
+    if (j + 1 < nb) step(j + 1, sB, sA);
   }
 
   // normalise and write: lane holds query r, d rows 32*db + 8i + 4*hf + j
@@ -302,8 +374,8 @@ __global__ __launch_bounds__(256 * (G < 4 ? G : 4)) void k_prefill_pool(const Pr
   __shared__ __align__(16) uint16_t sk[kKB * kKStride];
   __shared__ float red[NW][kKB];
 
-  const int t = a.T - 1 - (int)blockIdx.x;
-  const int g = blockIdx.y, b = blockIdx.z;
+  int t, g, b;
+  if (!xcd_work_item(a.T * a.Hkv * a.B, 1, a.T, a.Hkv, t, g, b)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int l32 = lane & 31, hf = lane >> 5;
@@ -337,36 +409,37 @@ __global__ __launch_bounds__(256 * (G < 4 ? G : 4)) void k_prefill_pool(const Pr
         lse[ri] = rr < N ? lp[rr] : 0.f;
       }
     }
-    KvRegs<NT, false> regs;
-    regs.load([&](int kr) { return kr < P ? kr : -1; }, kbase, nullptr, row_bytes);
+    RowStager<NT> regs;
+    regs.load_dense(kbase, row_bytes, P);
     for (int kb = 0; kb < P; kb += kKB) {
       __syncthreads();
-      regs.store(sk, nullptr);
+      regs.store(sk);
       __syncthreads();
-      if (kb + kKB < P)
-        regs.load([&](int kr) { return kb + kKB + kr < P ? kb + kKB + kr : -1; }, kbase, nullptr,
-                  row_bytes);
+      if (kb + kKB < P) regs.load_dense(kbase + (int64_t)(kb + kKB) * row_bytes, row_bytes, P - kb - kKB);
       const bool need_mask = (kb + kKB - 1 > row0) || (kb + kKB > P) || (row0 + 32 > N);
+      f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+      for (int ds = 0; ds < 8; ++ds) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const bf16x8_t kf = as_bf16x8(lds16(sk + (kt * 32 + l32) * kKStride + ds * 16 + hf * 8));
+          acc[kt] = mfma32(qf[ds], kf, acc[kt]);
+        }
+      }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        f32x16_t acc = f32x16_t{};
-#pragma unroll
-        for (int ds = 0; ds < 8; ++ds) {
-          const bf16x8_t kf = as_bf16x8(lds16(sk + (kt * 32 + l32) * kKStride + ds * 16 + hf * 8));
-          acc = mfma32(qf[ds], kf, acc);
-        }
         const int j = kb + kt * 32 + l32;
         float cs = 0.f;
         if (need_mask) {
 #pragma unroll
           for (int ri = 0; ri < 16; ++ri) {
             const int rr = row0 + 8 * (ri >> 2) + 4 * hf + (ri & 3);
-            const float p = exp2f_fast(fmaf(acc[ri], c, -lse[ri]));
+            const float p = exp2f_fast(fmaf(acc[kt][ri], c, -lse[ri]));
             cs += (j <= rr && rr < N && j < P) ? p : 0.f;
           }
         } else {
 #pragma unroll
-          for (int ri = 0; ri < 16; ++ri) cs += exp2f_fast(fmaf(acc[ri], c, -lse[ri]));
+          for (int ri = 0; ri < 16; ++ri) cs += exp2f_fast(fmaf(acc[kt][ri], c, -lse[ri]));
         }
         cs += __shfl_xor(cs, 32, 64);
         if (hf == 0) red[wave][kt * 32 + l32] = cs;
@@ -385,7 +458,8 @@ __global__ __launch_bounds__(256 * (G < 4 ? G : 4)) void k_prefill_pool(const Pr
 }  // namespace
 
 hipError_t launch_prefill_flash(const PrefillArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_prefill_attn<false>, dim3(a.T, a.Hq, a.B), dim3(256), 0, s, a);
+  const int Tp = (a.T + 1) / 2;
+  hipLaunchKernelGGL((k_prefill_attn<false, 8>), dim3(xcd_grid(Tp * a.Hq * a.B)), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
@@ -393,19 +467,27 @@ hipError_t launch_prefill_flash(const PrefillArgs& a, hipStream_t s) {
 size_t prefill_sparse_max_list() { return 24576; }
 
 hipError_t prefill_set_max_lds() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill_attn<true>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)(prefill_sparse_max_list() * sizeof(int32_t)));
+  const int bytes = (int)(prefill_sparse_max_list() * sizeof(int32_t));
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill_attn<true, 8>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill_attn<true, 4>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
 hipError_t launch_prefill_sparse(const PrefillArgs& a, hipStream_t s) {
   const size_t lds = (size_t)a.k_max * sizeof(int32_t);
-  hipLaunchKernelGGL(k_prefill_attn<true>, dim3(a.T, a.Hq, a.B), dim3(256), lds, s, a);
+  if ((a.Hq / a.Hkv) % 2 == 0)
+    hipLaunchKernelGGL((k_prefill_attn<true, 8>), dim3(xcd_grid(a.T * (a.Hq / 2) * a.B)), dim3(512),
+                       lds, s, a);
+  else
+    hipLaunchKernelGGL((k_prefill_attn<true, 4>), dim3(xcd_grid(a.T * a.Hq * a.B)), dim3(256), lds,
+                       s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_pool(const PrefillArgs& a, hipStream_t s) {
-  dim3 grid(a.T, a.Hkv, a.B);
+  dim3 grid(xcd_grid(a.T * a.Hkv * a.B));
   switch (a.Hq / a.Hkv) {
     case 1: hipLaunchKernelGGL(k_prefill_pool<1>, grid, dim3(256), 0, s, a); break;
     case 2: hipLaunchKernelGGL(k_prefill_pool<2>, grid, dim3(512), 0, s, a); break;
