@@ -19,6 +19,7 @@ HIP events on its launch stream inside the timed steps.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -33,6 +34,14 @@ sys.path.insert(0, ROOT)
 METRIC = "decode attn µs/layer + HBM GB/s at 32k/128k ctx; prefill attn TFLOP/s"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+# HBM traffic of the kernels, read by rocprofv3 counters and stored as text
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_kernels_llama8b.md")
+CSRC = os.path.join(ROOT, "long_context_anchor_amd", "csrc")
+KERNEL_SOURCES = {"prefill_flash": "prefill.hip", "prefill_pool": "prefill.hip",
+                  "prefill_sparse": "prefill.hip", "decode_splitk": "decode.hip",
+                  "decode_combine": "decode.hip", "decode_pool": "decode.hip",
+                  "reuse_decode": "decode.hip", "topk_select": "select.hip"}
+COPY_BYTES = 1 << 30  # the calibration copy reads and writes this many bytes
 
 
 def log(*a):
@@ -184,6 +193,91 @@ def cpu_baseline(dec, torch):
 
 
 # ---------------------------------------------------------------------------
+# HBM traffic (counter) support
+# ---------------------------------------------------------------------------
+
+def kernel_source_hash(kernel):
+    """sha256 over the sources a kernel is built from (its .hip and the shared headers)."""
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "common.h", "kernels.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel, config):
+    """HBM bytes per launch of `kernel` on `config` from the stored counter summary.
+
+    The summary holds lines `traffic | <kernel> | <config> | <bytes> | <source hash>`;
+    the figure is returned only while the kernel's sources still hash the same,
+    else None (the counters describe code that no longer exists)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    cur = kernel_source_hash(kernel)
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            parts = [x.strip() for x in line.strip().strip("|").split("|")]
+            if len(parts) == 5 and parts[0] == "traffic" and parts[1] == kernel and parts[2] == config:
+                return float(parts[3]) if parts[4] == cur else None
+    return None
+
+
+def traffic_probe(torch, K, synth, configs):
+    """One launch of every kernel of the hot path, plus a plain copy of known size.
+
+    Meant to run under `rocprofv3 --pmc FETCH_SIZE` (then WRITE_SIZE): the copy
+    (an elementwise multiply by one reading and writing COPY_BYTES) calibrates
+    the counters, which are then read per dispatch for each kernel."""
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.mul(src, 1, out=dst)
+    torch.cuda.synchronize()
+    log("copy done")
+    # prefill: one anchor layer and one reuse layer of the 32K prompt
+    cfg = configs.CONFIGS[4]
+    N = cfg.ctx_len
+    lin = synth.heavy_lineages(cfg.seed, cfg.n_layers, cfg.n_kv_heads, N, cfg.heavy, cfg.drift)
+    maps = synth.head_maps(cfg.seed, cfg.n_layers, cfg.anchors, cfg.n_kv_heads, cfg.head_map_kind)
+    lay = [synth.prefill_layer(cfg.seed, l, 1, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, N,
+                               synth.layer_heavy_sets(lin, l, cfg.anchors, maps), cfg.alpha,
+                               cfg.gamma, cfg.dtype, device="cuda") for l in (0, 1)]
+    rule = K.PREFILL_RULE
+    sh = K.make_shape(lay[0][0], lay[0][1], N)
+    ws = K.workspace(K.OP_ANCHOR_PREFILL, sh, 0, rule)
+    T = N // rule.tile
+    kmax = K.kascade_topk_for_len(N, rule)
+    idx = torch.empty((1, T, cfg.n_kv_heads, kmax), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(lay[0][0])
+    K.check(K.kascade_anchor_prefill(sh, *lay[0], rule, out, None, idx, None, ws, ws.numel()),
+            "anchor_prefill")
+    K.check(K.kascade_reuse_prefill(sh, *lay[1], rule, idx, maps[1], out, None, 0), "reuse_prefill")
+    torch.cuda.synchronize()
+    del lay, out, ws, idx
+    log("prefill done")
+    # decode: one anchor and one reuse layer at 128K context, batch 4
+    cfg = configs.CONFIGS[3]
+    N = cfg.ctx_len
+    lin = synth.heavy_lineages(cfg.seed, cfg.n_layers, cfg.n_kv_heads, N, cfg.heavy, cfg.drift)
+    maps = synth.head_maps(cfg.seed, cfg.n_layers, cfg.anchors, cfg.n_kv_heads, cfg.head_map_kind)
+    lay = [synth.decode_layer(cfg.seed, l, cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, N,
+                              synth.layer_heavy_sets(lin, l, cfg.anchors, maps), cfg.alpha, cfg.dtype,
+                              device="cuda") for l in (0, 1)]
+    sh = K.make_shape(lay[0][0], lay[0][1], N)
+    ws_a = K.workspace(K.OP_ANCHOR_DECODE, sh, cfg.topk)
+    ws_r = K.workspace(K.OP_REUSE_DECODE, sh, cfg.topk)
+    idx = torch.empty((cfg.batch, cfg.n_kv_heads, cfg.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(lay[0][0])
+    K.check(K.kascade_anchor_decode(sh, *lay[0], cfg.topk, out, None, idx, None, ws_a, ws_a.numel()),
+            "anchor_decode")
+    K.check(K.kascade_reuse_decode(sh, *lay[1], cfg.topk, idx, maps[1], out, ws_r, ws_r.numel()),
+            "reuse_decode")
+    torch.cuda.synchronize()
+    log("decode done")
+    print(json.dumps({"probe": "traffic", "copy_bytes": COPY_BYTES,
+                      "hashes": {k: kernel_source_hash(k) for k in KERNEL_SOURCES}}), flush=True)
+
+
+# ---------------------------------------------------------------------------
 
 def main():
     ap = argparse.ArgumentParser()
@@ -193,6 +287,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["decode32k", "decode128k", "prefill"], default=None,
                     help="run one section only (profiling)")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="one launch of each kernel plus a calibration copy, for rocprofv3 --pmc")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -208,6 +304,9 @@ def main():
         sys.exit(3)
     K.lib()  # fails loudly when the HIP library is missing
     torch.cuda.set_device(0)
+    if args.traffic_probe:
+        traffic_probe(torch, K, synth, configs)
+        return
 
     sections = ["decode32k", "decode128k", "prefill"] if args.only is None else [args.only]
     log("building workloads", sections)
@@ -312,7 +411,7 @@ def main():
     names = {0: "decode_splitk", 1: "decode_combine", 2: "decode_pool", 3: "topk_select",
              4: "reuse_decode", 5: "prefill_flash", 6: "prefill_pool", 7: "prefill_sparse"}
     avg_ms = dom_ms / max(dom_n, 1)
-    roof = {"kernel": names[dom], "launches": dom_n, "avg_ms": avg_ms, "traffic": None}
+    roof = {"kernel": names[dom], "launches": dom_n, "avg_ms": avg_ms}
     if dom in (5, 6, 7) and "prefill" in sections:
         w = work["prefill"]
         if dom == 5:
@@ -323,7 +422,8 @@ def main():
             per_launch = w["reuse_flops"]() / w["n_reuse"]
         ach = per_launch / (avg_ms * 1e-3) / 1e12
         roof.update({"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": ach / BF16_PEAK_TFLOPS, "algorithmic_per_launch": per_launch})
+                     "frac": ach / BF16_PEAK_TFLOPS, "algorithmic_per_launch": per_launch,
+                     "traffic": stored_traffic(names[dom], "prefill32k")})
     else:
         # decode kernels: algorithmic bytes of the launch (cache K+V or gathered rows)
         s = "decode128k" if "decode128k" in sections else "decode32k"
@@ -331,7 +431,8 @@ def main():
         per_launch = w["bytes_reuse"] if dom == 4 else w["bytes_anchor"]
         ach = per_launch / (avg_ms * 1e-3) / 1e9
         roof.update({"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "algorithmic_per_launch": per_launch})
+                     "frac": ach / HBM_PEAK_GBS, "algorithmic_per_launch": per_launch,
+                     "traffic": stored_traffic(names[dom], s)})
 
     ms_per_step = wall * 1e3 / args.steps
     value = comps.get("decode32k", {}).get("us_per_layer")
