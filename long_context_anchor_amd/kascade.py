@@ -50,6 +50,8 @@ class TopkRule(ctypes.Structure):
 
 
 PREFILL_RULE = TopkRule(128, 10, 64, 256)
+# decode k for a context of n keys: 10% of n to the nearest multiple of 64, at least 128
+DECODE_RULE = TopkRule(128, 10, 64, 128)
 
 
 class KascadeError(RuntimeError):

@@ -164,8 +164,7 @@ def prefill_layer(seed: int, layer: int, batch: int, n_q: int, n_kv: int, d: int
     n_max = n_max or n
     G = n_q // n_kv
     gen = _tgen(device, seed, 202, layer)
-    u = _randn((n_kv, d), gen, device)
-    u = u / u.norm(dim=-1, keepdim=True)
+    u = _unit_rows(_randn((n_kv, d), gen, device))
     td = _DT[dtype]
     q = torch.empty((batch, n_q, n, d), device=device, dtype=td)
     k = torch.zeros((batch, n_kv, n_max, d), device=device, dtype=td)
@@ -181,6 +180,29 @@ def prefill_layer(seed: int, layer: int, batch: int, n_q: int, n_kv: int, d: int
         k[:, g, :n] = kk.to(td)
         v[:, g, :n] = _randn((batch, n, d), gen, device).to(td)
     return q, k, v
+
+
+def _unit_rows(x: torch.Tensor) -> torch.Tensor:
+    return x / x.norm(dim=-1, keepdim=True)
+
+
+def prefill_directions(seed: int, layer: int, n_kv: int, d: int, device="cpu") -> torch.Tensor:
+    """The per-KV-head unit directions u [n_kv, d] that prefill_layer plants
+    (the first draw of the same generator)."""
+    return _unit_rows(_randn((n_kv, d), _tgen(device, seed, 202, layer), device))
+
+
+def decode_step(seed: int, layer: int, step: int, batch: int, n_q: int, n_kv: int, d: int,
+                u: torch.Tensor, gamma: float, dtype: str, device="cpu"):
+    """Inputs of one generated token after a prefill: the query [B,Hq,d] is
+    z + gamma*u[h // G] and the appended K and V rows [B,Hkv,d] are N(0,1)."""
+    G = n_q // n_kv
+    gen = _tgen(device, seed, 505, layer, step)
+    q = _randn((batch, n_q, d), gen, device) + gamma * u.repeat_interleave(G, dim=0)
+    k_row = _randn((batch, n_kv, d), gen, device)
+    v_row = _randn((batch, n_kv, d), gen, device)
+    td = _DT[dtype]
+    return q.to(td), k_row.to(td), v_row.to(td)
 
 
 def score_rows(seed: int, rows: int, n: int, kind: str = "normal", device="cpu") -> torch.Tensor:

@@ -1,0 +1,294 @@
+"""End-to-end GPU parity on the Qwen3-8B-shaped workload (36 layers, 32 query /
+8 KV heads, d 128, bf16): anchors chosen by the oracle's DP on a seeded
+similarity matrix, "learned-looking" many-to-one head maps, a 65536-token
+causal prefill through every layer, then 512 generated tokens, each appending
+one K/V row per layer to caches of 66048 rows (k grows 6528 -> 6592).
+
+Everything runs through the C ABI.  The oracle (fp64, CPU) checks sampled
+prefill tiles of two anchor layers and two reuse layers, and four decode
+steps of an anchor layer and a reuse layer, on the very tensors the GPU used.
+Tolerances as in the other GPU tests: outputs max-abs 2e-2, lse 1e-3, index
+sets equal up to entries within 1e-5 (relative) of the oracle's k-th pooled
+value.  A decode step captured as one HIP graph is replayed and compared
+bitwise with the same step run eagerly.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_anchor_amd import configs, synth
+from long_context_anchor_amd import kascade as K
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+RULE = K.PREFILL_RULE
+CFG = configs.CONFIGS[5]
+N0 = CFG.ctx_len                       # prompt length
+N_MAX = N0 + CFG.decode_steps          # cache rows
+TILES = [0, 1, 20, 300, N0 // 128 - 1]
+STEPS = [0, 1, 255, CFG.decode_steps - 1]
+
+
+def DEC_K(n):
+    """Decode k for a context of n keys, from the library; the oracle's rule agrees."""
+    k = K.kascade_topk_for_len(n, K.DECODE_RULE)
+    assert k == oracle.topk_for_len(n)
+    return k
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def np64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+@pytest.fixture(scope="module")
+def run():
+    """Runs the whole workload on the GPU once and keeps what the checks need."""
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    L, Hq, Hkv, d, G = CFG.n_layers, CFG.n_q_heads, CFG.n_kv_heads, CFG.head_dim, CFG.group
+    S = synth.similarity_matrix(CFG.seed, L)
+    anchors, _ = oracle.dp_select_anchors(S, CFG.n_anchor_dp)
+    maps = synth.head_maps(CFG.seed, L, anchors, Hkv, "learned")
+    lin = synth.heavy_lineages(CFG.seed, L, Hkv, N0, CFG.heavy, CFG.drift)
+    anchor_of = {l: max(a for a in anchors if a <= l) for l in range(L)}
+    reuse_chk = [min(l for l in range(L) if l not in anchors), L - 1]
+    gs_chk = [0, Hkv - 1]                 # reuse KV heads checked
+    anchor_heads = {}                     # anchor layer -> anchor KV heads checked
+    for r in reuse_chk:
+        anchor_heads.setdefault(anchor_of[r], set()).update(int(maps[r][g]) for g in gs_chk)
+    anchor_heads.setdefault(anchors[0], set()).update([0])
+    say("e2e: anchors", anchors, "reuse checked", reuse_chk, "anchor heads", anchor_heads)
+
+    kmax = K.prefill_k_max(N0, RULE)
+    T = N0 // RULE.tile
+    caches, tile_idx = {}, {}
+    keep = {}                              # host copies for the prefill checks
+    ws_p = None
+    for l in range(L):
+        say("e2e prefill layer", l, "anchor" if l in anchors else "reuse")
+        q, k, v = synth.prefill_layer(CFG.seed, l, 1, Hq, Hkv, d, N0,
+                                      synth.layer_heavy_sets(lin, l, anchors, maps),
+                                      CFG.alpha, CFG.gamma, "bf16", device=DEV, n_max=N_MAX)
+        sh = K.make_shape(q, k, N0)
+        out = torch.empty_like(q)
+        if l in anchors:
+            if ws_p is None:
+                ws_p = K.workspace(K.OP_ANCHOR_PREFILL, sh, 0, RULE)
+            idx = torch.empty((1, T, Hkv, kmax), dtype=torch.int32, device=DEV)
+            lse = torch.empty((1, Hq, N0), dtype=torch.float32, device=DEV)
+            K.check(K.kascade_anchor_prefill(sh, q, k, v, RULE, out, lse, idx, None, ws_p,
+                                             ws_p.numel()), "anchor_prefill")
+            tile_idx[l] = idx
+        else:
+            lse = None
+            K.check(K.kascade_reuse_prefill(sh, q, k, v, RULE, tile_idx[anchor_of[l]], maps[l], out,
+                                            None, 0), "reuse_prefill")
+        torch.cuda.synchronize()
+        if l in anchor_heads or l in reuse_chk:
+            heads_g = sorted(anchor_heads[l]) if l in anchor_heads else gs_chk
+            rec = {"q": {}, "k": {}, "v": {}, "out": {}, "lse": {}}
+            for g in heads_g:
+                rec["q"][g] = np64(q[:, g * G:(g + 1) * G])
+                rec["k"][g] = np64(k[:, g:g + 1, :N0])
+                rec["v"][g] = np64(v[:, g:g + 1, :N0])
+                rec["out"][g] = np64(out[:, g * G:(g + 1) * G])
+                if lse is not None:
+                    rec["lse"][g] = lse[:, g * G:(g + 1) * G].cpu().numpy().astype(np.float64)
+            if l in anchor_heads:
+                rec["idx"] = tile_idx[l].cpu().numpy()
+            keep[l] = rec
+        caches[l] = (k, v)
+        del q, out, lse
+
+    # ---- decode: 512 generated tokens --------------------------------------
+    dirs = {l: synth.prefill_directions(CFG.seed, l, Hkv, d, device=DEV) for l in range(L)}
+    k_last = DEC_K(N_MAX)
+    sh_max = K.make_shape(torch.empty((1, Hq, d), device=DEV, dtype=torch.bfloat16),
+                          caches[0][0], N_MAX)
+    ws_a = K.workspace(K.OP_ANCHOR_DECODE, sh_max, k_last)
+    ws_r = K.workspace(K.OP_REUSE_DECODE, sh_max, k_last)
+    dec_idx = {a: torch.empty((1, Hkv, k_last), dtype=torch.int32, device=DEV) for a in anchors}
+    outs = {l: torch.empty((1, Hq, d), dtype=torch.bfloat16, device=DEV) for l in range(L)}
+    dec_keep = {}
+    dec_layers = [anchors[0], anchor_of[L - 1], L - 1]
+
+    def decode_step(s, qs):
+        n_cur = N0 + s + 1
+        kk = DEC_K(n_cur)
+        for l in range(L):
+            k, v = caches[l]
+            sh = K.make_shape(qs[l], k, n_cur)
+            if l in anchors:
+                K.check(K.kascade_anchor_decode(sh, qs[l], k, v, kk, outs[l], None, dec_idx[l], None,
+                                                ws_a, ws_a.numel()), "anchor_decode")
+            else:
+                K.check(K.kascade_reuse_decode(sh, qs[l], k, v, kk, dec_idx[anchor_of[l]], maps[l],
+                                               outs[l], ws_r, ws_r.numel()), "reuse_decode")
+        return kk
+
+    qs = {}
+    for s in range(CFG.decode_steps):
+        n_cur = N0 + s + 1
+        for l in range(L):
+            q, kr, vr = synth.decode_step(CFG.seed, l, s, 1, Hq, Hkv, d, dirs[l], CFG.gamma, "bf16",
+                                          device=DEV)
+            caches[l][0][:, :, n_cur - 1] = kr
+            caches[l][1][:, :, n_cur - 1] = vr
+            qs[l] = q
+        kk = decode_step(s, qs)
+        if s in STEPS:
+            torch.cuda.synchronize()
+            say("e2e decode step", s, "ctx", n_cur, "k", kk)
+            # the lists are [B, Hkv, k] contiguous at the step's k
+            dec_keep[s] = {l: (qs[l].clone(), outs[l].clone(),
+                               dec_idx[l].view(-1)[:Hkv * kk].view(1, Hkv, kk).clone()
+                               if l in anchors else None)
+                           for l in dec_layers}
+    torch.cuda.synchronize()
+    return dict(anchors=anchors, maps=maps, anchor_of=anchor_of, reuse_chk=reuse_chk, gs_chk=gs_chk,
+                anchor_heads=anchor_heads, keep=keep, caches=caches, dec_keep=dec_keep,
+                dec_layers=dec_layers, decode_step=decode_step, qs=qs, outs=outs, dec_idx=dec_idx,
+                S=S)
+
+
+def _oracle_tile_lists(rec, g, t):
+    """The oracle's pooled row and Top-k list of tile t for anchor KV head g."""
+    P, kt = oracle.prefill_tile_k(t, N0)
+    pooled = oracle.tile_pool_one(rec["q"][g], rec["k"][g], 0, t, 0)
+    return pooled, oracle.topk_full_sort(pooled, kt), kt
+
+
+@pytest.mark.timeout(900)
+def test_e2e_schedule(run):
+    """The DP's anchors (layer 0 always among them) and the head maps used."""
+    anchors = run["anchors"]
+    assert len(anchors) == CFG.n_anchor_dp and anchors[0] == 0
+    assert anchors == sorted(set(anchors))
+    best = oracle.coverage_score(run["S"], anchors)
+    # no single-anchor move improves the DP's coverage
+    for i in range(1, len(anchors)):
+        for c in range(1, CFG.n_layers):
+            if c in anchors:
+                continue
+            alt = sorted(anchors[:i] + [c] + anchors[i + 1:])
+            assert oracle.coverage_score(run["S"], alt) <= best + 1e-12
+    for l, m in run["maps"].items():
+        assert m.shape == (CFG.n_kv_heads,) and m.min() >= 0 and m.max() < CFG.n_kv_heads
+
+
+@pytest.mark.timeout(600)
+def test_e2e_prefill_anchor_layers(run):
+    G = CFG.group
+    for a, heads in sorted(run["anchor_heads"].items()):
+        rec = run["keep"][a]
+        for g in sorted(heads):
+            for t in TILES:
+                say("e2e anchor prefill layer", a, "g", g, "tile", t)
+                rows = list(range(128 * t, 128 * (t + 1)))
+                for hh in (0, G - 1):
+                    ro, rl, _ = oracle.dense_prefill_rows(rec["q"][g], rec["k"][g], rec["v"][g], 0, hh,
+                                                          rows)
+                    assert np.max(np.abs(rec["out"][g][0, hh, rows] - ro)) <= 2e-2
+                    assert np.max(np.abs(rec["lse"][g][0, hh, rows] - rl)) <= 1e-3
+                pooled, ref, kt = _oracle_tile_lists(rec, g, t)
+                row = rec["idx"][0, t, g]
+                assert np.all(row[kt:] == -1)
+                sel = row[:kt]
+                assert np.all(np.diff(sel) > 0)
+                ok, nd = oracle.index_sets_agree(sel, ref, pooled)
+                assert ok, (a, g, t, nd)
+
+
+@pytest.mark.timeout(600)
+def test_e2e_prefill_reuse_layers(run):
+    G = CFG.group
+    for r in run["reuse_chk"]:
+        a = run["anchor_of"][r]
+        hm = run["maps"][r]
+        rec, arec = run["keep"][r], run["keep"][a]
+        for g in run["gs_chk"]:
+            ga = int(hm[g])
+            for t in TILES:
+                say("e2e reuse prefill layer", r, "g", g, "-> anchor", a, "head", ga, "tile", t)
+                _, ref, kt = _oracle_tile_lists(arec, ga, t)
+                lists = -np.ones((1, N0 // 128, 1, K.prefill_k_max(N0, RULE)), dtype=np.int64)
+                lists[0, t, 0, :kt] = ref
+                rows = list(range(128 * t, 128 * (t + 1), 7))
+                for hh in (0, G - 1):
+                    want = oracle.sparse_prefill_rows(rec["q"][g], rec["k"][g], rec["v"][g], lists, [0],
+                                                      0, hh, rows)
+                    assert np.max(np.abs(rec["out"][g][0, hh, rows] - want)) <= 2e-2
+
+
+@pytest.mark.timeout(600)
+def test_e2e_decode_steps(run):
+    anchors, maps, anchor_of = run["anchors"], run["maps"], run["anchor_of"]
+    a0, a_last, r = run["dec_layers"]
+    k_all = {l: np64(run["caches"][l][0]) for l in (a0, a_last, r)}
+    v_all = {l: np64(run["caches"][l][1]) for l in (a0, a_last, r)}
+    for s in STEPS:
+        n_cur = N0 + s + 1
+        kk = DEC_K(n_cur)
+        rec = run["dec_keep"][s]
+        ref_idx = {}
+        for a in sorted({a0, a_last}):
+            say("e2e decode anchor", a, "step", s, "ctx", n_cur, "k", kk)
+            q, out, idx = rec[a]
+            ro, rl, rp, ri = oracle.anchor_decode(np64(q), k_all[a][:, :, :n_cur], v_all[a][:, :, :n_cur],
+                                                  kk)
+            assert np.max(np.abs(np64(out) - ro)) <= 2e-2
+            gi = idx.cpu().numpy()
+            for g in range(CFG.n_kv_heads):
+                assert np.all(np.diff(gi[0, g]) > 0)
+                ok, nd = oracle.index_sets_agree(gi[0, g], ri[0, g], rp[0, g])
+                assert ok, (a, s, g, nd)
+            ref_idx[a] = ri
+        say("e2e decode reuse", r, "step", s)
+        q, out, _ = rec[r]
+        ro = oracle.reuse_decode(np64(q), k_all[r][:, :, :n_cur], v_all[r][:, :, :n_cur],
+                                 ref_idx[anchor_of[r]], maps[r])
+        assert np.max(np.abs(np64(out) - ro)) <= 2e-2
+
+
+@pytest.mark.timeout(300)
+def test_e2e_decode_step_graph_replay(run):
+    """One decode step (all 36 layers, last context length) captured as a HIP
+    graph; each replay equals the eager run bit for bit."""
+    s = CFG.decode_steps - 1
+    outs, dec_idx = run["outs"], run["dec_idx"]
+    run["decode_step"](s, run["qs"])
+    torch.cuda.synchronize()
+    eager = {l: o.clone() for l, o in outs.items()}
+    eager_idx = {a: i.clone() for a, i in dec_idx.items()}
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            run["decode_step"](s, run["qs"])
+    torch.cuda.current_stream().wait_stream(st)
+    for rep in range(3):
+        for o in outs.values():
+            o.zero_()
+        for i in dec_idx.values():
+            i.fill_(-7)
+        torch.cuda.synchronize()
+        say("graph replay", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for l, o in outs.items():
+            assert torch.equal(o.view(torch.int16), eager[l].view(torch.int16)), (rep, l)
+        for a, i in dec_idx.items():
+            assert torch.equal(i, eager_idx[a]), (rep, a)
+        # eager work between replays
+        run["decode_step"](s, run["qs"])
+        torch.cuda.synchronize()
