@@ -71,7 +71,14 @@ def build_decode(cfg_id, torch, K, synth, configs):
     out = torch.empty_like(layers[0][0])
     anchor_of = {l: max(a for a in cfg.anchors if a <= l) for l in range(L)}
 
+    ws_d = K.workspace(K.OP_DENSE_DECODE, sh)
+    lse = torch.empty(layers[0][0].shape[:2], dtype=torch.float32, device="cuda")
+
     def run(kind=None):
+        if kind == "dense":   # the GPU's own dense decode on every layer (comparison)
+            for q, k, v in layers:
+                K.check(K.kascade_dense_decode(sh, q, k, v, out, lse, ws_d, ws_d.numel()), "dense_decode")
+            return
         for l, (q, k, v) in enumerate(layers):
             if l in cfg.anchors:
                 if kind in (None, "anchor"):
@@ -87,8 +94,10 @@ def build_decode(cfg_id, torch, K, synth, configs):
     io = cfg.batch * cfg.n_q_heads * cfg.head_dim * e * 2 + cfg.batch * cfg.n_kv_heads * cfg.topk * 4
     bytes_anchor = 2 * cfg.batch * cfg.n_kv_heads * N * cfg.head_dim * e + io
     bytes_reuse = 2 * cfg.batch * cfg.n_kv_heads * cfg.topk * cfg.head_dim * e + io
+    bytes_dense = 2 * cfg.batch * cfg.n_kv_heads * N * cfg.head_dim * e + \
+        cfg.batch * cfg.n_q_heads * cfg.head_dim * e * 2
     return dict(cfg=cfg, run=run, n_anchor=n_anchor, n_reuse=n_reuse, bytes_anchor=bytes_anchor,
-                bytes_reuse=bytes_reuse, layers=layers, maps=maps)
+                bytes_reuse=bytes_reuse, bytes_dense=bytes_dense, layers=layers, maps=maps)
 
 
 def build_prefill(torch, K, synth, configs):
@@ -111,7 +120,13 @@ def build_prefill(torch, K, synth, configs):
     out = torch.empty_like(layers[0][0])
     anchor_of = {l: max(a for a in cfg.anchors if a <= l) for l in range(L)}
 
+    lse = torch.empty(layers[0][0].shape[:3], dtype=torch.float32, device="cuda")
+
     def run(kind=None):
+        if kind == "dense":   # the GPU's own dense causal prefill (comparison), one layer
+            q, k, v = layers[0]
+            K.check(K.kascade_dense_prefill(sh, q, k, v, out, lse), "dense_prefill")
+            return
         for l, (q, k, v) in enumerate(layers):
             if l in cfg.anchors:
                 if kind in (None, "anchor"):
@@ -369,7 +384,7 @@ def main():
         by = w["n_anchor"] * w["bytes_anchor"] + w["n_reuse"] * w["bytes_reuse"]
         # per-kind breakdown outside the timed steps
         per = {}
-        for kind, n in (("anchor", w["n_anchor"]), ("reuse", w["n_reuse"])):
+        for kind, n in (("anchor", w["n_anchor"]), ("reuse", w["n_reuse"]), ("dense", L)):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             reps = 5
             e0.record()
@@ -385,6 +400,9 @@ def main():
             "anchor_us": per["anchor"], "reuse_us": per["reuse"],
             "anchor_GBps": w["bytes_anchor"] / (per["anchor"] * 1e-6) / 1e9,
             "reuse_GBps": w["bytes_reuse"] / (per["reuse"] * 1e-6) / 1e9,
+            "dense_us_per_layer": per["dense"],
+            "dense_GBps": w["bytes_dense"] / (per["dense"] * 1e-6) / 1e9,
+            "speedup_vs_dense": per["dense"] / (sec_ms[s] * 1e3 / L),
             "context": w["cfg"].ctx_len, "batch": w["cfg"].batch, "topk": w["cfg"].topk,
         }
     if "prefill" in sections:
@@ -392,7 +410,7 @@ def main():
         rf = w["reuse_flops"]()
         fl = w["n_anchor"] * (w["flops_flash"] + w["flops_pool"]) + rf
         per = {}
-        for kind, n in (("anchor", w["n_anchor"]), ("reuse", w["n_reuse"])):
+        for kind, n in (("anchor", w["n_anchor"]), ("reuse", w["n_reuse"]), ("dense", 1)):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             w["run"](kind)
@@ -405,6 +423,11 @@ def main():
             "anchor_TFLOPs": (w["flops_flash"] + w["flops_pool"]) / (per["anchor"] * 1e-3) / 1e12,
             "reuse_TFLOPs": rf / w["n_reuse"] / (per["reuse"] * 1e-3) / 1e12,
             "mfma_frac": fl / (sec_ms["prefill"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "anchor_mfma_frac": (w["flops_flash"] + w["flops_pool"]) / (per["anchor"] * 1e-3) / 1e12
+            / BF16_PEAK_TFLOPS,
+            "dense_ms_per_layer": per["dense"],
+            "dense_TFLOPs": w["flops_flash"] / (per["dense"] * 1e-3) / 1e12,
+            "speedup_vs_dense": per["dense"] * w["cfg"].n_layers / sec_ms["prefill"],
         }
 
     # roofline of the dominant kernel

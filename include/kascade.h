@@ -39,6 +39,8 @@
  * Supported.  dtype F32 with head_dim 64, dtype BF16 with head_dim 128
  *             (one 256-byte K/V row in both cases).  Prefill: BF16,
  *             head_dim 128, tile 128, batch 1..65535, Hq/Hkv in {1,2,4,8}.
+ *             Decode: ctx_len * kv_stride_n * element size below 4 GiB
+ *             (one head's rows; 16.7M keys at 256 bytes per row).
  * Threads.    Calls are thread-safe on distinct streams with distinct
  *             workspaces.
  */

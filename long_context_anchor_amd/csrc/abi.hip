@@ -20,6 +20,10 @@ constexpr int kMaxDevices = 64;
 struct DeviceInfo {
   bool init = false;
   int select_cache_cap = 0;
+  int cus = 0;
+  // workgroups of each split-K variant resident per CU, [dtype][log2 G][kind]
+  // with kind 0 dense, 1 dense + score spill, 2 gather; 0 = not queried yet
+  int splitk_bpc[2][4][3] = {};
 };
 DeviceInfo g_dev[kMaxDevices];
 std::mutex g_dev_mu;
@@ -51,6 +55,11 @@ int device_setup(DeviceInfo** out) {
       return KASCADE_ERR_HIP;
     }
     d.select_cache_cap = cap;
+    e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) {
+      g_last_hip_error = (int)e;
+      return KASCADE_ERR_HIP;
+    }
     e = prefill_set_max_lds();
     if (e != hipSuccess) {
       g_last_hip_error = (int)e;
@@ -59,6 +68,26 @@ int device_setup(DeviceInfo** out) {
     d.init = true;
   }
   *out = &d;
+  return KASCADE_OK;
+}
+
+// Workgroup slots of the whole GPU for one split-K variant (CUs x resident
+// workgroups per CU), queried once per device and variant.
+int splitk_slots(DeviceInfo* d, int dtype, int G, bool gather, bool spill, int* slots) {
+  const int lg = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
+  const int kind = gather ? 2 : spill ? 1 : 0;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  int& b = d->splitk_bpc[dtype == KASCADE_BF16 ? 1 : 0][lg][kind];
+  if (b == 0) {
+    int n = 0;
+    hipError_t e = decode_splitk_blocks_per_cu(dtype, G, gather, spill, &n);
+    if (e != hipSuccess) {
+      g_last_hip_error = (int)e;
+      return KASCADE_ERR_HIP;
+    }
+    b = n < 1 ? 1 : n;
+  }
+  *slots = d->cus * b;
   return KASCADE_OK;
 }
 
@@ -146,6 +175,9 @@ int check_shape(const kascade_shape* s, bool prefill) {
   if (s->kv_stride_h < (int64_t)s->ctx_len * s->kv_stride_n && s->n_kv_heads > 1)
     return KASCADE_ERR_SHAPE;
   if (prefill && s->q_stride_n < d) return KASCADE_ERR_SHAPE;
+  // decode kernels address a head's rows with 32-bit byte offsets
+  if (!prefill && (int64_t)s->ctx_len * s->kv_stride_n * es > (int64_t)0xFFFFFF00)
+    return KASCADE_ERR_SHAPE;
   return KASCADE_OK;
 }
 
@@ -181,18 +213,44 @@ struct DecodePlan {
   size_t off_hist, off_scores, off_part, off_lse2, off_pooled, total;
 };
 
-DecodePlan plan_decode(const kascade_shape* s, int n_keys, bool spill, bool pooled_ws) {
+constexpr int kMinKeysPerSplit = 64;
+constexpr int kMaxSplitsPerRow = 2048;   // the combine keeps one weight per split in LDS
+constexpr int kMaxSlots = 2048;          // planning bound on resident workgroups
+
+// Splits per (batch, KV head) row.  The grid is sized to whole rounds of the
+// GPU's resident workgroup slots (a partial last round leaves most CUs idle
+// while a few finish), with at most kPlanMaxKeys keys per split when that
+// takes more than one round.  slots = 0 gives the largest split count any
+// slots <= kMaxSlots can produce (workspace sizing).
+int decode_splits(int64_t n_keys, int64_t rows, int slots, int* kps_out) {
+  int64_t S;
+  if (slots <= 0) {
+    S = kMaxSlots / rows + (n_keys + kPlanMaxKeys - 1) / kPlanMaxKeys;
+  } else {
+    const int64_t sl = slots > kMaxSlots ? kMaxSlots : slots;
+    const int64_t total = n_keys * rows;
+    const int64_t rounds = (total + sl * kPlanMaxKeys - 1) / (sl * kPlanMaxKeys);
+    S = sl * rounds / rows;
+  }
+  S = S < 1 ? 1 : S;
+  const int64_t min_kps = (n_keys + kMaxSplitsPerRow - 1) / kMaxSplitsPerRow;
+  int64_t kps = (n_keys + S - 1) / S;
+  kps = kps < min_kps ? min_kps : kps;
+  kps = (kps + 15) / 16 * 16;              // whole load instructions for the 4 waves
+  kps = kps < kMinKeysPerSplit ? kMinKeysPerSplit : kps;
+  *kps_out = (int)kps;
+  return (int)((n_keys + kps - 1) / kps);
+}
+
+DecodePlan plan_decode(const kascade_shape* s, int n_keys, bool spill, bool pooled_ws,
+                       int slots) {
   DecodePlan p;
   const int64_t rows = (int64_t)s->batch * s->n_kv_heads;
-  // about 1024 workgroups, 256..4096 keys each
-  int64_t per = (n_keys * rows + 1023) / 1024;
-  per = (per + 255) / 256 * 256;
-  per = per < 256 ? 256 : (per > 4096 ? 4096 : per);
-  // at most 2048 splits per row (the combine keeps one weight per split in LDS)
-  const int64_t min_per = ((n_keys + 2047) / 2048 + 255) / 256 * 256;
-  per = per < min_per ? min_per : per;
-  p.kps = (int)per;
-  p.splits = (int)((n_keys + per - 1) / per);
+  p.splits = decode_splits(n_keys, rows, slots, &p.kps);
+  // the workspace always has room for the largest plan
+  int kps_max = 0;
+  const int splits_ws = decode_splits(n_keys, rows, 0, &kps_max);
+  const int splits_room = splits_ws > p.splits ? splits_ws : p.splits;
   const int64_t BH = (int64_t)s->batch * s->n_q_heads;
   size_t off = 0;
   p.off_hist = off;
@@ -200,7 +258,7 @@ DecodePlan plan_decode(const kascade_shape* s, int n_keys, bool spill, bool pool
   p.off_scores = off;
   if (spill) off += align256((size_t)BH * s->ctx_len * 4);
   p.off_part = off;
-  off += align256((size_t)BH * p.splits * (s->head_dim + 2) * 4);
+  off += align256((size_t)BH * splits_room * (s->head_dim + 2) * 4);
   p.off_lse2 = off;
   off += align256((size_t)BH * 4);
   p.off_pooled = off;
@@ -311,9 +369,9 @@ size_t kascade_workspace_bytes(int op, const kascade_shape* s, int32_t topk,
   const bool prefill = op == 2 || op == 3 || op == 5;
   if (check_shape(s, prefill) != KASCADE_OK) return 0;
   switch (op) {
-    case 0: return plan_decode(s, s->ctx_len, true, true).total;
-    case 1: return topk >= 1 ? plan_decode(s, topk, false, false).total : 0;
-    case 4: return plan_decode(s, s->ctx_len, false, false).total;
+    case 0: return plan_decode(s, s->ctx_len, true, true, 0).total;
+    case 1: return topk >= 1 ? plan_decode(s, topk, false, false, 0).total : 0;
+    case 4: return plan_decode(s, s->ctx_len, false, false, 0).total;
     case 2: return check_rule(rule) == KASCADE_OK ? plan_prefill(s, rule, true).total : 0;
     case 3: return 0;
     case 5: return 0;
@@ -329,10 +387,14 @@ int kascade_anchor_decode(const kascade_shape* s, const void* q, const void* k, 
   if (!q || !k || !v || !out || !topk_idx) return KASCADE_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return KASCADE_ERR_ARG;
   if (topk < 1 || topk > s->ctx_len) return KASCADE_ERR_TOPK;
-  const DecodePlan p = plan_decode(s, s->ctx_len, true, true);
-  if (!ws || ws_bytes < p.total) return KASCADE_ERR_WORKSPACE;
+  if (!ws || ws_bytes < plan_decode(s, s->ctx_len, true, true, 0).total)
+    return KASCADE_ERR_WORKSPACE;
   DeviceInfo* dev = nullptr;
   if ((st = device_setup(&dev))) return st;
+  int slots = 0;
+  if ((st = splitk_slots(dev, s->dtype, s->n_q_heads / s->n_kv_heads, false, true, &slots)))
+    return st;
+  const DecodePlan p = plan_decode(s, s->ctx_len, true, true, slots);
   char* w = reinterpret_cast<char*>(ws);
   DecodeArgs a = decode_args(s, q, k, v, s->ctx_len, p, w);
   a.scores = reinterpret_cast<float*>(w + p.off_scores);
@@ -376,10 +438,14 @@ int kascade_reuse_decode(const kascade_shape* s, const void* q, const void* k, c
   if (topk < 1 || topk > s->ctx_len) return KASCADE_ERR_TOPK;
   HeadMap hm;
   if ((st = check_head_map(head_map, s->n_kv_heads, &hm))) return st;
-  const DecodePlan p = plan_decode(s, topk, false, false);
-  if (!ws || ws_bytes < p.total) return KASCADE_ERR_WORKSPACE;
+  if (!ws || ws_bytes < plan_decode(s, topk, false, false, 0).total) return KASCADE_ERR_WORKSPACE;
   DeviceInfo* dev = nullptr;
   if ((st = device_setup(&dev))) return st;
+  int slots = 0;
+  if ((st = splitk_slots(dev, s->dtype, s->n_q_heads / s->n_kv_heads, true, false, &slots)))
+    return st;
+  const DecodePlan p = plan_decode(s, topk, false, false, slots);
+  if (p.kps > kMaxGatherKeys) return KASCADE_ERR_SHAPE;
   char* w = reinterpret_cast<char*>(ws);
   DecodeArgs a = decode_args(s, q, k, v, topk, p, w);
   a.idx = idx;
@@ -403,10 +469,14 @@ int kascade_dense_decode(const kascade_shape* s, const void* q, const void* k, c
   if (st) return st;
   if (!q || !k || !v || !out) return KASCADE_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return KASCADE_ERR_ARG;
-  const DecodePlan p = plan_decode(s, s->ctx_len, false, false);
-  if (!ws || ws_bytes < p.total) return KASCADE_ERR_WORKSPACE;
+  if (!ws || ws_bytes < plan_decode(s, s->ctx_len, false, false, 0).total)
+    return KASCADE_ERR_WORKSPACE;
   DeviceInfo* dev = nullptr;
   if ((st = device_setup(&dev))) return st;
+  int slots = 0;
+  if ((st = splitk_slots(dev, s->dtype, s->n_q_heads / s->n_kv_heads, false, false, &slots)))
+    return st;
+  const DecodePlan p = plan_decode(s, s->ctx_len, false, false, slots);
   char* w = reinterpret_cast<char*>(ws);
   DecodeArgs a = decode_args(s, q, k, v, s->ctx_len, p, w);
   hipError_t e = timed(KASCADE_K_DECODE_SPLITK, stream,

@@ -23,6 +23,8 @@ namespace kc {
 namespace {
 
 constexpr int kThreads = 256;      // 4 waves
+constexpr int kListPad = 64;       // LDS list entries past the split that a step may read
+constexpr float kLazyLog2 = 8.f;   // slack of the lazily moved softmax reference (log2 units)
 
 template <typename T>
 struct Elem;
@@ -75,7 +77,6 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk(const DecodeArgs a) 
   // register footprint at two waves per SIMD
   constexpr int kRows = G >= 4 ? 8 : 16;
   constexpr int kWaveRows = 4 * kRows;
-  constexpr int kBlockRows = 4 * kWaveRows;
   __shared__ float s_m[4][G];
   __shared__ float s_l[4][G];
   __shared__ float s_o[4][G][D];
@@ -119,13 +120,18 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk(const DecodeArgs a) 
     for (int e = 0; e < EPL; ++e) o[hh][e] = 0.f;
   }
 
-  for (int c = k0 + wave * kWaveRows; c < k1; c += kBlockRows) {
+  // each wave takes a contiguous quarter of the split (a multiple of the 4
+  // rows one load instruction covers), so the waves finish together
+  const int per_wave = ((k1 - k0 + 15) >> 4) << 2;
+  const int w0 = k0 + wave * per_wave;
+  const int w1 = min(k1, w0 + per_wave);
+  for (int c = w0; c < w1; c += kWaveRows) {
     uint4 kr[kRows], vr[kRows];
     bool ok[kRows];
 #pragma unroll
     for (int t = 0; t < kRows; ++t) {
       const int r = c + 4 * t + gi;
-      ok[t] = r < k1;
+      ok[t] = r < w1;
       // gathered positions are clamped into the cache so a bad list cannot fault
       int64_t j = GATHER ? (ok[t] ? min(max(s_list[r - k0], 0), a.n_ctx - 1) : 0) : r;
       kr[t] = ok[t] ? ld16(kb + j * row_bytes) : make_uint4(0, 0, 0, 0);
@@ -148,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk(const DecodeArgs a) 
     if (SPILL) {
       // lane li writes the score of row t = li: consecutive floats per wave
       const int r = c + 4 * li + gi;
-      if (li < kRows && r < k1) {
+      if (li < kRows && r < w1) {
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
           float mine = sc[hh][0];
@@ -214,6 +220,304 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk(const DecodeArgs a) 
 #pragma unroll
       for (int e = 0; e < EPL; ++e) s_o[wave][hh][li * EPL + e] = o[hh][e];
     }
+  }
+  __syncthreads();
+  for (int x = tid; x < G * D; x += kThreads) {
+    const int hh = x / D, dd = x % D;
+    float M = kNegInf;
+    for (int q = 0; q < 4; ++q) M = fmaxf(M, s_m[q][hh]);
+    float L = 0.f, O = 0.f;
+    if (M != kNegInf) {
+      for (int q = 0; q < 4; ++q) {
+        const float w = exp2f_fast(s_m[q][hh] - M);
+        L = fmaf(s_l[q][hh], w, L);
+        O = fmaf(s_o[q][hh][dd], w, O);
+      }
+    }
+    float* pp = a.part + (((int64_t)b * a.Hq + g * G + hh) * a.n_splits + split) * (D + 2);
+    pp[2 + dd] = O;
+    if (dd == 0) {
+      pp[0] = M;
+      pp[1] = L;
+    }
+  }
+}
+
+// ---- bf16 split-K kernel with head slots ---------------------------------------
+//
+// The same work as k_decode_splitk for bf16 caches, laid out so that the
+// per-row softmax runs once per head instead of once per head per lane.
+// Lane li of a 16-lane row "owns" head own = li / (16/G) of the group and
+// keeps its partial dots in slot order: slot k holds head k ^ own.  A
+// reduce-scatter over the row (mirror, half mirror, xor 2, xor 1) then
+// leaves every lane with the full score of its own head for the row.  The
+// probabilities of the other heads come back through the same lane
+// exchanges, and P.V runs on pairs of rows with v_dot2c_f32_bf16 (P rounded
+// to bf16, fp32 accumulation), so a row costs 16 dot2 for the scores, 5 DPP
+// adds, one exp and 16 dot2 for the output per lane.
+
+// Lane moves within 16-lane rows; every control used here reads a lane of
+// the same row, so bound_ctrl never applies and no old value is needed.
+template <int CTRL>
+KC_INLINE uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
+}
+constexpr int DPP_XOR3 = 0x1B;    // quad_perm [3,2,1,0]
+constexpr int DPP_ROR8 = 0x128;   // row_ror:8, lane i <- i ^ 8 within 16 lanes
+
+// Value of a lane of the same 16-lane row whose own head is ours ^ K
+// (LG = log2 G).  Own heads are li >> (4 - LG), so any lane li ^ X with
+// X >> (4 - LG) == K will do; each case picks one or two DPP moves.
+template <int K, int LG>
+KC_INLINE uint32_t slot_xchg(uint32_t v) {
+  static_assert(K >= 1 && K < (1 << LG), "slot exchange");
+  if constexpr (LG == 1) {
+    return dpp_u<DPP_MIRROR>(v);                            // X = 15
+  } else if constexpr (LG == 2) {
+    if constexpr (K == 1) return dpp_u<DPP_HALF_MIRROR>(v);  // X = 7
+    else if constexpr (K == 2) return dpp_u<DPP_ROR8>(v);    // X = 8
+    else return dpp_u<DPP_MIRROR>(v);                        // X = 15
+  } else {
+    if constexpr (K == 1) return dpp_u<DPP_XOR2>(v);                              // X = 2
+    else if constexpr (K == 2) return dpp_u<DPP_XOR3>(dpp_u<DPP_HALF_MIRROR>(v));  // X = 4
+    else if constexpr (K == 3) return dpp_u<DPP_HALF_MIRROR>(v);                  // X = 7
+    else if constexpr (K == 4) return dpp_u<DPP_ROR8>(v);                         // X = 8
+    else if constexpr (K == 5) return dpp_u<DPP_XOR2>(dpp_u<DPP_ROR8>(v));         // X = 10
+    else if constexpr (K == 6) return dpp_u<DPP_XOR3>(dpp_u<DPP_MIRROR>(v));       // X = 12
+    else return dpp_u<DPP_MIRROR>(v);                                              // X = 15
+  }
+}
+// Reduce-scatter of G slot partials over a 16-lane row: returns, in every
+// lane, the row sum of the lane's own head (slot 0).
+template <int G>
+KC_INLINE float reduce_scatter(float (&s)[G]) {
+  constexpr int F0 = G - 1, F1 = (G - 1) >> 1, F2 = (G - 1) >> 2;
+  if constexpr (F0 > 0) {
+#pragma unroll
+    for (int k = 0; k < G / 2; ++k) s[k] += dpp_f<DPP_MIRROR>(s[k ^ F0]);
+  } else {
+    s[0] += dpp_f<DPP_MIRROR>(s[0]);
+  }
+  if constexpr (F1 > 0) {
+#pragma unroll
+    for (int k = 0; k < G / 4; ++k) s[k] += dpp_f<DPP_HALF_MIRROR>(s[k ^ F1]);
+  } else {
+    s[0] += dpp_f<DPP_HALF_MIRROR>(s[0]);
+  }
+  if constexpr (F2 > 0) {
+    s[0] += dpp_f<DPP_XOR2>(s[1]);
+  } else {
+    s[0] += dpp_f<DPP_XOR2>(s[0]);
+  }
+  s[0] += dpp_f<DPP_XOR1>(s[0]);
+  return s[0];
+}
+
+template <int G, int LG, int K = 1>
+KC_INLINE void slots_from_own(uint32_t own_v, uint32_t (&out)[G]) {
+  if constexpr (K == 1) out[0] = own_v;
+  if constexpr (K < G) {
+    out[K] = slot_xchg<K, LG>(own_v);
+    slots_from_own<G, LG, K + 1>(own_v, out);
+  }
+}
+
+template <int G, bool GATHER, bool SPILL, int kRows = 4>
+__global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeArgs a) {
+  constexpr int D = 128;
+  constexpr int LG = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
+  static_assert(kRows % 4 == 0, "list entries are read four at a time");
+  constexpr int kWaveRows = 4 * kRows;  // rows per wave per step
+  __shared__ float s_m[4][G];
+  __shared__ float s_l[4][G];
+  __shared__ float s_o[4][G][D];
+  extern __shared__ __align__(16) int32_t s_list[];   // kps + kListPad entries
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int gi = lane >> 4, li = lane & 15;
+  const int own = li >> (4 - LG);
+  const int k0 = split * a.keys_per_split;
+  const int k1 = min(a.n_keys, k0 + a.keys_per_split);
+
+  if (a.hist0 && split == 0) {
+    uint32_t* h0 = a.hist0 + ((int64_t)b * a.Hkv + g) * 2048;
+    for (int i = tid; i < 2048; i += kThreads) h0[i] = 0u;
+  }
+  if (GATHER) {
+    const int32_t* list = a.idx + (int64_t)b * a.idx_sb + (int64_t)a.hm.m[g] * a.idx_sg;
+    for (int i = tid; i < k1 - k0; i += kThreads) s_list[i] = list[k0 + i];
+    __syncthreads();
+  }
+
+  // query slices in slot order: slot k = head k ^ own of the group
+  uint4 qs[G];
+#pragma unroll
+  for (int k = 0; k < G; ++k) {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_sb +
+                         (int64_t)(g * G + (k ^ own)) * a.q_sh;
+    qs[k] = ld16(reinterpret_cast<const char*>(qp) + li * 16);
+  }
+  // 32-bit byte offsets from the head's base (the host keeps a head under 4 GiB)
+  const uint32_t row_bytes = (uint32_t)a.kv_sn * (uint32_t)sizeof(uint16_t);
+  const int64_t head_off = ((int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh) * (int64_t)sizeof(uint16_t);
+  const char* kbase = reinterpret_cast<const char*>(a.k) + head_off;
+  const char* vbase = reinterpret_cast<const char*>(a.v) + head_off;
+  const uint32_t lane_off = (uint32_t)li * 16u;
+
+  float m = kNegInf, l = 0.f;   // own head
+  float o[G][8];                // slot k: head k ^ own, elements 8 li .. 8 li + 7
+#pragma unroll
+  for (int k = 0; k < G; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[k][e] = 0.f;
+
+  // each wave takes a contiguous quarter of the split; in a step, lane group
+  // gi takes kRows consecutive rows
+  const int per_wave = ((k1 - k0 + 15) >> 4) << 2;
+  const int w0 = k0 + wave * per_wave;
+  const int w1 = min(k1, w0 + per_wave);
+  for (int c = w0; c < w1; c += kWaveRows) {
+    const bool full = c + kWaveRows <= w1;   // uniform over the wave
+    const int r0 = c + kRows * gi;
+    uint32_t off[kRows];
+    if (GATHER) {
+      // entries past w1 are read (the LDS list is padded) and replaced below
+#pragma unroll
+      for (int t4 = 0; t4 < kRows; t4 += 4) {
+        const int4 j4 = *reinterpret_cast<const int4*>(s_list + (r0 + t4 - k0));
+        const int jj[4] = {j4.x, j4.y, j4.z, j4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          // gathered positions are clamped into the cache so a bad list cannot fault
+          const int j = min(max(jj[u], 0), a.n_ctx - 1);
+          off[t4 + u] = (uint32_t)j * row_bytes + lane_off;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < kRows; ++t) off[t] = (uint32_t)min(r0 + t, w1 - 1) * row_bytes + lane_off;
+    }
+    uint4 kr[kRows], vr[kRows];
+#pragma unroll
+    for (int t = 0; t < kRows; ++t) kr[t] = ld16(kbase + off[t]);
+#pragma unroll
+    for (int t = 0; t < kRows; ++t) vr[t] = ld16(vbase + off[t]);
+    if (!full) {
+      // rows past the end: their V must not meet p = 0 as inf/nan
+#pragma unroll
+      for (int t = 0; t < kRows; ++t)
+        if (r0 + t >= w1) vr[t] = make_uint4(0, 0, 0, 0);
+    }
+
+    float sc[kRows];
+#pragma unroll
+    for (int t = 0; t < kRows; ++t) {
+      float part[G];
+#pragma unroll
+      for (int k = 0; k < G; ++k) part[k] = slice_dot(kr[t], qs[k], 0.f, uint16_t());
+      sc[t] = reduce_scatter<G>(part) * a.scale_log2;
+    }
+    if (!full) {
+#pragma unroll
+      for (int t = 0; t < kRows; ++t) sc[t] = (r0 + t < w1) ? sc[t] : kNegInf;
+    }
+    if (SPILL) {
+      // lane li = own * (16/G) + x writes rows t = x, x + 16/G, ... of its own head
+      constexpr int LPH = 16 >> LG;
+      const int x = li & (LPH - 1);
+      float* dst = a.scores + ((int64_t)b * a.Hq + g * G + own) * a.n_keys;
+#pragma unroll
+      for (int j = 0; j * LPH < kRows; ++j) {
+        float mine = sc[j * LPH];
+#pragma unroll
+        for (int u = 1; u < LPH && j * LPH + u < kRows; ++u) mine = (x == u) ? sc[j * LPH + u] : mine;
+        const int t = j * LPH + x;
+        if (t < kRows && r0 + t < w1) dst[r0 + t] = mine;
+      }
+    }
+    // Lazy rescaling: the reference max m only moves when a score exceeds it
+    // by more than kLazyLog2 (so p <= 2^kLazyLog2), and the rescale of the
+    // accumulators runs only in steps where some lane of the wave moves.
+    float cm = sc[0];
+#pragma unroll
+    for (int t = 1; t < kRows; ++t) cm = fmaxf(cm, sc[t]);
+    const bool move = cm > m + kLazyLog2;   // false while both are -inf
+    if (__any(move)) {
+      const float mn = move ? cm : m;
+      const float alpha = (mn == kNegInf) ? 1.f : exp2f_fast(m - mn);
+      m = mn;
+      l *= alpha;
+      uint32_t al[G];
+      slots_from_own<G, LG>(__float_as_uint(alpha), al);
+#pragma unroll
+      for (int k = 0; k < G; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[k][e] *= __uint_as_float(al[k]);
+    }
+    float p[kRows];
+    if (full && m != kNegInf) {
+#pragma unroll
+      for (int t = 0; t < kRows; ++t) p[t] = exp2f_fast(sc[t] - m);
+    } else {
+#pragma unroll
+      for (int t = 0; t < kRows; ++t) p[t] = (sc[t] == kNegInf) ? 0.f : exp2f_fast(sc[t] - m);
+    }
+#pragma unroll
+    for (int t = 0; t < kRows; ++t) l += p[t];
+#pragma unroll
+    for (int t = 0; t < kRows; t += 2) {
+      uint32_t pk[G];
+      slots_from_own<G, LG>(pack_bf16x2(p[t], p[t + 1]), pk);
+      const uint32_t w0v[4] = {vr[t].x, vr[t].y, vr[t].z, vr[t].w};
+      const uint32_t w1v[4] = {vr[t + 1].x, vr[t + 1].y, vr[t + 1].z, vr[t + 1].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // (row t, row t+1) pairs of elements 2j and 2j+1
+        const uint32_t ev = __builtin_amdgcn_perm(w1v[j], w0v[j], 0x05040100u);
+        const uint32_t od = __builtin_amdgcn_perm(w1v[j], w0v[j], 0x07060302u);
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+          o[k][2 * j] = dot2_bf16(ev, pk[k], o[k][2 * j]);
+          o[k][2 * j + 1] = dot2_bf16(od, pk[k], o[k][2 * j + 1]);
+        }
+      }
+    }
+  }
+
+  // merge the 4 lane-groups of each wave (lanes li, li+16, li+32, li+48 own
+  // the same head and output slice), then the 4 waves through LDS
+  {
+    float M = fmaxf(m, __shfl_xor(m, 16, 64));
+    M = fmaxf(M, __shfl_xor(M, 32, 64));
+    const float w = (M == kNegInf) ? 0.f : exp2f_fast(m - M);
+    float L = l * w;
+    L += __shfl_xor(L, 16, 64);
+    L += __shfl_xor(L, 32, 64);
+    uint32_t ws[G];
+    slots_from_own<G, LG>(__float_as_uint(w), ws);
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = o[k][e] * __uint_as_float(ws[k]);
+        x += __shfl_xor(x, 16, 64);
+        x += __shfl_xor(x, 32, 64);
+        o[k][e] = x;
+      }
+    }
+    m = M;
+    l = L;
+  }
+  if (gi == 0) {
+    if ((li & ((16 >> LG) - 1)) == 0) {
+      s_m[wave][own] = m;
+      s_l[wave][own] = l;
+    }
+#pragma unroll
+    for (int k = 0; k < G; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_o[wave][k ^ own][li * 8 + e] = o[k][e];
   }
   __syncthreads();
   for (int x = tid; x < G * D; x += kThreads) {
@@ -357,17 +661,49 @@ __global__ __launch_bounds__(256) void k_decode_pool(const PoolDecodeArgs a) {
   }
 }
 
+// bf16 caches run the head-slot kernel, fp32 caches the plain one.
+template <typename T, int G, bool GATHER, bool SPILL>
+constexpr void (*splitk_kernel())(const DecodeArgs) {
+  if constexpr (sizeof(T) == 2) return k_decode_splitk_slots<G, GATHER, SPILL>;
+  else return k_decode_splitk<T, G, GATHER, SPILL>;
+}
+
+template <typename T, int G>
+hipError_t splitk_blocks_t(bool gather, bool spill, int* blocks) {
+  if (gather)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        blocks, splitk_kernel<T, G, true, false>(), kThreads,
+        (kPlanMaxKeys + kListPad) * sizeof(int32_t));
+  if (spill)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, splitk_kernel<T, G, false, true>(),
+                                                        kThreads, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, splitk_kernel<T, G, false, false>(),
+                                                      kThreads, 0);
+}
+
+template <typename T>
+hipError_t splitk_blocks_g(int G, bool gather, bool spill, int* blocks) {
+  switch (G) {
+    case 1: return splitk_blocks_t<T, 1>(gather, spill, blocks);
+    case 2: return splitk_blocks_t<T, 2>(gather, spill, blocks);
+    case 4: return splitk_blocks_t<T, 4>(gather, spill, blocks);
+    case 8: return splitk_blocks_t<T, 8>(gather, spill, blocks);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename T, int G>
 hipError_t launch_splitk_t(const DecodeArgs& a, bool gather, hipStream_t s) {
   if (a.n_splits > kMaxSplits || a.n_splits < 1) return hipErrorInvalidValue;
+  if (gather && a.keys_per_split > kMaxGatherKeys) return hipErrorInvalidValue;
   dim3 grid(a.n_splits, a.Hkv, a.B);
   if (gather) {
-    size_t lds = (size_t)a.keys_per_split * sizeof(int32_t);
-    hipLaunchKernelGGL((k_decode_splitk<T, G, true, false>), grid, dim3(kThreads), lds, s, a);
+    size_t lds = (size_t)(a.keys_per_split + kListPad) * sizeof(int32_t);
+    hipLaunchKernelGGL((splitk_kernel<T, G, true, false>()), grid, dim3(kThreads), lds, s, a);
   } else if (a.scores) {
-    hipLaunchKernelGGL((k_decode_splitk<T, G, false, true>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((splitk_kernel<T, G, false, true>()), grid, dim3(kThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL((k_decode_splitk<T, G, false, false>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((splitk_kernel<T, G, false, false>()), grid, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -384,6 +720,11 @@ hipError_t launch_splitk_g(const DecodeArgs& a, bool gather, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t decode_splitk_blocks_per_cu(int dtype, int G, bool gather, bool spill, int* blocks) {
+  return dtype == 1 ? splitk_blocks_g<uint16_t>(G, gather, spill, blocks)
+                    : splitk_blocks_g<float>(G, gather, spill, blocks);
+}
 
 hipError_t launch_decode_splitk(const DecodeArgs& a, int dtype, bool gather, hipStream_t s) {
   return dtype == 1 ? launch_splitk_g<uint16_t>(a, gather, s) : launch_splitk_g<float>(a, gather, s);

@@ -84,6 +84,12 @@ struct PrefillArgs {
 };
 
 // Launchers: return hipSuccess or the launch error.
+// Largest split of a gathered list (its indices are staged in LDS), and the
+// split size the planner aims to stay under (the occupancy query assumes it).
+constexpr int kMaxGatherKeys = 16384;
+constexpr int kPlanMaxKeys = 4096;
+// Workgroups of the split-K kernel variant that fit on one CU at once.
+hipError_t decode_splitk_blocks_per_cu(int dtype, int G, bool gather, bool spill, int* blocks);
 hipError_t launch_decode_splitk(const DecodeArgs& a, int dtype, bool gather, hipStream_t s);
 hipError_t launch_decode_combine(const CombineArgs& a, int dtype, hipStream_t s);
 hipError_t launch_decode_pool(const PoolDecodeArgs& a, hipStream_t s);
