@@ -485,39 +485,62 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
     }
   }
 
-  // merge the 4 lane-groups of each wave (lanes li, li+16, li+32, li+48 own
-  // the same head and output slice), then the 4 waves through LDS
+  // Merge the 4 lane groups of each wave (rows gi of the wave; lanes li,
+  // li+16, li+32, li+48 own the same head and output slice) with
+  // v_permlane32_swap / v_permlane16_swap: for swap(a, b) the two results
+  // add up to a[l] + a[l^32] in lanes 0..31 and b[l^32] + b[l] in lanes
+  // 32..63 (rows of 16 lanes for the 16-lane swap).  Max and sums are
+  // exchanged in full; the G*8 output values are reduce-scattered in two
+  // halvings, after which lane (gi, li) holds values gi*2G .. gi*2G+2G-1 of
+  // its slot-major list (slot k, element e at k*8+e).
   {
-    float M = fmaxf(m, __shfl_xor(m, 16, 64));
-    M = fmaxf(M, __shfl_xor(M, 32, 64));
+    auto swap32 = [](float x, float y) {
+      return __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    };
+    auto swap16 = [](float x, float y) {
+      return __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    };
+    auto r0 = [](auto r) { return __uint_as_float(r[0]); };
+    auto r1 = [](auto r) { return __uint_as_float(r[1]); };
+    auto s32 = swap32(m, m);
+    float M = fmaxf(r0(s32), r1(s32));
+    auto s16 = swap16(M, M);
+    M = fmaxf(r0(s16), r1(s16));
     const float w = (M == kNegInf) ? 0.f : exp2f_fast(m - M);
     float L = l * w;
-    L += __shfl_xor(L, 16, 64);
-    L += __shfl_xor(L, 32, 64);
+    s32 = swap32(L, L);
+    L = r0(s32) + r1(s32);
+    s16 = swap16(L, L);
+    L = r0(s16) + r1(s16);
     uint32_t ws[G];
     slots_from_own<G, LG>(__float_as_uint(w), ws);
-#pragma unroll
-    for (int k = 0; k < G; ++k) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float x = o[k][e] * __uint_as_float(ws[k]);
-        x += __shfl_xor(x, 16, 64);
-        x += __shfl_xor(x, 32, 64);
-        o[k][e] = x;
-      }
-    }
-    m = M;
-    l = L;
-  }
-  if (gi == 0) {
-    if ((li & ((16 >> LG) - 1)) == 0) {
-      s_m[wave][own] = m;
-      s_l[wave][own] = l;
-    }
+    constexpr int N = 8 * G;
+    float v[N];
 #pragma unroll
     for (int k = 0; k < G; ++k)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_o[wave][k ^ own][li * 8 + e] = o[k][e];
+      for (int e = 0; e < 8; ++e) v[k * 8 + e] = o[k][e] * __uint_as_float(ws[k]);
+#pragma unroll
+    for (int n = 0; n < N / 2; ++n) {
+      const auto r = swap32(v[n], v[n + N / 2]);
+      v[n] = r0(r) + r1(r);
+    }
+#pragma unroll
+    for (int n = 0; n < N / 4; ++n) {
+      const auto r = swap16(v[n], v[n + N / 4]);
+      v[n] = r0(r) + r1(r);
+    }
+    // value n is list entry n + gi * N/4: slot (n + gi*N/4) / 8, element % 8
+    if (li % (16 >> LG) == 0 && gi == 0) {
+      s_m[wave][own] = M;
+      s_l[wave][own] = L;
+    }
+#pragma unroll
+    for (int n = 0; n < N / 4; n += 2) {
+      const int idx = n + gi * (N / 4);
+      const int k = idx >> 3, e = idx & 7;
+      *reinterpret_cast<float2*>(&s_o[wave][k ^ own][li * 8 + e]) = make_float2(v[n], v[n + 1]);
+    }
   }
   __syncthreads();
   for (int x = tid; x < G * D; x += kThreads) {
