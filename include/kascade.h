@@ -40,7 +40,9 @@
  *             (one 256-byte K/V row in both cases).  Prefill: BF16,
  *             head_dim 128, tile 128, batch 1..65535, Hq/Hkv in {1,2,4,8}.
  *             Decode: ctx_len * kv_stride_n * element size below 4 GiB
- *             (one head's rows; 16.7M keys at 256 bytes per row).
+ *             (one head's rows; 16.7M keys at 256 bytes per row); a bf16
+ *             anchor decode also needs ctx_len <= 2048 * spill split (about
+ *             8.6M keys for Hq/Hkv <= 4, 4.3M for 8), else KASCADE_ERR_SHAPE.
  * Threads.    Calls are thread-safe on distinct streams with distinct
  *             workspaces.
  */

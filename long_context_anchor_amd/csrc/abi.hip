@@ -21,9 +21,12 @@ struct DeviceInfo {
   bool init = false;
   int select_cache_cap = 0;
   int cus = 0;
-  // workgroups of each split-K variant resident per CU, [dtype][log2 G][kind]
-  // with kind 0 dense, 1 dense + score spill, 2 gather; 0 = not queried yet
+  size_t lds_per_cu = 0;
+  // split-K variants [dtype][log2 G][kind] (kind 0 dense, 1 dense + score
+  // spill, 2 gather): resident workgroups per CU without dynamic LDS (0 = not
+  // queried yet) and static LDS bytes
   int splitk_bpc[2][4][3] = {};
+  size_t splitk_lds[2][4][3] = {};
 };
 DeviceInfo g_dev[kMaxDevices];
 std::mutex g_dev_mu;
@@ -56,10 +59,15 @@ int device_setup(DeviceInfo** out) {
     }
     d.select_cache_cap = cap;
     e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int lds_cu = 0;
+    if (e == hipSuccess)
+      e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+    if (e == hipSuccess) e = decode_set_max_lds();
     if (e != hipSuccess) {
       g_last_hip_error = (int)e;
       return KASCADE_ERR_HIP;
     }
+    d.lds_per_cu = (size_t)lds_cu;
     e = prefill_set_max_lds();
     if (e != hipSuccess) {
       g_last_hip_error = (int)e;
@@ -71,23 +79,37 @@ int device_setup(DeviceInfo** out) {
   return KASCADE_OK;
 }
 
-// Workgroup slots of the whole GPU for one split-K variant (CUs x resident
-// workgroups per CU), queried once per device and variant.
-int splitk_slots(DeviceInfo* d, int dtype, int G, bool gather, bool spill, int* slots) {
+// Workgroup slots of the whole GPU for one split-K variant running splits of
+// kps keys: CUs x resident workgroups (registers or LDS, whichever binds).
+int splitk_slots(DeviceInfo* d, int dtype, int G, bool gather, bool spill, int kps, int* slots) {
   const int lg = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
   const int kind = gather ? 2 : spill ? 1 : 0;
-  std::lock_guard<std::mutex> lk(g_dev_mu);
-  int& b = d->splitk_bpc[dtype == KASCADE_BF16 ? 1 : 0][lg][kind];
-  if (b == 0) {
-    int n = 0;
-    hipError_t e = decode_splitk_blocks_per_cu(dtype, G, gather, spill, &n);
-    if (e != hipSuccess) {
-      g_last_hip_error = (int)e;
-      return KASCADE_ERR_HIP;
+  const int dt = dtype == KASCADE_BF16 ? 1 : 0;
+  int bpc;
+  size_t st;
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    int& b = d->splitk_bpc[dt][lg][kind];
+    if (b == 0) {
+      int n = 0;
+      size_t sl = 0;
+      hipError_t e = decode_splitk_attrs(dtype, G, gather, spill, &n, &sl);
+      if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return KASCADE_ERR_HIP;
+      }
+      b = n < 1 ? 1 : n;
+      d->splitk_lds[dt][lg][kind] = sl;
     }
-    b = n < 1 ? 1 : n;
+    bpc = b;
+    st = d->splitk_lds[dt][lg][kind];
   }
-  *slots = d->cus * b;
+  const size_t per_wg = st + decode_splitk_dyn_lds(dtype, G, gather, spill, kps);
+  if (per_wg > 0 && d->lds_per_cu > 0) {
+    const int by_lds = (int)(d->lds_per_cu / per_wg);
+    bpc = by_lds < bpc ? by_lds : bpc;
+  }
+  *slots = d->cus * (bpc < 1 ? 1 : bpc);
   return KASCADE_OK;
 }
 
@@ -219,17 +241,17 @@ constexpr int kMaxSlots = 2048;          // planning bound on resident workgroup
 
 // Splits per (batch, KV head) row.  The grid is sized to whole rounds of the
 // GPU's resident workgroup slots (a partial last round leaves most CUs idle
-// while a few finish), with at most kPlanMaxKeys keys per split when that
-// takes more than one round.  slots = 0 gives the largest split count any
+// while a few finish), with at most max_kps keys per split when that takes
+// more than one round.  slots = 0 gives the largest split count any
 // slots <= kMaxSlots can produce (workspace sizing).
-int decode_splits(int64_t n_keys, int64_t rows, int slots, int* kps_out) {
+int decode_splits(int64_t n_keys, int64_t rows, int slots, int64_t max_kps, int* kps_out) {
   int64_t S;
   if (slots <= 0) {
-    S = kMaxSlots / rows + (n_keys + kPlanMaxKeys - 1) / kPlanMaxKeys;
+    S = kMaxSlots / rows + (n_keys + max_kps - 1) / max_kps;
   } else {
     const int64_t sl = slots > kMaxSlots ? kMaxSlots : slots;
     const int64_t total = n_keys * rows;
-    const int64_t rounds = (total + sl * kPlanMaxKeys - 1) / (sl * kPlanMaxKeys);
+    const int64_t rounds = (total + sl * max_kps - 1) / (sl * max_kps);
     S = sl * rounds / rows;
   }
   S = S < 1 ? 1 : S;
@@ -242,14 +264,20 @@ int decode_splits(int64_t n_keys, int64_t rows, int slots, int* kps_out) {
   return (int)((n_keys + kps - 1) / kps);
 }
 
+int64_t decode_max_kps(const kascade_shape* s, bool spill) {
+  return spill && s->dtype == KASCADE_BF16 ? spill_max_keys(s->n_q_heads / s->n_kv_heads)
+                                           : kPlanMaxKeys;
+}
+
 DecodePlan plan_decode(const kascade_shape* s, int n_keys, bool spill, bool pooled_ws,
                        int slots) {
   DecodePlan p;
   const int64_t rows = (int64_t)s->batch * s->n_kv_heads;
-  p.splits = decode_splits(n_keys, rows, slots, &p.kps);
+  const int64_t max_kps = decode_max_kps(s, spill);
+  p.splits = decode_splits(n_keys, rows, slots, max_kps, &p.kps);
   // the workspace always has room for the largest plan
   int kps_max = 0;
-  const int splits_ws = decode_splits(n_keys, rows, 0, &kps_max);
+  const int splits_ws = decode_splits(n_keys, rows, 0, max_kps, &kps_max);
   const int splits_room = splits_ws > p.splits ? splits_ws : p.splits;
   const int64_t BH = (int64_t)s->batch * s->n_q_heads;
   size_t off = 0;
@@ -265,6 +293,21 @@ DecodePlan plan_decode(const kascade_shape* s, int n_keys, bool spill, bool pool
   if (pooled_ws) off += align256((size_t)rows * s->ctx_len * 4);
   p.total = off;
   return p;
+}
+
+// Plan with the slots the variant leaves at the largest split, then once more
+// if the planned split needs less LDS and so leaves more slots.
+int plan_decode_dev(DeviceInfo* d, const kascade_shape* s, int n_keys, bool gather, bool spill,
+                    bool pooled_ws, DecodePlan* p) {
+  const int G = s->n_q_heads / s->n_kv_heads;
+  int slots = 0, st;
+  if ((st = splitk_slots(d, s->dtype, G, gather, spill, (int)decode_max_kps(s, spill), &slots)))
+    return st;
+  *p = plan_decode(s, n_keys, spill, pooled_ws, slots);
+  int slots2 = 0;
+  if ((st = splitk_slots(d, s->dtype, G, gather, spill, p->kps, &slots2))) return st;
+  if (slots2 > slots) *p = plan_decode(s, n_keys, spill, pooled_ws, slots2);
+  return KASCADE_OK;
 }
 
 DecodeArgs decode_args(const kascade_shape* s, const void* q, const void* k, const void* v,
@@ -391,10 +434,9 @@ int kascade_anchor_decode(const kascade_shape* s, const void* q, const void* k, 
     return KASCADE_ERR_WORKSPACE;
   DeviceInfo* dev = nullptr;
   if ((st = device_setup(&dev))) return st;
-  int slots = 0;
-  if ((st = splitk_slots(dev, s->dtype, s->n_q_heads / s->n_kv_heads, false, true, &slots)))
-    return st;
-  const DecodePlan p = plan_decode(s, s->ctx_len, true, true, slots);
+  DecodePlan p;
+  if ((st = plan_decode_dev(dev, s, s->ctx_len, false, true, true, &p))) return st;
+  if (p.kps > decode_max_kps(s, true)) return KASCADE_ERR_SHAPE;   // LDS score buffer
   char* w = reinterpret_cast<char*>(ws);
   DecodeArgs a = decode_args(s, q, k, v, s->ctx_len, p, w);
   a.scores = reinterpret_cast<float*>(w + p.off_scores);
@@ -441,10 +483,8 @@ int kascade_reuse_decode(const kascade_shape* s, const void* q, const void* k, c
   if (!ws || ws_bytes < plan_decode(s, topk, false, false, 0).total) return KASCADE_ERR_WORKSPACE;
   DeviceInfo* dev = nullptr;
   if ((st = device_setup(&dev))) return st;
-  int slots = 0;
-  if ((st = splitk_slots(dev, s->dtype, s->n_q_heads / s->n_kv_heads, true, false, &slots)))
-    return st;
-  const DecodePlan p = plan_decode(s, topk, false, false, slots);
+  DecodePlan p;
+  if ((st = plan_decode_dev(dev, s, topk, true, false, false, &p))) return st;
   if (p.kps > kMaxGatherKeys) return KASCADE_ERR_SHAPE;
   char* w = reinterpret_cast<char*>(ws);
   DecodeArgs a = decode_args(s, q, k, v, topk, p, w);
@@ -473,10 +513,8 @@ int kascade_dense_decode(const kascade_shape* s, const void* q, const void* k, c
     return KASCADE_ERR_WORKSPACE;
   DeviceInfo* dev = nullptr;
   if ((st = device_setup(&dev))) return st;
-  int slots = 0;
-  if ((st = splitk_slots(dev, s->dtype, s->n_q_heads / s->n_kv_heads, false, false, &slots)))
-    return st;
-  const DecodePlan p = plan_decode(s, s->ctx_len, false, false, slots);
+  DecodePlan p;
+  if ((st = plan_decode_dev(dev, s, s->ctx_len, false, false, false, &p))) return st;
   char* w = reinterpret_cast<char*>(ws);
   DecodeArgs a = decode_args(s, q, k, v, s->ctx_len, p, w);
   hipError_t e = timed(KASCADE_K_DECODE_SPLITK, stream,

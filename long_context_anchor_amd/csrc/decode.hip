@@ -25,6 +25,7 @@ namespace {
 constexpr int kThreads = 256;      // 4 waves
 constexpr int kListPad = 64;       // LDS list entries past the split that a step may read
 constexpr float kLazyLog2 = 8.f;   // slack of the lazily moved softmax reference (log2 units)
+constexpr int kSpillPad = 16;      // per-head slack of the LDS score buffer
 
 template <typename T>
 struct Elem;
@@ -372,6 +373,12 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[k][e] = 0.f;
 
+  // Score spill (anchor pass): one lane per (head, lane group) keeps the
+  // group's scores in LDS ([G][kps + kSpillPad]); the split's scores leave in
+  // one coalesced burst after the loop.  Stores issued inside the loop would
+  // share vmcnt with the K/V loads and hold up every following wait.
+  float* const s_sc = reinterpret_cast<float*>(s_list);
+
   // each wave takes a contiguous quarter of the split; in a step, lane group
   // gi takes kRows consecutive rows
   const int per_wave = ((k1 - k0 + 15) >> 4) << 2;
@@ -422,18 +429,17 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
 #pragma unroll
       for (int t = 0; t < kRows; ++t) sc[t] = (r0 + t < w1) ? sc[t] : kNegInf;
     }
-    if (SPILL) {
-      // lane li = own * (16/G) + x writes rows t = x, x + 16/G, ... of its own head
-      constexpr int LPH = 16 >> LG;
-      const int x = li & (LPH - 1);
-      float* dst = a.scores + ((int64_t)b * a.Hq + g * G + own) * a.n_keys;
+    if (SPILL && (li & ((16 >> LG) - 1)) == 0) {
+      // rows past w1 belong to the next wave's range and are not written
+      float* dst = s_sc + own * (a.keys_per_split + kSpillPad) + (r0 - k0);
+      if (full) {
 #pragma unroll
-      for (int j = 0; j * LPH < kRows; ++j) {
-        float mine = sc[j * LPH];
+        for (int t4 = 0; t4 < kRows; t4 += 4)
+          *reinterpret_cast<float4*>(dst + t4) = make_float4(sc[t4], sc[t4 + 1], sc[t4 + 2], sc[t4 + 3]);
+      } else {
 #pragma unroll
-        for (int u = 1; u < LPH && j * LPH + u < kRows; ++u) mine = (x == u) ? sc[j * LPH + u] : mine;
-        const int t = j * LPH + x;
-        if (t < kRows && r0 + t < w1) dst[r0 + t] = mine;
+        for (int t = 0; t < kRows; ++t)
+          if (r0 + t < w1) dst[t] = sc[t];
       }
     }
     // Lazy rescaling: the reference max m only moves when a score exceeds it
@@ -482,6 +488,20 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
           o[k][2 * j + 1] = dot2_bf16(od, pk[k], o[k][2 * j + 1]);
         }
       }
+    }
+  }
+
+  if (SPILL) {
+    __syncthreads();
+    const int n = k1 - k0;
+    for (int hh = 0; hh < G; ++hh) {
+      const float* src = s_sc + hh * (a.keys_per_split + kSpillPad);
+      float* dst = a.scores + ((int64_t)b * a.Hq + g * G + hh) * a.n_keys + k0;
+      const int nv = (a.n_keys & 3) == 0 ? (n & ~3) : 0;   // 16-byte rows only
+      for (int i = tid * 4; i < nv; i += kThreads * 4)
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4_t*>(src + i),
+                                    reinterpret_cast<f32x4_t*>(dst + i));
+      for (int i = nv + tid; i < n; i += kThreads) __builtin_nontemporal_store(src[i], dst + i);
     }
   }
 
@@ -692,27 +712,32 @@ constexpr void (*splitk_kernel())(const DecodeArgs) {
 }
 
 template <typename T, int G>
-hipError_t splitk_blocks_t(bool gather, bool spill, int* blocks) {
-  if (gather)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks, splitk_kernel<T, G, true, false>(), kThreads,
-        (kPlanMaxKeys + kListPad) * sizeof(int32_t));
-  if (spill)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, splitk_kernel<T, G, false, true>(),
-                                                        kThreads, 0);
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, splitk_kernel<T, G, false, false>(),
-                                                      kThreads, 0);
+hipError_t splitk_attrs_t(bool gather, bool spill, int* blocks, size_t* static_lds) {
+  void (*k)(const DecodeArgs) = gather ? splitk_kernel<T, G, true, false>()
+                                : spill ? splitk_kernel<T, G, false, true>()
+                                        : splitk_kernel<T, G, false, false>();
+  hipFuncAttributes fa;
+  hipError_t e = hipFuncGetAttributes(&fa, (const void*)k);
+  if (e != hipSuccess) return e;
+  *static_lds = fa.sharedSizeBytes;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k, kThreads, 0);
 }
 
 template <typename T>
-hipError_t splitk_blocks_g(int G, bool gather, bool spill, int* blocks) {
+hipError_t splitk_attrs_g(int G, bool gather, bool spill, int* blocks, size_t* static_lds) {
   switch (G) {
-    case 1: return splitk_blocks_t<T, 1>(gather, spill, blocks);
-    case 2: return splitk_blocks_t<T, 2>(gather, spill, blocks);
-    case 4: return splitk_blocks_t<T, 4>(gather, spill, blocks);
-    case 8: return splitk_blocks_t<T, 8>(gather, spill, blocks);
+    case 1: return splitk_attrs_t<T, 1>(gather, spill, blocks, static_lds);
+    case 2: return splitk_attrs_t<T, 2>(gather, spill, blocks, static_lds);
+    case 4: return splitk_attrs_t<T, 4>(gather, spill, blocks, static_lds);
+    case 8: return splitk_attrs_t<T, 8>(gather, spill, blocks, static_lds);
   }
   return hipErrorInvalidValue;
+}
+
+template <int G>
+hipError_t spill_set_lds_g() {
+  return hipFuncSetAttribute((const void*)k_decode_splitk_slots<G, false, true>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSpillMaxLds);
 }
 
 template <typename T, int G>
@@ -724,7 +749,9 @@ hipError_t launch_splitk_t(const DecodeArgs& a, bool gather, hipStream_t s) {
     size_t lds = (size_t)(a.keys_per_split + kListPad) * sizeof(int32_t);
     hipLaunchKernelGGL((splitk_kernel<T, G, true, false>()), grid, dim3(kThreads), lds, s, a);
   } else if (a.scores) {
-    hipLaunchKernelGGL((splitk_kernel<T, G, false, true>()), grid, dim3(kThreads), 0, s, a);
+    const size_t lds = sizeof(T) == 2 ? spill_lds_bytes(G, a.keys_per_split) : 0;
+    if (lds > kSpillMaxLds) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((splitk_kernel<T, G, false, true>()), grid, dim3(kThreads), lds, s, a);
   } else {
     hipLaunchKernelGGL((splitk_kernel<T, G, false, false>()), grid, dim3(kThreads), 0, s, a);
   }
@@ -744,9 +771,33 @@ hipError_t launch_splitk_g(const DecodeArgs& a, bool gather, hipStream_t s) {
 
 }  // namespace
 
-hipError_t decode_splitk_blocks_per_cu(int dtype, int G, bool gather, bool spill, int* blocks) {
-  return dtype == 1 ? splitk_blocks_g<uint16_t>(G, gather, spill, blocks)
-                    : splitk_blocks_g<float>(G, gather, spill, blocks);
+size_t spill_lds_bytes(int G, int keys_per_split) {
+  return (size_t)G * (size_t)(keys_per_split + kSpillPad) * sizeof(float);
+}
+
+int spill_max_keys(int G) {
+  const int k = (int)(kSpillMaxLds / ((size_t)G * sizeof(float))) - kSpillPad;
+  return (k < kPlanMaxKeys ? k : kPlanMaxKeys) & ~15;
+}
+
+hipError_t decode_set_max_lds() {
+  hipError_t e;
+  if ((e = spill_set_lds_g<1>()) != hipSuccess) return e;
+  if ((e = spill_set_lds_g<2>()) != hipSuccess) return e;
+  if ((e = spill_set_lds_g<4>()) != hipSuccess) return e;
+  return spill_set_lds_g<8>();
+}
+
+hipError_t decode_splitk_attrs(int dtype, int G, bool gather, bool spill, int* blocks,
+                               size_t* static_lds) {
+  return dtype == 1 ? splitk_attrs_g<uint16_t>(G, gather, spill, blocks, static_lds)
+                    : splitk_attrs_g<float>(G, gather, spill, blocks, static_lds);
+}
+
+size_t decode_splitk_dyn_lds(int dtype, int G, bool gather, bool spill, int kps) {
+  if (gather) return (size_t)(kps + kListPad) * sizeof(int32_t);
+  if (spill && dtype == 1) return spill_lds_bytes(G, kps);
+  return 0;
 }
 
 hipError_t launch_decode_splitk(const DecodeArgs& a, int dtype, bool gather, hipStream_t s) {

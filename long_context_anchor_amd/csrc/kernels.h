@@ -88,8 +88,18 @@ struct PrefillArgs {
 // split size the planner aims to stay under (the occupancy query assumes it).
 constexpr int kMaxGatherKeys = 16384;
 constexpr int kPlanMaxKeys = 4096;
-// Workgroups of the split-K kernel variant that fit on one CU at once.
-hipError_t decode_splitk_blocks_per_cu(int dtype, int G, bool gather, bool spill, int* blocks);
+
+// A bf16 anchor split keeps its scores in LDS until it ends: at most
+// kSpillMaxLds bytes of them, i.e. spill_max_keys(G) keys per split.
+constexpr size_t kSpillMaxLds = 66 * 1024 + 1024;
+size_t spill_lds_bytes(int G, int keys_per_split);
+int spill_max_keys(int G);
+hipError_t decode_set_max_lds();
+// Split-K kernel variant: workgroups per CU without dynamic LDS, its static
+// LDS, and the dynamic LDS of a split of kps keys.
+hipError_t decode_splitk_attrs(int dtype, int G, bool gather, bool spill, int* blocks,
+                               size_t* static_lds);
+size_t decode_splitk_dyn_lds(int dtype, int G, bool gather, bool spill, int kps);
 hipError_t launch_decode_splitk(const DecodeArgs& a, int dtype, bool gather, hipStream_t s);
 hipError_t launch_decode_combine(const CombineArgs& a, int dtype, hipStream_t s);
 hipError_t launch_decode_pool(const PoolDecodeArgs& a, hipStream_t s);
