@@ -232,8 +232,14 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct DecodePlan {
   int kps, splits;
+  int wide_chunks;   // > 0: the anchor's select runs over chunks of many workgroups
   size_t off_hist, off_scores, off_part, off_lse2, off_pooled, total;
+  size_t off_hist1, off_ncand, off_cand, off_chunk, off_thr;
 };
+
+// Rows this long or longer are selected by the many-workgroup path.
+constexpr int kWideMinKeys = 4096;
+constexpr int kWideMaxChunks = 1024;
 
 constexpr int kMinKeysPerSplit = 64;
 constexpr int kMaxSplitsPerRow = 2048;   // the combine keeps one weight per split in LDS
@@ -291,6 +297,22 @@ DecodePlan plan_decode(const kascade_shape* s, int n_keys, bool spill, bool pool
   off += align256((size_t)BH * 4);
   p.off_pooled = off;
   if (pooled_ws) off += align256((size_t)rows * s->ctx_len * 4);
+  p.wide_chunks = 0;
+  p.off_hist1 = p.off_ncand = p.off_cand = p.off_chunk = p.off_thr = 0;
+  const int chunks = (s->ctx_len + kWideChunk - 1) / kWideChunk;
+  if (spill && s->ctx_len >= kWideMinKeys && chunks <= kWideMaxChunks) {
+    p.wide_chunks = chunks;
+    p.off_hist1 = off;
+    off += align256((size_t)rows * 2048 * 4);
+    p.off_ncand = off;
+    off += align256((size_t)rows * 4);
+    p.off_cand = off;
+    off += align256((size_t)rows * s->ctx_len * 4);
+    p.off_chunk = off;
+    off += align256((size_t)rows * chunks * 2 * 4);
+    p.off_thr = off;
+    off += align256((size_t)rows * 2 * 4);
+  }
   p.total = off;
   return p;
 }
@@ -441,6 +463,10 @@ int kascade_anchor_decode(const kascade_shape* s, const void* q, const void* k, 
   DecodeArgs a = decode_args(s, q, k, v, s->ctx_len, p, w);
   a.scores = reinterpret_cast<float*>(w + p.off_scores);
   a.hist0 = reinterpret_cast<uint32_t*>(w + p.off_hist);
+  if (p.wide_chunks) {
+    a.hist1 = reinterpret_cast<uint32_t*>(w + p.off_hist1);
+    a.ncand = reinterpret_cast<uint32_t*>(w + p.off_ncand);
+  }
   float* lse2 = reinterpret_cast<float*>(w + p.off_lse2);
   float* pooled = pooled_out ? pooled_out : reinterpret_cast<float*>(w + p.off_pooled);
   hipError_t e = timed(KASCADE_K_DECODE_SPLITK, stream,
@@ -454,6 +480,26 @@ int kascade_anchor_decode(const kascade_shape* s, const void* q, const void* k, 
                        s->ctx_len};
   e = timed(KASCADE_K_DECODE_POOL, stream, [&] { return launch_decode_pool(pa, stream); });
   if (e != hipSuccess) return hip_status(e);
+  if (p.wide_chunks) {
+    WideSelectArgs wa;
+    memset(&wa, 0, sizeof(wa));
+    wa.src = pooled;
+    wa.row_stride = s->ctx_len;
+    wa.rows = s->batch * s->n_kv_heads;
+    wa.n = s->ctx_len;
+    wa.k = topk;
+    wa.chunks = p.wide_chunks;
+    wa.idx = topk_idx;
+    wa.idx_stride = topk;
+    wa.hist0 = a.hist0;
+    wa.hist1 = a.hist1;
+    wa.ncand = a.ncand;
+    wa.cand = reinterpret_cast<uint32_t*>(w + p.off_cand);
+    wa.chunk_cnt = reinterpret_cast<uint32_t*>(w + p.off_chunk);
+    wa.thr = reinterpret_cast<uint32_t*>(w + p.off_thr);
+    e = timed(KASCADE_K_TOPK_SELECT, stream, [&] { return launch_topk_select_wide(wa, stream); });
+    return hip_status(e);
+  }
   SelectArgs sa;
   memset(&sa, 0, sizeof(sa));
   sa.src = pooled;

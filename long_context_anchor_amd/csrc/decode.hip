@@ -90,8 +90,14 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk(const DecodeArgs a) 
   const int k1 = min(a.n_keys, k0 + a.keys_per_split);
 
   if (a.hist0 && split == 0) {
-    uint32_t* h0 = a.hist0 + ((int64_t)b * a.Hkv + g) * 2048;
+    const int64_t row = (int64_t)b * a.Hkv + g;
+    uint32_t* h0 = a.hist0 + row * 2048;
     for (int i = tid; i < 2048; i += kThreads) h0[i] = 0u;
+    if (a.hist1) {
+      uint32_t* h1 = a.hist1 + row * 2048;
+      for (int i = tid; i < 2048; i += kThreads) h1[i] = 0u;
+      if (tid == 0) a.ncand[row] = 0u;
+    }
   }
   if (GATHER) {
     const int32_t* list = a.idx + (int64_t)b * a.idx_sb + (int64_t)a.hm.m[g] * a.idx_sg;
@@ -342,8 +348,14 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
   const int k1 = min(a.n_keys, k0 + a.keys_per_split);
 
   if (a.hist0 && split == 0) {
-    uint32_t* h0 = a.hist0 + ((int64_t)b * a.Hkv + g) * 2048;
+    const int64_t row = (int64_t)b * a.Hkv + g;
+    uint32_t* h0 = a.hist0 + row * 2048;
     for (int i = tid; i < 2048; i += kThreads) h0[i] = 0u;
+    if (a.hist1) {
+      uint32_t* h1 = a.hist1 + row * 2048;
+      for (int i = tid; i < 2048; i += kThreads) h1[i] = 0u;
+      if (tid == 0) a.ncand[row] = 0u;
+    }
   }
   if (GATHER) {
     const int32_t* list = a.idx + (int64_t)b * a.idx_sb + (int64_t)a.hm.m[g] * a.idx_sg;
@@ -584,74 +596,76 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
   }
 }
 
-// One workgroup per (batch, query head): merge the splits.  The split
-// weights 2^(m_s - M) are formed once in LDS; every thread then sums a
-// strided share of the splits for one output column (independent loads).
-constexpr int kCombineThreads = 256;
+// One workgroup per (batch, query head): merge the splits.  Thread
+// (part, dd) folds splits part, part + PARTS, ... into a running
+// (max, sum, output column dd) with all of its loads issued up front, then
+// the PARTS partial states of each column meet once in LDS.
+constexpr int kCombineThreads = 1024;
 constexpr int kMaxSplits = 2048;
 
 template <typename T>
 __global__ __launch_bounds__(kCombineThreads) void k_decode_combine(const CombineArgs a) {
   constexpr int D = Elem<T>::D;
   constexpr int PARTS = kCombineThreads / D;
-  __shared__ float sw[kMaxSplits];
-  __shared__ float sred[kCombineThreads];
+  constexpr int kBatch = 8;   // splits whose loads are in flight together
+  __shared__ float sm[PARTS][D], sl[PARTS][D], so[PARTS][D];
   const int bh = blockIdx.x, tid = threadIdx.x;
+  const int dd = tid % D, part = tid / D;
   const int S = a.n_splits;
   const float* p = a.part + (int64_t)bh * S * (D + 2);
 
-  float mx = kNegInf;
-  for (int s = tid; s < S; s += kCombineThreads) mx = fmaxf(mx, p[(int64_t)s * (D + 2)]);
-  sred[tid] = mx;
-  __syncthreads();
-  for (int o = kCombineThreads / 2; o > 0; o >>= 1) {
-    if (tid < o) sred[tid] = fmaxf(sred[tid], sred[tid + o]);
-    __syncthreads();
+  float M = kNegInf, L = 0.f, O = 0.f;
+  for (int s0 = part; s0 < S; s0 += PARTS * kBatch) {
+    float mv[kBatch], lv[kBatch], ov[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int s = s0 + u * PARTS;
+      const float* ps = p + (int64_t)min(s, S - 1) * (D + 2);
+      mv[u] = s < S ? ps[0] : kNegInf;
+      lv[u] = ps[1];
+      ov[u] = ps[2 + dd];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float mn = fmaxf(M, mv[u]);
+      if (mn == kNegInf) continue;   // nothing seen yet (empty splits)
+      const float sc = exp2f_fast(M - mn), w = exp2f_fast(mv[u] - mn);
+      L = fmaf(L, sc, lv[u] * w);
+      O = fmaf(O, sc, ov[u] * w);
+      M = mn;
+    }
   }
-  const float M = sred[0];
-  __syncthreads();
-  float lp = 0.f;
-  for (int s = tid; s < S; s += kCombineThreads) {
-    const float* ps = p + (int64_t)s * (D + 2);
-    const float w = exp2f_fast(ps[0] - M);
-    sw[s] = w;
-    lp = fmaf(ps[1], w, lp);
-  }
-  sred[tid] = lp;
-  __syncthreads();
-  for (int o = kCombineThreads / 2; o > 0; o >>= 1) {
-    if (tid < o) sred[tid] += sred[tid + o];
-    __syncthreads();
-  }
-  const float L = sred[0];
-  __syncthreads();
-  const int dd = tid % D, part = tid / D;
-  float O = 0.f;
-#pragma unroll 8
-  for (int s = part; s < S; s += PARTS) O = fmaf(p[(int64_t)s * (D + 2) + 2 + dd], sw[s], O);
-  sred[tid] = O;
+  sm[part][dd] = M;
+  sl[part][dd] = L;
+  so[part][dd] = O;
   __syncthreads();
   if (tid < D) {
-    float acc = 0.f;
+    float Mt = kNegInf;
 #pragma unroll
-    for (int q = 0; q < PARTS; ++q) acc += sred[q * D + tid];
-    const float r = acc / L;
+    for (int q = 0; q < PARTS; ++q) Mt = fmaxf(Mt, sm[q][tid]);
+    float Lt = 0.f, Ot = 0.f;
+    if (Mt != kNegInf) {
+#pragma unroll
+      for (int q = 0; q < PARTS; ++q) {
+        const float w = exp2f_fast(sm[q][tid] - Mt);
+        Lt = fmaf(sl[q][tid], w, Lt);
+        Ot = fmaf(so[q][tid], w, Ot);
+      }
+    }
+    const float r = Lt > 0.f ? Ot / Lt : 0.f;
     if constexpr (sizeof(T) == 2) {
       reinterpret_cast<uint16_t*>(a.out)[(int64_t)bh * D + tid] = (uint16_t)f32_to_bf16_bits(r);
     } else {
       reinterpret_cast<float*>(a.out)[(int64_t)bh * D + tid] = r;
     }
     if (tid == 0) {
-      const float lse2 = M + log2f_fast(L);
+      const float lse2 = Mt + log2f_fast(Lt);
       if (a.lse2) a.lse2[bh] = lse2;
       if (a.lse_out) a.lse_out[bh] = lse2 * kLn2;
     }
   }
 }
 
-// pooled[b,g,j] = sum over the G heads h of group g of 2^(s[b,h,j] - lse2[b,h]),
-// plus the row's histogram of key bits 31..21 (the select kernel's first
-// digit), counted in LDS and added to the row's global histogram.
 template <int G>
 __global__ __launch_bounds__(256) void k_decode_pool(const PoolDecodeArgs a) {
   __shared__ uint32_t sh[2048];

@@ -29,6 +29,8 @@ struct DecodeArgs {
   int64_t idx_sb, idx_sg;
   HeadMap hm;
   uint32_t* hist0;               // [B*Hkv][2048] zeroed here for the pooling kernel, or null
+  uint32_t* hist1;               // [B*Hkv][2048] zeroed here for the wide select, or null
+  uint32_t* ncand;               // [B*Hkv] zeroed here for the wide select, or null
 };
 
 struct CombineArgs {
@@ -104,6 +106,25 @@ hipError_t launch_decode_splitk(const DecodeArgs& a, int dtype, bool gather, hip
 hipError_t launch_decode_combine(const CombineArgs& a, int dtype, hipStream_t s);
 hipError_t launch_decode_pool(const PoolDecodeArgs& a, hipStream_t s);
 hipError_t launch_topk_select(const SelectArgs& a, hipStream_t s);
+
+// Exact Top-k of a few long fp32 rows (decode pooled rows) by chunks of
+// kWideChunk keys over many workgroups, in three passes.  hist0 is complete
+// (the pooling pass), hist1 and ncand are zero on entry.
+constexpr int kWideChunk = 2048;
+struct WideSelectArgs {
+  const float* src;              // [rows][row_stride]
+  int64_t row_stride;
+  int32_t rows, n, k, chunks;
+  int32_t* idx;                  // [rows][idx_stride]
+  int64_t idx_stride;
+  const uint32_t* hist0;         // [rows][2048]
+  uint32_t* hist1;               // [rows][2048]
+  uint32_t* cand;                // [rows][n] keys of the digit-0 bin
+  uint32_t* ncand;               // [rows]
+  uint32_t* chunk_cnt;           // [rows][chunks][2] (greater, equal) per chunk
+  uint32_t* thr;                 // [rows][2] the k-th key and how many equal keys to take
+};
+hipError_t launch_topk_select_wide(const WideSelectArgs& a, hipStream_t s);
 size_t topk_select_lds_bytes(int cache_cap);
 hipError_t topk_select_set_max_lds(size_t bytes);
 hipError_t launch_prefill_flash(const PrefillArgs& a, hipStream_t s);

@@ -321,6 +321,253 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const SelectArgs a)
 }  // namespace
 
 // LDS bytes of the select kernel for a given row cache capacity.
+// ---- wide select: few long rows, many workgroups per row ------------------
+//
+// The same radix select (digits of 11, 11 and 10 bits) and index-ordered
+// compaction as k_topk_select, spread over chunks of kWideChunk keys:
+//   pass A (chunks x rows): every chunk finds digit 0's bin from the complete
+//     histogram, counts digit 1 of its keys in that bin (LDS, then integer
+//     atomics into hist1) and appends those keys to the row's candidates;
+//   pass B (chunks x rows): every chunk resolves digits 1 and 2 (digit 2 over
+//     the candidates), which fixes the k-th largest key T and how many keys
+//     equal to T are taken, and counts its keys > T and == T;
+//   pass C (chunks x rows): every chunk sums the counts of the chunks before
+//     it and writes its selected indices in index order.
+// Every workgroup repeats the small histogram scans instead of waiting for
+// another; kernel boundaries order the passes.  Histograms are integer
+// atomics and candidate order is only ever counted, so the output is
+// deterministic.
+
+constexpr int kWideThreads = 256;
+constexpr int kWideWaves = kWideThreads / 64;
+constexpr int kPerThread = kWideChunk / kWideThreads;   // 8 consecutive keys
+
+// Exclusive prefix sum over the 256-thread block; `sh` holds >= 5 words.
+KC_INLINE uint32_t scan256(uint32_t x, uint32_t* sh, uint32_t& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kWideWaves; ++w) {
+    const uint32_t v = sh[w];
+    before += w < wave ? v : 0u;
+    tot += v;
+  }
+  __syncthreads();
+  total = tot;
+  return before + incl - x;
+}
+
+// Bin of a histogram (nb = 2048 or 1024 bins, global or LDS) holding the
+// need-th largest key, scanning from the top bin down; `above` receives the
+// count of keys in higher bins.  Thread t owns nb/256 consecutive bins
+// counted from the top.
+template <int NB>
+KC_INLINE uint32_t find_bin256(const uint32_t* hist, uint32_t need, uint32_t* sh, uint32_t* s_sel,
+                               uint32_t& above) {
+  constexpr int W = NB / kWideThreads;
+  const int tid = threadIdx.x;
+  const int hi = NB - W * tid;   // bins [hi - W, hi)
+  uint32_t h[W], tot = 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    h[i] = hist[hi - 1 - i];
+    tot += h[i];
+  }
+  if (tid == 0) {   // a histogram holding fewer than `need` keys selects bin 0
+    s_sel[0] = 0u;
+    s_sel[1] = 0u;
+  }
+  uint32_t all;
+  const uint32_t before = scan256(tot, sh, all);
+  if (before < need && before + tot >= need) {
+    uint32_t cum = before;
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      if (cum + h[i] >= need) {
+        s_sel[0] = (uint32_t)(hi - 1 - i);
+        s_sel[1] = cum;
+        break;
+      }
+      cum += h[i];
+    }
+  }
+  __syncthreads();
+  const uint32_t bin = s_sel[0];
+  above = s_sel[1];
+  __syncthreads();
+  return bin;
+}
+
+// The thread's 8 consecutive keys of chunk c (keys past n read as 0; every
+// use checks the position against n).
+KC_INLINE void chunk_keys(const WideSelectArgs& a, const float* src, int c, uint32_t (&key)[kPerThread],
+                          int& j0) {
+  j0 = c * kWideChunk + threadIdx.x * kPerThread;
+  const bool vec = (a.row_stride & 3) == 0 && ((reinterpret_cast<uintptr_t>(a.src) & 15) == 0);
+  if (vec && j0 + kPerThread <= a.n) {
+#pragma unroll
+    for (int q = 0; q < kPerThread; q += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(src + j0 + q);
+      key[q] = f32_order_key(v.x);
+      key[q + 1] = f32_order_key(v.y);
+      key[q + 2] = f32_order_key(v.z);
+      key[q + 3] = f32_order_key(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) key[q] = j0 + q < a.n ? f32_order_key(src[j0 + q]) : 0u;
+  }
+}
+
+__global__ __launch_bounds__(kWideThreads) void k_select_wide_a(const WideSelectArgs a) {
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t sh[8], s_sel[2], s_base;
+  const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  const float* src = a.src + (int64_t)row * a.row_stride;
+  uint32_t above;
+  const uint32_t b0 = find_bin256<kHistBins>(a.hist0 + (int64_t)row * kHistBins, (uint32_t)a.k, sh,
+                                             s_sel, above);
+  for (int i = tid; i < kHistBins; i += kWideThreads) hist[i] = 0u;
+  uint32_t key[kPerThread];
+  int j0;
+  chunk_keys(a, src, c, key, j0);
+  __syncthreads();
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const bool m = j0 + q < a.n && (key[q] >> 21) == b0;
+    if (m) atomicAdd(&hist[(key[q] >> 10) & 2047u], 1u);
+    cnt += m ? 1u : 0u;
+  }
+  uint32_t tot;
+  const uint32_t off = scan256(cnt, sh, tot);
+  if (tid == 0) s_base = tot ? atomicAdd(a.ncand + row, tot) : 0u;
+  __syncthreads();
+  uint32_t* cand = a.cand + (int64_t)row * a.n + s_base + off;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    if (j0 + q < a.n && (key[q] >> 21) == b0) *cand++ = key[q];
+  }
+  uint32_t* h1 = a.hist1 + (int64_t)row * kHistBins;
+  for (int i = tid; i < kHistBins; i += kWideThreads) {
+    const uint32_t v = hist[i];
+    if (v) atomicAdd(h1 + i, v);
+  }
+}
+
+__global__ __launch_bounds__(kWideThreads) void k_select_wide_b(const WideSelectArgs a) {
+  __shared__ uint32_t hist[1024];
+  __shared__ uint32_t sh[8], s_sel[2];
+  const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  const float* src = a.src + (int64_t)row * a.row_stride;
+  uint32_t need = (uint32_t)a.k, above;
+  const uint32_t b0 = find_bin256<kHistBins>(a.hist0 + (int64_t)row * kHistBins, need, sh, s_sel, above);
+  need -= above;
+  const uint32_t b1 = find_bin256<kHistBins>(a.hist1 + (int64_t)row * kHistBins, need, sh, s_sel, above);
+  need -= above;
+  const uint32_t p01 = (b0 << 11) | b1;
+  for (int i = tid; i < 1024; i += kWideThreads) hist[i] = 0u;
+  __syncthreads();
+  const uint32_t nc = a.ncand[row];
+  const uint32_t* cand = a.cand + (int64_t)row * a.n;
+  for (uint32_t i = tid; i < nc; i += kWideThreads) {
+    const uint32_t key = cand[i];
+    if ((key >> 10) == p01) atomicAdd(&hist[key & 1023u], 1u);
+  }
+  __syncthreads();
+  const uint32_t b2 = find_bin256<1024>(hist, need, sh, s_sel, above);
+  need -= above;
+  const uint32_t T = (p01 << 10) | b2;   // the k-th largest key; `need` keys == T are taken
+  uint32_t key[kPerThread];
+  int j0;
+  chunk_keys(a, src, c, key, j0);
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const bool in = j0 + q < a.n;
+    gt += (in && key[q] > T) ? 1u : 0u;
+    eq += (in && key[q] == T) ? 1u : 0u;
+  }
+  uint32_t tot;
+  scan256((gt << 16) | eq, sh, tot);
+  if (tid == 0) {
+    uint32_t* cc = a.chunk_cnt + ((int64_t)row * a.chunks + c) * 2;
+    cc[0] = tot >> 16;
+    cc[1] = tot & 0xFFFFu;
+    if (c == 0) {
+      a.thr[row * 2] = T;
+      a.thr[row * 2 + 1] = need;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kWideThreads) void k_select_wide_c(const WideSelectArgs a) {
+  __shared__ uint32_t sh[8];
+  const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  const float* src = a.src + (int64_t)row * a.row_stride;
+  const uint32_t T = a.thr[row * 2], need = a.thr[row * 2 + 1];
+  // counts of the chunks before this one (chunk counts fit 16 bits each;
+  // their sums are kept in 32-bit halves separately)
+  uint32_t gtb = 0, eqb = 0;
+  const uint32_t* cc = a.chunk_cnt + (int64_t)row * a.chunks * 2;
+  for (int i = tid; i < c; i += kWideThreads) {
+    gtb += cc[2 * i];
+    eqb += cc[2 * i + 1];
+  }
+  uint32_t gt_before, eq_before;
+  scan256(gtb, sh, gt_before);
+  scan256(eqb, sh, eq_before);
+  uint32_t key[kPerThread];
+  int j0;
+  chunk_keys(a, src, c, key, j0);
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const bool in = j0 + q < a.n;
+    gt += (in && key[q] > T) ? 1u : 0u;
+    eq += (in && key[q] == T) ? 1u : 0u;
+  }
+  uint32_t tot;
+  const uint32_t ex = scan256((gt << 16) | eq, sh, tot);
+  uint32_t g2 = gt_before + (ex >> 16), e2 = eq_before + (ex & 0xFFFFu);
+  int32_t* out = a.idx + (int64_t)row * a.idx_stride;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int j = j0 + q;
+    if (j < a.n) {
+      if (key[q] > T) {
+        out[g2 + min(e2, need)] = j;
+        ++g2;
+      } else if (key[q] == T) {
+        if (e2 < need) out[g2 + e2] = j;
+        ++e2;
+      }
+    }
+  }
+}
+
+hipError_t launch_topk_select_wide(const WideSelectArgs& a, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  if (a.chunks != (a.n + kWideChunk - 1) / kWideChunk || a.chunks > 65535) return hipErrorInvalidValue;
+  const dim3 grid(a.chunks, a.rows);
+  hipLaunchKernelGGL(k_select_wide_a, grid, dim3(kWideThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_select_wide_b, grid, dim3(kWideThreads), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_select_wide_c, grid, dim3(kWideThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 size_t topk_select_lds_bytes(int cache_cap) {
   return (size_t)(kHistBins + 32 + kCandCap + cache_cap) * sizeof(uint32_t);
 }

@@ -153,6 +153,22 @@ def test_anchor_decode_ragged_bf16(N, topk):
     _check_anchor(q, k, v, topk, cfg.tol)
 
 
+@pytest.mark.parametrize("N,topk", [(4096, 1), (9000, 1234), (4100, 4100), (70001, 7000)])
+def test_anchor_decode_long_rows_and_full_ties(N, topk):
+    """Rows of 4096+ keys (the many-workgroup select): one random layer, and
+    one with a zero query, whose pooled row is constant (every key ties, so
+    the list is the first topk positions)."""
+    say("anchor decode long rows", N, topk)
+    g = torch.Generator(device=DEV).manual_seed(N + topk)
+    q = torch.randn((2, 8, 128), generator=g, device=DEV).bfloat16()
+    k = torch.randn((2, 2, N, 128), generator=g, device=DEV).bfloat16()
+    v = torch.randn((2, 2, N, 128), generator=g, device=DEV).bfloat16()
+    _check_anchor(q, k, v, topk, 2e-2)
+    _, idx, _, _ = _check_anchor(torch.zeros_like(q), k, v, topk, 2e-2)
+    want = np.broadcast_to(np.arange(topk, dtype=np.int32), idx.shape)
+    assert np.array_equal(idx.cpu().numpy(), want)
+
+
 # ---------------------------------------------------------------------------
 # reuse decode
 # ---------------------------------------------------------------------------
@@ -226,7 +242,10 @@ def test_llama_128k_sampled():
         assert np.max(np.abs(np64(out[b:b + 1, hs]) - ro)) <= cfg.tol
         rpool = oracle.pool_decode(p, 1)[0, 0]
         ridx = oracle.topk_full_sort(rpool, cfg.topk)
-        ok, nd = oracle.index_sets_agree(idx[b, g].cpu().numpy(), ridx, rpool)
+        gi = idx[b, g].cpu().numpy()
+        # bit-exact against a full sort of the GPU's own pooled row
+        assert np.array_equal(gi, oracle.topk_full_sort(np64(pooled[b, g]), cfg.topk))
+        ok, nd = oracle.index_sets_agree(gi, ridx, rpool)
         assert ok, nd
         # reuse head g2 of layer 1 whose list comes from anchor head g
         for g2 in [x for x in range(cfg.n_kv_heads) if hm[x] == g]:
