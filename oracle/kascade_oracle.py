@@ -49,7 +49,8 @@ __all__ = [
     "dense_prefill", "dense_prefill_rows", "tile_pool", "tile_pool_one",
     "tile_topk", "sparse_prefill", "sparse_prefill_rows",
     "anchor_prefill", "reuse_prefill",
-    "sim", "layer_weight", "weighted_similarity", "dp_select_anchors",
+    "sim", "head_similarity", "head_map_from_similarity", "remapped_layer_similarity",
+    "layer_weight", "weighted_similarity", "dp_select_anchors",
     "brute_force_anchors", "coverage_score",
     "run_decode_layerstack", "index_sets_agree",
 ]
@@ -408,6 +409,52 @@ def sim(p_a, p_b, k: int) -> float:
     I_a = topk_full_sort(p_a, k)
     I_b = topk_full_sort(p_b, k)
     return float(p_b[I_a].sum() / p_b[I_b].sum())
+
+
+def head_similarity(pooled_a, pooled_b, k: int) -> np.ndarray:
+    """Per-KV-head cross-layer similarity, averaged over samples.
+
+    pooled_a, pooled_b: [S, Hkv, N] pooled post-softmax rows of layers a and b
+    for the same S calibration queries.  Returns M [Hkv_a, Hkv_b] with
+    M[ga, gb] = mean over samples s of sim(pooled_a[s, ga], pooled_b[s, gb], k):
+    [Explainer] eq. sim applied to every pair of KV heads, the quantity that
+    section "ヘッドリマッピング" maximises to pair each head of a reuse layer with
+    a head of its anchor.  Reading: samples are averaged with equal weight."""
+    pa = _f64(pooled_a)
+    pb = _f64(pooled_b)
+    S, Ha = pa.shape[0], pa.shape[1]
+    Hb = pb.shape[1]
+    M = np.zeros((Ha, Hb))
+    for ga in range(Ha):
+        for gb in range(Hb):
+            M[ga, gb] = sum(sim(pa[s, ga], pb[s, gb], k) for s in range(S)) / S
+    return M
+
+
+def head_map_from_similarity(M) -> np.ndarray:
+    """[Explainer] "ヘッドリマッピング": each KV head gb of the reuse layer takes
+    the anchor KV head with the largest similarity M[ga, gb]; ties go to the
+    lower ga.  Returns int32 [Hkv_b]."""
+    M = _f64(M)
+    out = np.zeros(M.shape[1], dtype=np.int32)
+    for gb in range(M.shape[1]):
+        best = 0
+        for ga in range(1, M.shape[0]):
+            if M[ga, gb] > M[best, gb]:
+                best = ga
+        out[gb] = best
+    return out
+
+
+def remapped_layer_similarity(M) -> float:
+    """Layer-level similarity of (anchor a, layer b) once b's heads are
+    remapped: the mean over b's KV heads of their best similarity.  Reading
+    of [Explainer] "レイヤー間類似度とアンカーレイヤー選択" together with
+    "ヘッドリマッピング": a reuse layer always runs with the remap, so the
+    similarity that selects anchors is the remapped one."""
+    M = _f64(M)
+    hm = head_map_from_similarity(M)
+    return float(np.mean([M[hm[gb], gb] for gb in range(M.shape[1])]))
 
 
 def layer_weight(x, y) -> float:

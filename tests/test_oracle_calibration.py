@@ -1,4 +1,5 @@
 """Pins for the oracle's offline anchor selection: eq. sim, eq. w and the DP."""
+import itertools
 import math
 
 import numpy as np
@@ -90,3 +91,57 @@ def test_dp_on_the_64k_end_to_end_similarity_matrix():
     a, v = oracle.dp_select_anchors(S, 6)
     assert len(a) == 6 and a[0] == 0
     assert abs(oracle.coverage_score(S, a) - v) < 1e-9
+
+
+# ---------------------------------------------------------------------------
+# per-head similarity, head maps, remapped layer similarity
+# ---------------------------------------------------------------------------
+
+def test_sim_closed_form_small():
+    # I_a = {0, 1}, I_b = {2, 3}: sim = (0.1 + 0.2) / (0.3 + 0.4) = 3/7
+    pa = np.array([0.4, 0.3, 0.2, 0.1])
+    pb = np.array([0.1, 0.2, 0.3, 0.4])
+    assert abs(oracle.sim(pa, pb, 2) - 3.0 / 7.0) < 1e-15
+
+
+def test_head_similarity_permuted_heads():
+    """Layer b's heads are a permutation of layer a's: the per-head similarity
+    is exactly 1 on the permutation, the head map recovers it, and the
+    remapped layer similarity is 1."""
+    rng = np.random.default_rng(3)
+    S, H, N, k = 3, 4, 200, 20
+    pa = rng.random((S, H, N)) ** 8
+    perm = np.array([2, 0, 3, 1])
+    pb = pa[:, perm, :]
+    M = oracle.head_similarity(pa, pb, k)
+    for gb in range(H):
+        assert M[perm[gb], gb] == 1.0
+        assert np.all(M[:, gb] <= 1.0 + 1e-15)
+    assert np.array_equal(oracle.head_map_from_similarity(M), perm)
+    assert oracle.remapped_layer_similarity(M) == 1.0
+
+
+def test_head_similarity_matches_definition_by_brute_force():
+    """Tiny rows: each Top-k set is the best k-subset by brute force."""
+    rng = np.random.default_rng(4)
+    S, H, N, k = 2, 2, 7, 3
+    pa = rng.random((S, H, N))
+    pb = rng.random((S, H, N))
+
+    def best(p):
+        return max(itertools.combinations(range(N), k), key=lambda c: (sum(p[list(c)]), [-x for x in c]))
+
+    M = oracle.head_similarity(pa, pb, k)
+    for ga in range(H):
+        for gb in range(H):
+            vals = []
+            for s in range(S):
+                Ia, Ib = list(best(pa[s, ga])), list(best(pb[s, gb]))
+                vals.append(pb[s, gb, Ia].sum() / pb[s, gb, Ib].sum())
+            assert abs(M[ga, gb] - np.mean(vals)) < 1e-14
+
+
+def test_head_map_ties_go_to_lower_head():
+    M = np.array([[0.5, 0.2], [0.5, 0.9], [0.1, 0.9]])
+    assert list(oracle.head_map_from_similarity(M)) == [0, 1]
+    assert abs(oracle.remapped_layer_similarity(M) - 0.7) < 1e-15
