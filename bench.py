@@ -292,6 +292,82 @@ def traffic_probe(torch, K, synth, configs):
                       "hashes": {k: kernel_source_hash(k) for k in KERNEL_SOURCES}}), flush=True)
 
 
+def calibration_bench(torch, K, synth, configs, args):
+    """Offline calibration on the 32K-context Llama-shaped decode layers: the
+    anchor decode pass of every layer over S calibration queries (pooled rows
+    and Top-k lists), the per-KV-head similarity of every layer pair, the
+    weighted similarity, the anchor DP and the head maps.  Prints one JSON
+    line; the oracle's similarity of one layer pair is timed beside it."""
+    import oracle
+    cfg = configs.CONFIGS[2]
+    L, Hkv, N, k, S = cfg.n_layers, cfg.n_kv_heads, cfg.ctx_len, cfg.topk, 4
+    lin = synth.heavy_lineages(cfg.seed, L, Hkv, N, cfg.heavy, cfg.drift)
+    maps = synth.head_maps(cfg.seed, L, cfg.anchors, Hkv, cfg.head_map_kind)
+    pooled = torch.empty((L, S, Hkv, N), dtype=torch.float32, device="cuda")
+    idx = torch.empty((L, S, Hkv, k), dtype=torch.int32, device="cuda")
+    layers = []
+    for l in range(L):
+        layers.append(synth.decode_layer(cfg.seed, l, S, cfg.n_q_heads, Hkv, cfg.head_dim, N,
+                                         synth.layer_heavy_sets(lin, l, cfg.anchors, maps),
+                                         cfg.alpha, cfg.dtype, device="cuda"))
+    sh = K.make_shape(layers[0][0], layers[0][1], N)
+    ws = K.workspace(K.OP_ANCHOR_DECODE, sh, k)
+    out = torch.empty_like(layers[0][0])
+
+    def passes():
+        for l, (q, kk, v) in enumerate(layers):
+            K.check(K.kascade_anchor_decode(sh, q, kk, v, k, out, None, idx[l], pooled[l], ws, ws.numel()),
+                    "anchor_decode")
+
+    sim = torch.zeros((L, L, Hkv, Hkv), dtype=torch.float32, device="cuda")
+
+    def simk():
+        K.check(K.kascade_calib_head_similarity(L, S, Hkv, N, k, pooled, idx, sim), "calib")
+
+    for _ in range(args.warmup):
+        passes()
+        simk()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record()
+    for _ in range(args.steps):
+        passes()
+    e[1].record()
+    for _ in range(args.steps):
+        simk()
+    e[2].record()
+    torch.cuda.synchronize()
+    t_pass = e[0].elapsed_time(e[1]) / args.steps
+    t_sim = e[1].elapsed_time(e[2]) / args.steps
+    t0 = time.perf_counter()
+    simh = sim.cpu().numpy()
+    Sm = K.kascade_weighted_similarity(L, Hkv, simh, None)
+    anchors, _ = K.kascade_select_anchors(L, len(cfg.anchors), Sm)
+    K.kascade_head_maps(L, Hkv, simh, anchors)
+    t_host = (time.perf_counter() - t0) * 1e3
+    pairs = L * (L + 1) // 2
+    gathered = pairs * Hkv * S * (Hkv + 1) * k * 4
+    # oracle on one layer pair (S queries), the same quantity
+    rp = []
+    for l in (0, 1):
+        q, kk, v = layers[l]
+        rp.append(oracle.anchor_decode(*(x.float().cpu().numpy().astype(np.float64) for x in (q, kk, v)), k)[2])
+    t1 = time.perf_counter()
+    oracle.head_similarity(rp[0], rp[1], k)
+    t_oracle_pair = time.perf_counter() - t1
+    print(json.dumps({
+        "metric": "calibration: per-KV-head similarity of all layer pairs (ms)", "value": t_sim,
+        "unit": "ms", "higher_is_better": False, "dtype": "f32 pooled rows, f64 sums",
+        "config": {"workload": "Llama-3.1-8B-shaped decode layers, 32 layers, 8 KV heads, 32K ctx, "
+                               "k=3264, %d calibration queries" % S},
+        "anchor_passes_ms": t_pass, "similarity_ms": t_sim, "host_dp_headmaps_ms": t_host,
+        "layer_pairs": pairs, "gathered_GBps": gathered / (t_sim * 1e-3) / 1e9,
+        "anchors": anchors,
+        "cpu_baseline": {"value": t_oracle_pair * pairs * 1e3, "unit": "ms", "kind": "oracle",
+                         "sample": "one layer pair timed (%.2f s), x %d pairs" % (t_oracle_pair, pairs)},
+    }), flush=True)
+
+
 # ---------------------------------------------------------------------------
 
 def main():
@@ -304,6 +380,8 @@ def main():
                     help="run one section only (profiling)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="one launch of each kernel plus a calibration copy, for rocprofv3 --pmc")
+    ap.add_argument("--calibration", action="store_true",
+                    help="time the offline calibration path (layer-pair similarities, DP, head maps)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -321,6 +399,9 @@ def main():
     torch.cuda.set_device(0)
     if args.traffic_probe:
         traffic_probe(torch, K, synth, configs)
+        return
+    if args.calibration:
+        calibration_bench(torch, K, synth, configs, args)
         return
 
     sections = ["decode32k", "decode128k", "prefill"] if args.only is None else [args.only]

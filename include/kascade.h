@@ -151,6 +151,53 @@ int kascade_reuse_prefill(const kascade_shape* shape, const void* q, const void*
                           void* out, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
+/* ---- calibration (offline: choosing anchors and head maps) -------------- */
+
+/* Per-KV-head similarity of every pair of layers a <= b over S calibration
+ * queries: [Explainer] "レイヤー間類似度とアンカーレイヤー選択" (eq. sim) applied to
+ * each pair of KV heads, the quantity "ヘッドリマッピング" maximises.
+ *   pooled   [L, S, Hkv, n] fp32 device: each layer's pooled post-softmax rows
+ *            (kascade_anchor_decode's pooled_out, one decode query per sample)
+ *   topk_idx [L, S, Hkv, k] int32 device: the rows' Top-k positions
+ *            (kascade_anchor_decode's topk_idx); entries are clamped into [0, n)
+ *   sim      [L, L, Hkv, Hkv] fp32 device, out: for a <= b
+ *            sim[a][b][ga][gb] = mean over s of
+ *              sum_{j in topk_idx[a,s,ga]} pooled[b,s,gb,j] /
+ *              sum_{j in topk_idx[b,s,gb]} pooled[b,s,gb,j];
+ *            entries with a > b are not written.  fp64 sums, deterministic. */
+int kascade_calib_head_similarity(int32_t L, int32_t S, int32_t n_kv_heads, int32_t n, int32_t k,
+                                  const float* pooled, const int32_t* topk_idx, float* sim,
+                                  hipStream_t stream);
+
+/* Layer weight, [Explainer] eq. w: *w_out = 1 - mean over tokens t of
+ * cos(x_t, y_t), x and y [tokens, dim] device arrays in `dtype` (F32 or
+ * BF16), the layer's input and output hidden states.  w_out: one float,
+ * device.  NaN if some token has a zero vector.  Workspace: at least
+ * kascade_layer_weight_workspace_bytes(tokens), contents irrelevant. */
+int kascade_layer_weight(const void* x, const void* y, int32_t tokens, int32_t dim, int32_t dtype,
+                         float* w_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+size_t kascade_layer_weight_workspace_bytes(int32_t tokens);
+
+/* HOST.  Weighted similarity matrix for the anchor DP from a host copy of
+ * kascade_calib_head_similarity's output: for a <= b
+ *   S[a][b] = w[b] * mean over gb of max over ga of sim[a][b][ga][gb]
+ * (each head of b at its best anchor head: the remapped similarity), 0 below
+ * the diagonal.  w: HOST [L] or NULL (all 1).  S: HOST [L, L] doubles. */
+int kascade_weighted_similarity(int32_t L, int32_t n_kv_heads, const float* sim, const float* w,
+                                double* S);
+
+/* HOST.  [Explainer] "動的計画法（Algorithm 1）": the M anchors (layer 0 among
+ * them) maximising sum_l S[a(l)][l], a(l) the last anchor <= l; ties keep the
+ * smallest start.  anchors: HOST [M] out, ascending; score: optional total. */
+int kascade_select_anchors(int32_t L, int32_t M, const double* S, int32_t* anchors, double* score);
+
+/* HOST.  [Explainer] "ヘッドリマッピング": head_maps [L, Hkv] out; for a layer b
+ * reusing anchor a(b), head_maps[b][gb] = argmax over ga of
+ * sim[a(b)][b][ga][gb] (ties to the lower ga); anchors get the identity.
+ * anchors: HOST [M] ascending with anchors[0] == 0. */
+int kascade_head_maps(int32_t L, int32_t n_kv_heads, const float* sim, const int32_t* anchors,
+                      int32_t M, int32_t* head_maps);
+
 /* ---- helpers ----------------------------------------------------------- */
 
 /* op: 0 anchor_decode, 1 reuse_decode, 2 anchor_prefill, 3 reuse_prefill,

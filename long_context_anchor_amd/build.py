@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkascade.so")
-SOURCES = ["abi.hip", "decode.hip", "select.hip", "prefill.hip"]
+SOURCES = ["abi.hip", "decode.hip", "select.hip", "prefill.hip", "calib.hip"]
 ARCH = os.environ.get("KASCADE_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -573,6 +573,130 @@ int kascade_dense_decode(const kascade_shape* s, const void* q, const void* k, c
   return hip_status(e);
 }
 
+// ---- calibration -------------------------------------------------------------
+
+int kascade_calib_head_similarity(int32_t L, int32_t S, int32_t n_kv_heads, int32_t n, int32_t k,
+                                  const float* pooled, const int32_t* topk_idx, float* sim,
+                                  hipStream_t stream) {
+  if (!pooled || !topk_idx || !sim) return KASCADE_ERR_NULL;
+  if (L < 1 || L > 65535 || S < 1 || n_kv_heads < 1 || n_kv_heads > kMaxKvHeads || n < 1)
+    return KASCADE_ERR_SHAPE;
+  if (k < 1 || k > n) return KASCADE_ERR_TOPK;
+  return hip_status(launch_calib_sim(pooled, topk_idx, L, S, n_kv_heads, n, k, sim, stream));
+}
+
+size_t kascade_layer_weight_workspace_bytes(int32_t tokens) {
+  return tokens < 1 ? 0 : (size_t)((tokens + 63) / 64) * sizeof(double);
+}
+
+int kascade_layer_weight(const void* x, const void* y, int32_t tokens, int32_t dim, int32_t dtype,
+                         float* w_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!x || !y || !w_out) return KASCADE_ERR_NULL;
+  if (tokens < 1 || dim < 1) return KASCADE_ERR_SHAPE;
+  if (dtype != KASCADE_F32 && dtype != KASCADE_BF16) return KASCADE_ERR_DTYPE;
+  if (!workspace || workspace_bytes < kascade_layer_weight_workspace_bytes(tokens))
+    return KASCADE_ERR_WORKSPACE;
+  return hip_status(launch_layer_weight(x, y, tokens, dim, dtype, reinterpret_cast<double*>(workspace),
+                                        w_out, stream));
+}
+
+int kascade_weighted_similarity(int32_t L, int32_t n_kv_heads, const float* sim, const float* w,
+                                double* S) {
+  if (!sim || !S) return KASCADE_ERR_NULL;
+  if (L < 1 || n_kv_heads < 1) return KASCADE_ERR_SHAPE;
+  const int H = n_kv_heads;
+  for (int a = 0; a < L; ++a) {
+    for (int b = 0; b < L; ++b) {
+      if (b < a) {
+        S[(int64_t)a * L + b] = 0.0;
+        continue;
+      }
+      // mean over b's heads of their best (lowest ga on ties) anchor head
+      double tot = 0.0;
+      for (int gb = 0; gb < H; ++gb) {
+        const float* col = sim + ((int64_t)a * L + b) * H * H + gb;
+        float best = col[0];
+        for (int ga = 1; ga < H; ++ga) best = col[(int64_t)ga * H] > best ? col[(int64_t)ga * H] : best;
+        tot += (double)best;
+      }
+      S[(int64_t)a * L + b] = (w ? (double)w[b] : 1.0) * (tot / H);
+    }
+  }
+  return KASCADE_OK;
+}
+
+int kascade_select_anchors(int32_t L, int32_t M, const double* S, int32_t* anchors, double* score) {
+  if (!S || !anchors) return KASCADE_ERR_NULL;
+  if (L < 1 || M < 1 || M > L) return KASCADE_ERR_ARG;
+  // pref[i][j] = sum_{l=i}^{j-1} S[i][l]: the similarity layers i..j-1 keep when i anchors them
+  std::vector<double> pref((size_t)L * (L + 1), 0.0);
+  for (int i = 0; i < L; ++i) {
+    double acc = 0.0;
+    for (int j = i; j < L; ++j) {
+      acc += S[(int64_t)i * L + j];
+      pref[(size_t)i * (L + 1) + j + 1] = acc;
+    }
+  }
+  const double NEG = -HUGE_VAL;
+  std::vector<double> dp((size_t)(M + 1) * (L + 1), NEG);
+  std::vector<int32_t> arg((size_t)(M + 1) * (L + 1), -1);
+  dp[0] = 0.0;
+  for (int m = 1; m <= M; ++m) {
+    for (int j = m; j <= L; ++j) {
+      double best = NEG;
+      int bi = -1;
+      for (int i = m - 1; i < j; ++i) {   // the last segment [i, j) starts at anchor i
+        const double prev = dp[(size_t)(m - 1) * (L + 1) + i];
+        if (prev == NEG) continue;
+        const double v = prev + pref[(size_t)i * (L + 1) + j];
+        if (v > best) {
+          best = v;
+          bi = i;
+        }
+      }
+      dp[(size_t)m * (L + 1) + j] = best;
+      arg[(size_t)m * (L + 1) + j] = bi;
+    }
+  }
+  int j = L;
+  for (int m = M; m >= 1; --m) {
+    const int i = arg[(size_t)m * (L + 1) + j];
+    anchors[m - 1] = i;
+    j = i;
+  }
+  if (score) *score = dp[(size_t)M * (L + 1) + L];
+  return KASCADE_OK;
+}
+
+int kascade_head_maps(int32_t L, int32_t n_kv_heads, const float* sim, const int32_t* anchors,
+                      int32_t M, int32_t* head_maps) {
+  if (!sim || !anchors || !head_maps) return KASCADE_ERR_NULL;
+  if (L < 1 || n_kv_heads < 1 || M < 1 || M > L) return KASCADE_ERR_ARG;
+  if (anchors[0] != 0) return KASCADE_ERR_ARG;
+  for (int m = 1; m < M; ++m)
+    if (anchors[m] <= anchors[m - 1] || anchors[m] >= L) return KASCADE_ERR_ARG;
+  const int H = n_kv_heads;
+  int a = 0, next = 1;
+  for (int b = 0; b < L; ++b) {
+    if (next < M && anchors[next] == b) {
+      a = b;
+      ++next;
+    }
+    for (int gb = 0; gb < H; ++gb) {
+      if (b == a) {
+        head_maps[(int64_t)b * H + gb] = gb;
+        continue;
+      }
+      const float* col = sim + ((int64_t)a * L + b) * H * H + gb;
+      int best = 0;
+      for (int ga = 1; ga < H; ++ga)
+        if (col[(int64_t)ga * H] > col[(int64_t)best * H]) best = ga;
+      head_maps[(int64_t)b * H + gb] = best;
+    }
+  }
+  return KASCADE_OK;
+}
+
 int kascade_topk_select_f32(const float* scores, int64_t row_stride, int32_t rows, int32_t n,
                             int32_t k, int32_t* idx, int64_t idx_stride, hipStream_t stream) {
   if (!scores || !idx) return KASCADE_ERR_NULL;

@@ -153,4 +153,10 @@ __host__ __device__ inline int64_t packed_row_offset(int32_t t, int32_t g, int32
   return (int64_t)Hkv * sum + (int64_t)g * Pt;
 }
 
+// Calibration (calib.hip).
+hipError_t launch_calib_sim(const float* pooled, const int32_t* idx, int L, int S, int Hkv, int N,
+                            int k, float* sim, hipStream_t s);
+hipError_t launch_layer_weight(const void* x, const void* y, int tokens, int dim, int dtype,
+                               double* part, float* w, hipStream_t s);
+
 }  // namespace kc

@@ -31,6 +31,8 @@ EXPORTS = [
     "kascade_topk_select_f32", "kascade_dense_decode", "kascade_dense_prefill",
     "kascade_kernel_timer_enable", "kascade_kernel_timer_read", "kascade_status_str",
     "kascade_last_hip_error", "kascade_version",
+    "kascade_calib_head_similarity", "kascade_layer_weight", "kascade_layer_weight_workspace_bytes",
+    "kascade_weighted_similarity", "kascade_select_anchors", "kascade_head_maps",
 ]
 
 
@@ -80,6 +82,12 @@ _SIGS = {
     "kascade_status_str": (ctypes.c_char_p, [_i32]),
     "kascade_last_hip_error": (_i32, []),
     "kascade_version": (ctypes.c_char_p, []),
+    "kascade_calib_head_similarity": (_i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "kascade_layer_weight": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "kascade_layer_weight_workspace_bytes": (_sz, [_i32]),
+    "kascade_weighted_similarity": (_i32, [_i32, _i32, _vp, _vp, _vp]),
+    "kascade_select_anchors": (_i32, [_i32, _i32, _vp, _vp, _vp]),
+    "kascade_head_maps": (_i32, [_i32, _i32, _vp, _vp, _i32, _vp]),
 }
 
 
@@ -183,6 +191,59 @@ def kascade_kernel_timer_read(kernel_id: int):
     if st:
         raise KascadeError(st, "kascade_kernel_timer_read")
     return ms.value, n.value
+
+
+def kascade_calib_head_similarity(L, S, n_kv_heads, n, k, pooled, topk_idx, sim, stream=None) -> int:
+    return lib().kascade_calib_head_similarity(L, S, n_kv_heads, n, k, _p(pooled), _p(topk_idx), _p(sim),
+                                               _stream(stream))
+
+
+def kascade_layer_weight(x, y, tokens, dim, dtype, w_out, workspace, workspace_bytes, stream=None) -> int:
+    return lib().kascade_layer_weight(_p(x), _p(y), tokens, dim, dtype, _p(w_out), _p(workspace),
+                                      workspace_bytes, _stream(stream))
+
+
+def kascade_layer_weight_workspace_bytes(tokens) -> int:
+    return lib().kascade_layer_weight_workspace_bytes(tokens)
+
+
+def _host(a, dtype):
+    """A C-contiguous NumPy array of `dtype` and its address (host arguments)."""
+    import numpy as np
+    arr = np.ascontiguousarray(a, dtype=dtype)
+    return arr, arr.ctypes.data
+
+
+def kascade_weighted_similarity(L, n_kv_heads, sim_host, w_host=None):
+    """Host call; returns S [L, L] float64."""
+    import numpy as np
+    sim, ps = _host(sim_host, np.float32)
+    w, pw = _host(w_host, np.float32) if w_host is not None else (None, None)
+    S = np.zeros((L, L), dtype=np.float64)
+    check(lib().kascade_weighted_similarity(L, n_kv_heads, ps, pw, S.ctypes.data),
+          "kascade_weighted_similarity")
+    return S
+
+
+def kascade_select_anchors(L, M, S_host):
+    """Host call; returns (anchors list, score)."""
+    import numpy as np
+    S, ps = _host(S_host, np.float64)
+    out = np.zeros(M, dtype=np.int32)
+    score = ctypes.c_double(0.0)
+    check(lib().kascade_select_anchors(L, M, ps, out.ctypes.data, ctypes.addressof(score)),
+          "kascade_select_anchors")
+    return [int(x) for x in out], score.value
+
+
+def kascade_head_maps(L, n_kv_heads, sim_host, anchors):
+    """Host call; returns head_maps int32 [L, n_kv_heads]."""
+    import numpy as np
+    sim, ps = _host(sim_host, np.float32)
+    an, pa = _host(anchors, np.int32)
+    out = np.zeros((L, n_kv_heads), dtype=np.int32)
+    check(lib().kascade_head_maps(L, n_kv_heads, ps, pa, len(an), out.ctypes.data), "kascade_head_maps")
+    return out
 
 
 def kascade_status_str(status: int) -> str:
@@ -332,3 +393,24 @@ def packed_row(pooled_b: torch.Tensor, t: int, g: int, n: int, n_kv: int, tile: 
     P = min(n, tile * (t + 1))
     off += g * P
     return pooled_b[off:off + P]
+
+
+def calib_head_similarity(pooled, topk_idx):
+    """pooled [L,S,Hkv,n] fp32, topk_idx [L,S,Hkv,k] int32 (device) -> sim [L,L,Hkv,Hkv] fp32."""
+    L, S, Hkv, n = pooled.shape
+    k = topk_idx.shape[-1]
+    sim = torch.zeros((L, L, Hkv, Hkv), dtype=torch.float32, device=pooled.device)
+    check(kascade_calib_head_similarity(L, S, Hkv, n, k, pooled, topk_idx, sim),
+          "kascade_calib_head_similarity")
+    return sim
+
+
+def layer_weight(x, y):
+    """x, y [tokens, dim] (f32 or bf16, device) -> w (0-d fp32 device tensor)."""
+    tokens, dim = x.shape
+    w = torch.empty((), dtype=torch.float32, device=x.device)
+    nb = max(kascade_layer_weight_workspace_bytes(tokens), 8)
+    ws = torch.empty(nb, dtype=torch.uint8, device=x.device)
+    check(kascade_layer_weight(x, y, tokens, dim, _dtype_code(x), w, ws, nb), "kascade_layer_weight")
+    return w
+
