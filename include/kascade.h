@@ -151,6 +151,40 @@ int kascade_reuse_prefill(const kascade_shape* shape, const void* q, const void*
                           void* out, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
+/* ---- paged KV caches (block tables) -------------------------------------- */
+
+/* A paged K or V cache: key j of batch b lives in physical block
+ * block_table[b * table_stride + j / block_size], row j % block_size; the
+ * element (head g, row r, dim i) of physical block p is at
+ *   cache + p * block_stride + g * shape->kv_stride_h + r * shape->kv_stride_n + i
+ * (shape->kv_stride_b is not used).  Both caches share the layout and table.
+ * block_size: a power of two; block_stride: a multiple of kv_stride_n, every
+ * head's block_size rows inside it, num_blocks * (block_stride / kv_stride_n)
+ * below 2^32.  Table entries and positions are clamped into range, so a bad
+ * table cannot fault.  bf16 only. */
+typedef struct kascade_paged_kv {
+  const int32_t* block_table;   /* DEVICE int32 [B, table_stride], table_stride >= ceil(N / block_size) */
+  int32_t table_stride;
+  int32_t block_size;
+  int32_t num_blocks;           /* physical blocks in each cache */
+  int32_t reserved;             /* must be 0 */
+  int64_t block_stride;         /* elements between physical blocks */
+} kascade_paged_kv;
+
+/* kascade_anchor_decode / kascade_reuse_decode over paged caches: the same
+ * results for the same logical keys (positions in topk_idx and
+ * anchor_topk_idx are logical).  Workspace sizes as for op 0 / op 1. */
+int kascade_anchor_decode_paged(const kascade_shape* shape, const kascade_paged_kv* paged,
+                                const void* q, const void* k_cache, const void* v_cache,
+                                int32_t topk, void* out, float* lse_out, int32_t* topk_idx,
+                                float* pooled_out, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+int kascade_reuse_decode_paged(const kascade_shape* shape, const kascade_paged_kv* paged,
+                               const void* q, const void* k_cache, const void* v_cache,
+                               int32_t topk, const int32_t* anchor_topk_idx,
+                               const int32_t* head_map, void* out, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
 /* ---- calibration (offline: choosing anchors and head maps) -------------- */
 
 /* Per-KV-head similarity of every pair of layers a <= b over S calibration

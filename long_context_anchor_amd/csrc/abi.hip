@@ -23,10 +23,10 @@ struct DeviceInfo {
   int cus = 0;
   size_t lds_per_cu = 0;
   // split-K variants [dtype][log2 G][kind] (kind 0 dense, 1 dense + score
-  // spill, 2 gather): resident workgroups per CU without dynamic LDS (0 = not
-  // queried yet) and static LDS bytes
-  int splitk_bpc[2][4][3] = {};
-  size_t splitk_lds[2][4][3] = {};
+  // spill, 2 gather; +3 for a paged cache): resident workgroups per CU
+  // without dynamic LDS (0 = not queried yet) and static LDS bytes
+  int splitk_bpc[2][4][6] = {};
+  size_t splitk_lds[2][4][6] = {};
 };
 DeviceInfo g_dev[kMaxDevices];
 std::mutex g_dev_mu;
@@ -81,9 +81,10 @@ int device_setup(DeviceInfo** out) {
 
 // Workgroup slots of the whole GPU for one split-K variant running splits of
 // kps keys: CUs x resident workgroups (registers or LDS, whichever binds).
-int splitk_slots(DeviceInfo* d, int dtype, int G, bool gather, bool spill, int kps, int* slots) {
+int splitk_slots(DeviceInfo* d, int dtype, int G, bool gather, bool spill, bool paged, int kps,
+                 int* slots) {
   const int lg = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
-  const int kind = gather ? 2 : spill ? 1 : 0;
+  const int kind = (gather ? 2 : spill ? 1 : 0) + (paged ? 3 : 0);
   const int dt = dtype == KASCADE_BF16 ? 1 : 0;
   int bpc;
   size_t st;
@@ -93,7 +94,7 @@ int splitk_slots(DeviceInfo* d, int dtype, int G, bool gather, bool spill, int k
     if (b == 0) {
       int n = 0;
       size_t sl = 0;
-      hipError_t e = decode_splitk_attrs(dtype, G, gather, spill, &n, &sl);
+      hipError_t e = decode_splitk_attrs(dtype, G, gather, spill, paged, &n, &sl);
       if (e != hipSuccess) {
         g_last_hip_error = (int)e;
         return KASCADE_ERR_HIP;
@@ -104,7 +105,7 @@ int splitk_slots(DeviceInfo* d, int dtype, int G, bool gather, bool spill, int k
     bpc = b;
     st = d->splitk_lds[dt][lg][kind];
   }
-  const size_t per_wg = st + decode_splitk_dyn_lds(dtype, G, gather, spill, kps);
+  const size_t per_wg = st + decode_splitk_dyn_lds(dtype, G, gather, spill, paged, kps);
   if (per_wg > 0 && d->lds_per_cu > 0) {
     const int by_lds = (int)(d->lds_per_cu / per_wg);
     bpc = by_lds < bpc ? by_lds : bpc;
@@ -168,7 +169,7 @@ size_t elem_size(int dtype) { return dtype == KASCADE_BF16 ? 2 : 4; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-int check_shape(const kascade_shape* s, bool prefill) {
+int check_shape(const kascade_shape* s, bool prefill, bool paged = false) {
   if (!s) return KASCADE_ERR_NULL;
   if (s->reserved != 0) return KASCADE_ERR_ARG;
   if (s->batch < 1 || s->batch > 65535 || s->n_q_heads < 1 || s->n_kv_heads < 1 ||
@@ -194,11 +195,11 @@ int check_shape(const kascade_shape* s, bool prefill) {
     return KASCADE_ERR_SHAPE;
   if (s->kv_stride_h < 0 || s->kv_stride_b < 0 || s->q_stride_b < 0 || s->q_stride_n < 0)
     return KASCADE_ERR_SHAPE;
-  if (s->kv_stride_h < (int64_t)s->ctx_len * s->kv_stride_n && s->n_kv_heads > 1)
+  if (!paged && s->kv_stride_h < (int64_t)s->ctx_len * s->kv_stride_n && s->n_kv_heads > 1)
     return KASCADE_ERR_SHAPE;
   if (prefill && s->q_stride_n < d) return KASCADE_ERR_SHAPE;
   // decode kernels address a head's rows with 32-bit byte offsets
-  if (!prefill && (int64_t)s->ctx_len * s->kv_stride_n * es > (int64_t)0xFFFFFF00)
+  if (!prefill && !paged && (int64_t)s->ctx_len * s->kv_stride_n * es > (int64_t)0xFFFFFF00)
     return KASCADE_ERR_SHAPE;
   return KASCADE_OK;
 }
@@ -320,14 +321,15 @@ DecodePlan plan_decode(const kascade_shape* s, int n_keys, bool spill, bool pool
 // Plan with the slots the variant leaves at the largest split, then once more
 // if the planned split needs less LDS and so leaves more slots.
 int plan_decode_dev(DeviceInfo* d, const kascade_shape* s, int n_keys, bool gather, bool spill,
-                    bool pooled_ws, DecodePlan* p) {
+                    bool pooled_ws, bool paged, DecodePlan* p) {
   const int G = s->n_q_heads / s->n_kv_heads;
   int slots = 0, st;
-  if ((st = splitk_slots(d, s->dtype, G, gather, spill, (int)decode_max_kps(s, spill), &slots)))
+  if ((st = splitk_slots(d, s->dtype, G, gather, spill, paged, (int)decode_max_kps(s, spill),
+                         &slots)))
     return st;
   *p = plan_decode(s, n_keys, spill, pooled_ws, slots);
   int slots2 = 0;
-  if ((st = splitk_slots(d, s->dtype, G, gather, spill, p->kps, &slots2))) return st;
+  if ((st = splitk_slots(d, s->dtype, G, gather, spill, paged, p->kps, &slots2))) return st;
   if (slots2 > slots) *p = plan_decode(s, n_keys, spill, pooled_ws, slots2);
   return KASCADE_OK;
 }
@@ -432,7 +434,8 @@ int32_t kascade_topk_for_len(int32_t n, const kascade_topk_rule* rule) {
 size_t kascade_workspace_bytes(int op, const kascade_shape* s, int32_t topk,
                                const kascade_topk_rule* rule) {
   const bool prefill = op == 2 || op == 3 || op == 5;
-  if (check_shape(s, prefill) != KASCADE_OK) return 0;
+  // sizes depend on the dimensions only (decode: paged caches too)
+  if (check_shape(s, prefill, !prefill) != KASCADE_OK) return 0;
   switch (op) {
     case 0: return plan_decode(s, s->ctx_len, true, true, 0).total;
     case 1: return topk >= 1 ? plan_decode(s, topk, false, false, 0).total : 0;
@@ -444,11 +447,45 @@ size_t kascade_workspace_bytes(int op, const kascade_shape* s, int32_t topk,
   return 0;
 }
 
-int kascade_anchor_decode(const kascade_shape* s, const void* q, const void* k, const void* v,
-                          int32_t topk, void* out, float* lse_out, int32_t* topk_idx,
-                          float* pooled_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  int st = check_shape(s, false);
+// A paged cache descriptor, checked against the shape.
+static int check_paged(const kascade_shape* s, const kascade_paged_kv* pg) {
+  if (!pg) return KASCADE_OK;
+  if (!pg->block_table) return KASCADE_ERR_NULL;
+  if (pg->reserved != 0) return KASCADE_ERR_ARG;
+  if (s->dtype != KASCADE_BF16) return KASCADE_ERR_DTYPE;
+  const int bs = pg->block_size;
+  if (bs < 1 || bs > (1 << 20) || (bs & (bs - 1)) != 0 || pg->num_blocks < 1) return KASCADE_ERR_SHAPE;
+  if ((int64_t)pg->table_stride < ((int64_t)s->ctx_len + bs - 1) / bs) return KASCADE_ERR_SHAPE;
+  if (pg->block_stride <= 0 || pg->block_stride % s->kv_stride_n != 0 ||
+      (pg->block_stride * 2) % 16 != 0)
+    return KASCADE_ERR_SHAPE;
+  // every head's rows stay inside the block; physical row numbers fit 32 bits
+  if ((int64_t)(s->n_kv_heads - 1) * s->kv_stride_h + (int64_t)(bs - 1) * s->kv_stride_n +
+          s->head_dim > pg->block_stride)
+    return KASCADE_ERR_SHAPE;
+  if ((int64_t)pg->num_blocks * (pg->block_stride / s->kv_stride_n) > (int64_t)0xFFFFFFF0)
+    return KASCADE_ERR_SHAPE;
+  return KASCADE_OK;
+}
+
+static void set_paged(DecodeArgs& a, const kascade_shape* s, const kascade_paged_kv* pg) {
+  if (!pg) return;
+  a.table = pg->block_table;
+  a.table_stride = pg->table_stride;
+  int sh = 0;
+  while ((1 << sh) < pg->block_size) ++sh;
+  a.blk_shift = sh;
+  a.num_blocks = pg->num_blocks;
+  a.blk_rows = pg->block_stride / s->kv_stride_n;
+}
+
+static int anchor_decode_impl(const kascade_shape* s, const kascade_paged_kv* pg, const void* q,
+                       const void* k, const void* v, int32_t topk, void* out, float* lse_out,
+                       int32_t* topk_idx, float* pooled_out, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  int st = check_shape(s, false, pg != nullptr);
   if (st) return st;
+  if ((st = check_paged(s, pg))) return st;
   if (!q || !k || !v || !out || !topk_idx) return KASCADE_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return KASCADE_ERR_ARG;
   if (topk < 1 || topk > s->ctx_len) return KASCADE_ERR_TOPK;
@@ -457,10 +494,11 @@ int kascade_anchor_decode(const kascade_shape* s, const void* q, const void* k, 
   DeviceInfo* dev = nullptr;
   if ((st = device_setup(&dev))) return st;
   DecodePlan p;
-  if ((st = plan_decode_dev(dev, s, s->ctx_len, false, true, true, &p))) return st;
+  if ((st = plan_decode_dev(dev, s, s->ctx_len, false, true, true, pg != nullptr, &p))) return st;
   if (p.kps > decode_max_kps(s, true)) return KASCADE_ERR_SHAPE;   // LDS score buffer
   char* w = reinterpret_cast<char*>(ws);
   DecodeArgs a = decode_args(s, q, k, v, s->ctx_len, p, w);
+  set_paged(a, s, pg);
   a.scores = reinterpret_cast<float*>(w + p.off_scores);
   a.hist0 = reinterpret_cast<uint32_t*>(w + p.off_hist);
   if (p.wide_chunks) {
@@ -516,11 +554,13 @@ int kascade_anchor_decode(const kascade_shape* s, const void* q, const void* k, 
   return hip_status(e);
 }
 
-int kascade_reuse_decode(const kascade_shape* s, const void* q, const void* k, const void* v,
-                         int32_t topk, const int32_t* idx, const int32_t* head_map, void* out,
-                         void* ws, size_t ws_bytes, hipStream_t stream) {
-  int st = check_shape(s, false);
+static int reuse_decode_impl(const kascade_shape* s, const kascade_paged_kv* pg, const void* q,
+                      const void* k, const void* v, int32_t topk, const int32_t* idx,
+                      const int32_t* head_map, void* out, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  int st = check_shape(s, false, pg != nullptr);
   if (st) return st;
+  if ((st = check_paged(s, pg))) return st;
   if (!q || !k || !v || !out || !idx) return KASCADE_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return KASCADE_ERR_ARG;
   if (topk < 1 || topk > s->ctx_len) return KASCADE_ERR_TOPK;
@@ -530,10 +570,11 @@ int kascade_reuse_decode(const kascade_shape* s, const void* q, const void* k, c
   DeviceInfo* dev = nullptr;
   if ((st = device_setup(&dev))) return st;
   DecodePlan p;
-  if ((st = plan_decode_dev(dev, s, topk, true, false, false, &p))) return st;
+  if ((st = plan_decode_dev(dev, s, topk, true, false, false, pg != nullptr, &p))) return st;
   if (p.kps > kMaxGatherKeys) return KASCADE_ERR_SHAPE;
   char* w = reinterpret_cast<char*>(ws);
   DecodeArgs a = decode_args(s, q, k, v, topk, p, w);
+  set_paged(a, s, pg);
   a.idx = idx;
   a.idx_sg = topk;
   a.idx_sb = (int64_t)s->n_kv_heads * topk;
@@ -548,6 +589,38 @@ int kascade_reuse_decode(const kascade_shape* s, const void* q, const void* k, c
   return hip_status(e);
 }
 
+int kascade_anchor_decode(const kascade_shape* s, const void* q, const void* k, const void* v,
+                          int32_t topk, void* out, float* lse_out, int32_t* topk_idx,
+                          float* pooled_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return anchor_decode_impl(s, nullptr, q, k, v, topk, out, lse_out, topk_idx, pooled_out, ws,
+                            ws_bytes, stream);
+}
+
+int kascade_reuse_decode(const kascade_shape* s, const void* q, const void* k, const void* v,
+                         int32_t topk, const int32_t* idx, const int32_t* head_map, void* out,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
+  return reuse_decode_impl(s, nullptr, q, k, v, topk, idx, head_map, out, ws, ws_bytes, stream);
+}
+
+int kascade_anchor_decode_paged(const kascade_shape* s, const kascade_paged_kv* paged,
+                                const void* q, const void* k_cache, const void* v_cache,
+                                int32_t topk, void* out, float* lse_out, int32_t* topk_idx,
+                                float* pooled_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!paged) return KASCADE_ERR_NULL;
+  return anchor_decode_impl(s, paged, q, k_cache, v_cache, topk, out, lse_out, topk_idx,
+                            pooled_out, ws, ws_bytes, stream);
+}
+
+int kascade_reuse_decode_paged(const kascade_shape* s, const kascade_paged_kv* paged,
+                               const void* q, const void* k_cache, const void* v_cache,
+                               int32_t topk, const int32_t* anchor_topk_idx,
+                               const int32_t* head_map, void* out, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  if (!paged) return KASCADE_ERR_NULL;
+  return reuse_decode_impl(s, paged, q, k_cache, v_cache, topk, anchor_topk_idx, head_map, out, ws,
+                           ws_bytes, stream);
+}
+
 int kascade_dense_decode(const kascade_shape* s, const void* q, const void* k, const void* v,
                          void* out, float* lse_out, void* ws, size_t ws_bytes,
                          hipStream_t stream) {
@@ -560,7 +633,7 @@ int kascade_dense_decode(const kascade_shape* s, const void* q, const void* k, c
   DeviceInfo* dev = nullptr;
   if ((st = device_setup(&dev))) return st;
   DecodePlan p;
-  if ((st = plan_decode_dev(dev, s, s->ctx_len, false, false, false, &p))) return st;
+  if ((st = plan_decode_dev(dev, s, s->ctx_len, false, false, false, false, &p))) return st;
   char* w = reinterpret_cast<char*>(ws);
   DecodeArgs a = decode_args(s, q, k, v, s->ctx_len, p, w);
   hipError_t e = timed(KASCADE_K_DECODE_SPLITK, stream,

@@ -15,6 +15,8 @@
 // registers; a score is the 16-lane DPP sum of the lanes' partial dots, so K
 // is read once for all G heads of the group.  Softmax runs in the log2
 // domain (scale folded with log2(e), v_exp_f32).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -329,16 +331,20 @@ KC_INLINE void slots_from_own(uint32_t own_v, uint32_t (&out)[G]) {
   }
 }
 
-template <int G, bool GATHER, bool SPILL, int kRows = 4>
+template <int G, bool GATHER, bool SPILL, bool PAGED = false, int kRows = 4>
 __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeArgs a) {
   constexpr int D = 128;
   constexpr int LG = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
   static_assert(kRows % 4 == 0, "list entries are read four at a time");
   constexpr int kWaveRows = 4 * kRows;  // rows per wave per step
+  // the split's rows go through an LDS list when they are gathered or paged
+  constexpr bool LIST = GATHER || PAGED;
   __shared__ float s_m[4][G];
   __shared__ float s_l[4][G];
   __shared__ float s_o[4][G][D];
-  extern __shared__ __align__(16) int32_t s_list[];   // kps + kListPad entries
+  // dynamic LDS: the row list (kps + kListPad entries: cache positions, or
+  // physical row numbers when paged), then the spilled scores
+  extern __shared__ __align__(16) int32_t s_list[];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -357,9 +363,20 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
       if (tid == 0) a.ncand[row] = 0u;
     }
   }
-  if (GATHER) {
+  if (LIST) {
     const int32_t* list = a.idx + (int64_t)b * a.idx_sb + (int64_t)a.hm.m[g] * a.idx_sg;
-    for (int i = tid; i < k1 - k0; i += kThreads) s_list[i] = list[k0 + i];
+    for (int i = tid; i < k1 - k0; i += kThreads) {
+      int j = GATHER ? list[k0 + i] : k0 + i;
+      if (PAGED) {
+        // logical position -> physical row (positions and blocks clamped so a
+        // bad list or table cannot fault)
+        j = min(max(j, 0), a.n_ctx - 1);
+        const int blk = min(max(a.table[(int64_t)b * a.table_stride + (j >> a.blk_shift)], 0),
+                            a.num_blocks - 1);
+        j = (int)((uint32_t)blk * (uint32_t)a.blk_rows + (uint32_t)(j & ((1 << a.blk_shift) - 1)));
+      }
+      s_list[i] = j;
+    }
     __syncthreads();
   }
 
@@ -371,9 +388,12 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
                          (int64_t)(g * G + (k ^ own)) * a.q_sh;
     qs[k] = ld16(reinterpret_cast<const char*>(qp) + li * 16);
   }
-  // 32-bit byte offsets from the head's base (the host keeps a head under 4 GiB)
+  // 32-bit byte offsets from the head's base (the host keeps a head under
+  // 4 GiB); paged caches use 64-bit offsets of physical rows
   const uint32_t row_bytes = (uint32_t)a.kv_sn * (uint32_t)sizeof(uint16_t);
-  const int64_t head_off = ((int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh) * (int64_t)sizeof(uint16_t);
+  const int64_t head_off =
+      ((PAGED ? 0 : (int64_t)b * a.kv_sb) + (int64_t)g * a.kv_sh) * (int64_t)sizeof(uint16_t);
+  const uint32_t max_row = PAGED ? (uint32_t)(a.num_blocks * a.blk_rows - 1) : (uint32_t)(a.n_ctx - 1);
   const char* kbase = reinterpret_cast<const char*>(a.k) + head_off;
   const char* vbase = reinterpret_cast<const char*>(a.v) + head_off;
   const uint32_t lane_off = (uint32_t)li * 16u;
@@ -389,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
   // group's scores in LDS ([G][kps + kSpillPad]); the split's scores leave in
   // one coalesced burst after the loop.  Stores issued inside the loop would
   // share vmcnt with the K/V loads and hold up every following wait.
-  float* const s_sc = reinterpret_cast<float*>(s_list);
+  float* const s_sc = reinterpret_cast<float*>(s_list) + (PAGED ? a.keys_per_split + kListPad : 0);
 
   // each wave takes a contiguous quarter of the split; in a step, lane group
   // gi takes kRows consecutive rows
@@ -399,8 +419,9 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
   for (int c = w0; c < w1; c += kWaveRows) {
     const bool full = c + kWaveRows <= w1;   // uniform over the wave
     const int r0 = c + kRows * gi;
-    uint32_t off[kRows];
-    if (GATHER) {
+    typedef typename std::conditional<PAGED, uint64_t, uint32_t>::type off_t;
+    off_t off[kRows];
+    if (LIST) {
       // entries past w1 are read (the LDS list is padded) and replaced below
 #pragma unroll
       for (int t4 = 0; t4 < kRows; t4 += 4) {
@@ -408,9 +429,9 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
         const int jj[4] = {j4.x, j4.y, j4.z, j4.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          // gathered positions are clamped into the cache so a bad list cannot fault
-          const int j = min(max(jj[u], 0), a.n_ctx - 1);
-          off[t4 + u] = (uint32_t)j * row_bytes + lane_off;
+          // rows are clamped into the cache so a bad list cannot fault
+          const uint32_t j = PAGED ? min((uint32_t)jj[u], max_row) : (uint32_t)min(max(jj[u], 0), (int)max_row);
+          off[t4 + u] = (off_t)j * row_bytes + lane_off;
         }
       }
     } else {
@@ -718,18 +739,25 @@ __global__ __launch_bounds__(256) void k_decode_pool(const PoolDecodeArgs a) {
   }
 }
 
-// bf16 caches run the head-slot kernel, fp32 caches the plain one.
-template <typename T, int G, bool GATHER, bool SPILL>
+// bf16 caches run the head-slot kernel, fp32 caches the plain one (which
+// has no paged variant: the host rejects paged fp32).
+template <typename T, int G, bool GATHER, bool SPILL, bool PAGED = false>
 constexpr void (*splitk_kernel())(const DecodeArgs) {
-  if constexpr (sizeof(T) == 2) return k_decode_splitk_slots<G, GATHER, SPILL>;
+  if constexpr (sizeof(T) == 2) return k_decode_splitk_slots<G, GATHER, SPILL, PAGED>;
   else return k_decode_splitk<T, G, GATHER, SPILL>;
 }
 
+template <typename T, int G, bool PAGED>
+void (*splitk_pick(bool gather, bool spill))(const DecodeArgs) {
+  return gather ? splitk_kernel<T, G, true, false, PAGED>()
+         : spill ? splitk_kernel<T, G, false, true, PAGED>()
+                 : splitk_kernel<T, G, false, false, PAGED>();
+}
+
 template <typename T, int G>
-hipError_t splitk_attrs_t(bool gather, bool spill, int* blocks, size_t* static_lds) {
-  void (*k)(const DecodeArgs) = gather ? splitk_kernel<T, G, true, false>()
-                                : spill ? splitk_kernel<T, G, false, true>()
-                                        : splitk_kernel<T, G, false, false>();
+hipError_t splitk_attrs_t(bool gather, bool spill, bool paged, int* blocks, size_t* static_lds) {
+  void (*k)(const DecodeArgs) = paged ? splitk_pick<T, G, true>(gather, spill)
+                                      : splitk_pick<T, G, false>(gather, spill);
   hipFuncAttributes fa;
   hipError_t e = hipFuncGetAttributes(&fa, (const void*)k);
   if (e != hipSuccess) return e;
@@ -738,37 +766,42 @@ hipError_t splitk_attrs_t(bool gather, bool spill, int* blocks, size_t* static_l
 }
 
 template <typename T>
-hipError_t splitk_attrs_g(int G, bool gather, bool spill, int* blocks, size_t* static_lds) {
+hipError_t splitk_attrs_g(int G, bool gather, bool spill, bool paged, int* blocks,
+                          size_t* static_lds) {
   switch (G) {
-    case 1: return splitk_attrs_t<T, 1>(gather, spill, blocks, static_lds);
-    case 2: return splitk_attrs_t<T, 2>(gather, spill, blocks, static_lds);
-    case 4: return splitk_attrs_t<T, 4>(gather, spill, blocks, static_lds);
-    case 8: return splitk_attrs_t<T, 8>(gather, spill, blocks, static_lds);
+    case 1: return splitk_attrs_t<T, 1>(gather, spill, paged, blocks, static_lds);
+    case 2: return splitk_attrs_t<T, 2>(gather, spill, paged, blocks, static_lds);
+    case 4: return splitk_attrs_t<T, 4>(gather, spill, paged, blocks, static_lds);
+    case 8: return splitk_attrs_t<T, 8>(gather, spill, paged, blocks, static_lds);
   }
   return hipErrorInvalidValue;
 }
 
 template <int G>
 hipError_t spill_set_lds_g() {
-  return hipFuncSetAttribute((const void*)k_decode_splitk_slots<G, false, true>,
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSpillMaxLds);
+  hipError_t e = hipFuncSetAttribute((const void*)k_decode_splitk_slots<G, false, true>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSpillMaxLds);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)k_decode_splitk_slots<G, false, true, true>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)(kSpillMaxLds + (kPlanMaxKeys + kListPad) * sizeof(int32_t)));
 }
 
 template <typename T, int G>
 hipError_t launch_splitk_t(const DecodeArgs& a, bool gather, hipStream_t s) {
   if (a.n_splits > kMaxSplits || a.n_splits < 1) return hipErrorInvalidValue;
-  if (gather && a.keys_per_split > kMaxGatherKeys) return hipErrorInvalidValue;
+  const bool paged = a.table != nullptr;
+  if (paged && sizeof(T) != 2) return hipErrorInvalidValue;
+  if ((gather || paged) && a.keys_per_split > kMaxGatherKeys) return hipErrorInvalidValue;
+  const bool spill = !gather && a.scores;
+  const size_t lds = decode_splitk_dyn_lds(sizeof(T) == 2 ? 1 : 0, G, gather, spill, paged,
+                                           a.keys_per_split);
+  if (spill && lds > kSpillMaxLds + (paged ? (kPlanMaxKeys + kListPad) * sizeof(int32_t) : 0))
+    return hipErrorInvalidValue;
   dim3 grid(a.n_splits, a.Hkv, a.B);
-  if (gather) {
-    size_t lds = (size_t)(a.keys_per_split + kListPad) * sizeof(int32_t);
-    hipLaunchKernelGGL((splitk_kernel<T, G, true, false>()), grid, dim3(kThreads), lds, s, a);
-  } else if (a.scores) {
-    const size_t lds = sizeof(T) == 2 ? spill_lds_bytes(G, a.keys_per_split) : 0;
-    if (lds > kSpillMaxLds) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((splitk_kernel<T, G, false, true>()), grid, dim3(kThreads), lds, s, a);
-  } else {
-    hipLaunchKernelGGL((splitk_kernel<T, G, false, false>()), grid, dim3(kThreads), 0, s, a);
-  }
+  void (*k)(const DecodeArgs) = paged ? splitk_pick<T, G, true>(gather, spill)
+                                      : splitk_pick<T, G, false>(gather, spill);
+  hipLaunchKernelGGL(k, grid, dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -802,16 +835,16 @@ hipError_t decode_set_max_lds() {
   return spill_set_lds_g<8>();
 }
 
-hipError_t decode_splitk_attrs(int dtype, int G, bool gather, bool spill, int* blocks,
+hipError_t decode_splitk_attrs(int dtype, int G, bool gather, bool spill, bool paged, int* blocks,
                                size_t* static_lds) {
-  return dtype == 1 ? splitk_attrs_g<uint16_t>(G, gather, spill, blocks, static_lds)
-                    : splitk_attrs_g<float>(G, gather, spill, blocks, static_lds);
+  return dtype == 1 ? splitk_attrs_g<uint16_t>(G, gather, spill, paged, blocks, static_lds)
+                    : splitk_attrs_g<float>(G, gather, spill, paged, blocks, static_lds);
 }
 
-size_t decode_splitk_dyn_lds(int dtype, int G, bool gather, bool spill, int kps) {
-  if (gather) return (size_t)(kps + kListPad) * sizeof(int32_t);
-  if (spill && dtype == 1) return spill_lds_bytes(G, kps);
-  return 0;
+size_t decode_splitk_dyn_lds(int dtype, int G, bool gather, bool spill, bool paged, int kps) {
+  size_t bytes = (gather || paged) ? (size_t)(kps + kListPad) * sizeof(int32_t) : 0;
+  if (spill && dtype == 1) bytes += spill_lds_bytes(G, kps);
+  return bytes;
 }
 
 hipError_t launch_decode_splitk(const DecodeArgs& a, int dtype, bool gather, hipStream_t s) {

@@ -31,6 +31,12 @@ struct DecodeArgs {
   uint32_t* hist0;               // [B*Hkv][2048] zeroed here for the pooling kernel, or null
   uint32_t* hist1;               // [B*Hkv][2048] zeroed here for the wide select, or null
   uint32_t* ncand;               // [B*Hkv] zeroed here for the wide select, or null
+  // paged caches: key j of batch b is row (j & (bs-1)) of physical block
+  // table[b * table_stride + (j >> blk_shift)]; physical row number
+  // R = block * blk_rows + row, address = base + g*kv_sh + R*kv_sn (elements)
+  const int32_t* table;
+  int32_t table_stride, blk_shift, num_blocks;
+  int64_t blk_rows;
 };
 
 struct CombineArgs {
@@ -99,9 +105,10 @@ int spill_max_keys(int G);
 hipError_t decode_set_max_lds();
 // Split-K kernel variant: workgroups per CU without dynamic LDS, its static
 // LDS, and the dynamic LDS of a split of kps keys.
-hipError_t decode_splitk_attrs(int dtype, int G, bool gather, bool spill, int* blocks,
+hipError_t decode_splitk_attrs(int dtype, int G, bool gather, bool spill, bool paged, int* blocks,
                                size_t* static_lds);
-size_t decode_splitk_dyn_lds(int dtype, int G, bool gather, bool spill, int kps);
+size_t decode_splitk_dyn_lds(int dtype, int G, bool gather, bool spill, bool paged, int kps);
+// paged: a.table is set (bf16 only)
 hipError_t launch_decode_splitk(const DecodeArgs& a, int dtype, bool gather, hipStream_t s);
 hipError_t launch_decode_combine(const CombineArgs& a, int dtype, hipStream_t s);
 hipError_t launch_decode_pool(const PoolDecodeArgs& a, hipStream_t s);

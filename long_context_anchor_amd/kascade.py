@@ -31,6 +31,7 @@ EXPORTS = [
     "kascade_topk_select_f32", "kascade_dense_decode", "kascade_dense_prefill",
     "kascade_kernel_timer_enable", "kascade_kernel_timer_read", "kascade_status_str",
     "kascade_last_hip_error", "kascade_version",
+    "kascade_anchor_decode_paged", "kascade_reuse_decode_paged",
     "kascade_calib_head_similarity", "kascade_layer_weight", "kascade_layer_weight_workspace_bytes",
     "kascade_weighted_similarity", "kascade_select_anchors", "kascade_head_maps",
 ]
@@ -44,6 +45,12 @@ class Shape(ctypes.Structure):
         ("q_stride_b", ctypes.c_int64), ("q_stride_h", ctypes.c_int64), ("q_stride_n", ctypes.c_int64),
         ("kv_stride_b", ctypes.c_int64), ("kv_stride_h", ctypes.c_int64), ("kv_stride_n", ctypes.c_int64),
     ]
+
+
+class PagedKV(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("table_stride", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("block_stride", ctypes.c_int64)]
 
 
 class TopkRule(ctypes.Structure):
@@ -82,6 +89,8 @@ _SIGS = {
     "kascade_status_str": (ctypes.c_char_p, [_i32]),
     "kascade_last_hip_error": (_i32, []),
     "kascade_version": (ctypes.c_char_p, []),
+    "kascade_anchor_decode_paged": (_i32, [ctypes.POINTER(Shape), ctypes.POINTER(PagedKV), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kascade_reuse_decode_paged": (_i32, [ctypes.POINTER(Shape), ctypes.POINTER(PagedKV), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kascade_calib_head_similarity": (_i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "kascade_layer_weight": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "kascade_layer_weight_workspace_bytes": (_sz, [_i32]),
@@ -191,6 +200,23 @@ def kascade_kernel_timer_read(kernel_id: int):
     if st:
         raise KascadeError(st, "kascade_kernel_timer_read")
     return ms.value, n.value
+
+
+def kascade_anchor_decode_paged(shape, paged, q, k_cache, v_cache, topk, out, lse_out, topk_idx, pooled_out,
+                                workspace, workspace_bytes, stream=None) -> int:
+    return lib().kascade_anchor_decode_paged(ctypes.byref(shape), ctypes.byref(paged), _p(q), _p(k_cache),
+                                             _p(v_cache), topk, _p(out), _p(lse_out), _p(topk_idx),
+                                             _p(pooled_out), _p(workspace), workspace_bytes,
+                                             _stream(stream))
+
+
+def kascade_reuse_decode_paged(shape, paged, q, k_cache, v_cache, topk, anchor_topk_idx, head_map, out,
+                               workspace, workspace_bytes, stream=None) -> int:
+    hm = (ctypes.c_int32 * len(head_map))(*[int(x) for x in head_map]) if head_map is not None else None
+    return lib().kascade_reuse_decode_paged(ctypes.byref(shape), ctypes.byref(paged), _p(q), _p(k_cache),
+                                            _p(v_cache), topk, _p(anchor_topk_idx),
+                                            ctypes.cast(hm, _vp) if hm is not None else None, _p(out),
+                                            _p(workspace), workspace_bytes, _stream(stream))
 
 
 def kascade_calib_head_similarity(L, S, n_kv_heads, n, k, pooled, topk_idx, sim, stream=None) -> int:
@@ -413,4 +439,43 @@ def layer_weight(x, y):
     ws = torch.empty(nb, dtype=torch.uint8, device=x.device)
     check(kascade_layer_weight(x, y, tokens, dim, _dtype_code(x), w, ws, nb), "kascade_layer_weight")
     return w
+
+
+def paged_shape(q, k_cache, n_ctx: int, scale: float = 0.0) -> Shape:
+    """Shape for a paged cache [num_blocks, Hkv, block_size, d] (vLLM-style layout)."""
+    return Shape(q.shape[0], q.shape[1], k_cache.shape[1], q.shape[-1], n_ctx, _dtype_code(q), scale, 0,
+                 q.stride(0), q.stride(1), 0, 0, k_cache.stride(1), k_cache.stride(2))
+
+
+def paged_kv(block_table, k_cache) -> PagedKV:
+    """Descriptor for caches laid out [num_blocks, Hkv, block_size, d]."""
+    return PagedKV(block_table.data_ptr(), block_table.stride(0), k_cache.shape[2], k_cache.shape[0], 0,
+                   k_cache.stride(0))
+
+
+def anchor_decode_paged(q, k_cache, v_cache, block_table, n_ctx: int, topk: int, want_pooled=False):
+    """Paged anchor decode; returns (out, lse, idx, pooled or None)."""
+    sh = paged_shape(q, k_cache, n_ctx)
+    pg = paged_kv(block_table, k_cache)
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    out = torch.empty((B, Hq, d), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    idx = torch.empty((B, Hkv, topk), dtype=torch.int32, device=q.device)
+    pooled = torch.empty((B, Hkv, n_ctx), dtype=torch.float32, device=q.device) if want_pooled else None
+    ws = workspace(OP_ANCHOR_DECODE, sh, topk)
+    check(kascade_anchor_decode_paged(sh, pg, q, k_cache, v_cache, topk, out, lse, idx, pooled, ws, ws.numel()),
+          "kascade_anchor_decode_paged")
+    return out, lse, idx, pooled
+
+
+def reuse_decode_paged(q, k_cache, v_cache, block_table, n_ctx: int, anchor_idx, head_map):
+    sh = paged_shape(q, k_cache, n_ctx)
+    pg = paged_kv(block_table, k_cache)
+    topk = anchor_idx.shape[-1]
+    out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    ws = workspace(OP_REUSE_DECODE, sh, topk)
+    check(kascade_reuse_decode_paged(sh, pg, q, k_cache, v_cache, topk, anchor_idx, head_map, out, ws,
+                                     ws.numel()), "kascade_reuse_decode_paged")
+    return out
 

@@ -121,3 +121,31 @@ def test_select_validation():
 
 def test_timer_api_bounds():
     assert K.lib().kascade_kernel_timer_enable(99, 1) == -8
+
+
+def test_paged_decode_validation_errors():
+    """Paged entry points reject bad descriptors before any device call."""
+    sh = _shape(N=1000, d=128, Hq=8, Hkv=2, dtype=K.KASCADE_BF16)
+    sh.kv_stride_b = 0
+    sh.kv_stride_h = 16 * 128
+    ws = 1 << 30
+
+    def desc(**kw):
+        pg = K.PagedKV(FAKE, 70, 16, 200, 0, 2 * 16 * 128)
+        for f, v in kw.items():
+            setattr(pg, f, v)
+        return pg
+
+    def anchor(pg, shape=sh):
+        return K.kascade_anchor_decode_paged(shape, pg, FAKE, FAKE, FAKE, 10, FAKE, None, FAKE, None, FAKE,
+                                             ws, 0)
+
+    assert anchor(desc(block_size=24)) == -2        # not a power of two
+    assert anchor(desc(table_stride=10)) == -2      # table shorter than ceil(N / block_size)
+    assert anchor(desc(reserved=1)) == -8
+    assert anchor(desc(block_stride=100)) == -2     # not a multiple of the row stride
+    assert anchor(desc(block_stride=16 * 128)) == -2    # second head's rows outside the block
+    assert anchor(desc(block_table=None)) == -1
+    assert anchor(desc(block_size=32), shape=_shape(N=1000)) == -3   # fp32 caches are not paged
+    assert K.kascade_reuse_decode_paged(sh, desc(block_table=None), FAKE, FAKE, FAKE, 10, FAKE, [0, 1], FAKE,
+                                        FAKE, ws, 0) == -1
