@@ -368,6 +368,81 @@ def calibration_bench(torch, K, synth, configs, args):
     }), flush=True)
 
 
+def paged_bench(torch, K, synth, configs, args):
+    """Decode over paged caches (block size 16, blocks scattered by a seeded
+    permutation) against the same layers in contiguous caches, on the 32K
+    (B=1) and 128K (B=4) Llama-shaped workloads with 8 distinct layers each.
+    Prints one JSON line."""
+    res = {}
+    for cid, name in ((2, "decode32k"), (3, "decode128k")):
+        cfg = configs.CONFIGS[cid]
+        N, B, Hkv, k = cfg.ctx_len, cfg.batch, cfg.n_kv_heads, cfg.topk
+        bs, nl = 16, 8
+        lin = synth.heavy_lineages(cfg.seed, nl, Hkv, N, cfg.heavy, cfg.drift)
+        maps = synth.head_maps(cfg.seed, nl, (0,), Hkv, cfg.head_map_kind)
+        nb = N // bs
+        rng = np.random.default_rng(cid)
+        layers = []
+        for l in range(nl):
+            q, kk, v = synth.decode_layer(cfg.seed, l, B, cfg.n_q_heads, Hkv, cfg.head_dim, N,
+                                          synth.layer_heavy_sets(lin, l, (0,), maps), cfg.alpha, cfg.dtype,
+                                          device="cuda")
+            perm = torch.as_tensor(rng.permutation(B * nb).reshape(B, nb), dtype=torch.int64, device="cuda")
+            kc = torch.empty((B * nb, Hkv, bs, cfg.head_dim), dtype=kk.dtype, device="cuda")
+            vc = torch.empty_like(kc)
+            kc[perm.reshape(-1)] = kk.view(B, Hkv, nb, bs, -1).permute(0, 2, 1, 3, 4).reshape(B * nb, Hkv, bs, -1)
+            vc[perm.reshape(-1)] = v.view(B, Hkv, nb, bs, -1).permute(0, 2, 1, 3, 4).reshape(B * nb, Hkv, bs, -1)
+            layers.append((q, kk, v, kc, vc, perm.to(torch.int32).contiguous()))
+        sh = K.make_shape(layers[0][0], layers[0][1], N)
+        shp = K.paged_shape(layers[0][0], layers[0][3], N)
+        ws_a = K.workspace(K.OP_ANCHOR_DECODE, sh, k)
+        ws_r = K.workspace(K.OP_REUSE_DECODE, sh, k)
+        idx = torch.empty((B, Hkv, k), dtype=torch.int32, device="cuda")
+        out = torch.empty_like(layers[0][0])
+
+        def run(kind, paged):
+            for q, kk, v, kc, vc, tab in layers:
+                if paged:
+                    pg = K.paged_kv(tab, kc)
+                    if kind == "anchor":
+                        K.check(K.kascade_anchor_decode_paged(shp, pg, q, kc, vc, k, out, None, idx, None, ws_a,
+                                                              ws_a.numel()), "anchor_paged")
+                    else:
+                        K.check(K.kascade_reuse_decode_paged(shp, pg, q, kc, vc, k, idx, maps[1], out, ws_r,
+                                                             ws_r.numel()), "reuse_paged")
+                elif kind == "anchor":
+                    K.check(K.kascade_anchor_decode(sh, q, kk, v, k, out, None, idx, None, ws_a, ws_a.numel()),
+                            "anchor")
+                else:
+                    K.check(K.kascade_reuse_decode(sh, q, kk, v, k, idx, maps[1], out, ws_r, ws_r.numel()),
+                            "reuse")
+
+        row = {}
+        for kind in ("anchor", "reuse"):
+            for paged in (False, True):
+                for _ in range(args.warmup):
+                    run(kind, paged)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(args.steps):
+                    run(kind, paged)
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / (args.steps * nl)
+                by = 2 * B * Hkv * (N if kind == "anchor" else k) * cfg.head_dim * 2
+                row["%s_%s_us" % (kind, "paged" if paged else "contig")] = us
+                row["%s_%s_GBps" % (kind, "paged" if paged else "contig")] = by / (us * 1e-6) / 1e9
+        res[name] = row
+        del layers
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "paged-KV decode attention us/layer (block size 16) vs contiguous",
+                      "unit": "us/layer", "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": "Llama-3.1-8B-shaped decode layers, 32q/8kv heads, d=128, "
+                                             "32K B=1 k=3264 and 128K B=4 k=13120, 8 distinct layers"},
+                      "components": res}), flush=True)
+
+
 # ---------------------------------------------------------------------------
 
 def main():
@@ -382,6 +457,8 @@ def main():
                     help="one launch of each kernel plus a calibration copy, for rocprofv3 --pmc")
     ap.add_argument("--calibration", action="store_true",
                     help="time the offline calibration path (layer-pair similarities, DP, head maps)")
+    ap.add_argument("--paged", action="store_true",
+                    help="time decode over paged KV caches against contiguous caches")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -402,6 +479,9 @@ def main():
         return
     if args.calibration:
         calibration_bench(torch, K, synth, configs, args)
+        return
+    if args.paged:
+        paged_bench(torch, K, synth, configs, args)
         return
 
     sections = ["decode32k", "decode128k", "prefill"] if args.only is None else [args.only]

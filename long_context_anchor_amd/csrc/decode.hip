@@ -377,6 +377,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
       }
       s_list[i] = j;
     }
+    // a step may read up to 15 entries past the split's rows: make them row 0
+    for (int i = (k1 - k0) + tid; i < (k1 - k0) + kListPad; i += kThreads) s_list[i] = 0;
     __syncthreads();
   }
 
@@ -393,7 +395,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
   const uint32_t row_bytes = (uint32_t)a.kv_sn * (uint32_t)sizeof(uint16_t);
   const int64_t head_off =
       ((PAGED ? 0 : (int64_t)b * a.kv_sb) + (int64_t)g * a.kv_sh) * (int64_t)sizeof(uint16_t);
-  const uint32_t max_row = PAGED ? (uint32_t)(a.num_blocks * a.blk_rows - 1) : (uint32_t)(a.n_ctx - 1);
+  // last valid row: head g's rows of the last block end at row bs-1 (the
+  // head offset is added to every row address)
+  const uint32_t max_row = PAGED ? (uint32_t)((a.num_blocks - 1) * a.blk_rows + ((1 << a.blk_shift) - 1))
+                                 : (uint32_t)(a.n_ctx - 1);
   const char* kbase = reinterpret_cast<const char*>(a.k) + head_off;
   const char* vbase = reinterpret_cast<const char*>(a.v) + head_off;
   const uint32_t lane_off = (uint32_t)li * 16u;
