@@ -36,12 +36,12 @@
  *             identical outputs.
  * Workspace.  Scratch only: no contents carry over between calls, any
  *             initial contents are fine.
- * Supported.  dtype F32 with head_dim 64, dtype BF16 with head_dim 128
- *             (one 256-byte K/V row in both cases).  Prefill: BF16,
- *             head_dim 128, tile 128, batch 1..65535, Hq/Hkv in {1,2,4,8}.
- *             Decode: ctx_len * kv_stride_n * element size below 4 GiB
- *             (one head's rows; 16.7M keys at 256 bytes per row); a bf16
- *             anchor decode also needs ctx_len <= 2048 * spill split (about
+ * Supported.  dtype F32 with head_dim 64, dtype BF16 or F16 with head_dim
+ *             128 (one 256-byte K/V row in every case).  Prefill: BF16 or
+ *             F16, head_dim 128, tile 128, batch 1..65535, Hq/Hkv in
+ *             {1,2,4,8}.  Decode: ctx_len * kv_stride_n * element size below
+ *             4 GiB (one head's rows; 16.7M keys at 256 bytes per row); a
+ *             16-bit anchor decode also needs ctx_len <= 2048 * spill split (about
  *             8.6M keys for Hq/Hkv <= 4, 4.3M for 8), else KASCADE_ERR_SHAPE.
  * Threads.    Calls are thread-safe on distinct streams with distinct
  *             workspaces.
@@ -69,7 +69,7 @@ typedef enum {
   KASCADE_ERR_ARG = -8         /* another argument is out of range           */
 } kascade_status;
 
-typedef enum { KASCADE_F32 = 0, KASCADE_BF16 = 1 } kascade_dtype;
+typedef enum { KASCADE_F32 = 0, KASCADE_BF16 = 1, KASCADE_F16 = 2 } kascade_dtype;
 
 typedef struct kascade_shape {
   int32_t batch;        /* B                                                */
@@ -127,7 +127,7 @@ int kascade_reuse_decode(const kascade_shape* shape, const void* q, const void* 
 
 /* Anchor-layer prefill (causal).  [Abstract]: tile-level operations in
  * prefill; [Explainer] "実装のポイント": 128-query tiles.
- *   out  [B,Hq,N,d] bf16 dense causal attention; lse_out [B,Hq,N] or NULL
+ *   out  [B,Hq,N,d] dense causal attention (input dtype); lse_out [B,Hq,N] or NULL
  *   tile_topk_idx [B,T,Hkv,k_max] int32, T = ceil(N/tile), k_max = k of the
  *        last tile: row (b,t,g) holds the k_t positions j < P_t with the
  *        largest pooled probability sum over the G heads of group g and the
@@ -161,7 +161,7 @@ int kascade_reuse_prefill(const kascade_shape* shape, const void* q, const void*
  * block_size: a power of two; block_stride: a multiple of kv_stride_n, every
  * head's block_size rows inside it, num_blocks * (block_stride / kv_stride_n)
  * below 2^32.  Table entries and positions are clamped into range, so a bad
- * table cannot fault.  bf16 only. */
+ * table cannot fault.  BF16 or F16 only. */
 typedef struct kascade_paged_kv {
   const int32_t* block_table;   /* DEVICE int32 [B, table_stride], table_stride >= ceil(N / block_size) */
   int32_t table_stride;
@@ -204,8 +204,8 @@ int kascade_calib_head_similarity(int32_t L, int32_t S, int32_t n_kv_heads, int3
                                   hipStream_t stream);
 
 /* Layer weight, [Explainer] eq. w: *w_out = 1 - mean over tokens t of
- * cos(x_t, y_t), x and y [tokens, dim] device arrays in `dtype` (F32 or
- * BF16), the layer's input and output hidden states.  w_out: one float,
+ * cos(x_t, y_t), x and y [tokens, dim] device arrays in `dtype` (F32,
+ * BF16 or F16), the layer's input and output hidden states.  w_out: one float,
  * device.  NaN if some token has a zero vector.  Workspace: at least
  * kascade_layer_weight_workspace_bytes(tokens), contents irrelevant. */
 int kascade_layer_weight(const void* x, const void* y, int32_t tokens, int32_t dim, int32_t dtype,

@@ -25,8 +25,8 @@ struct DeviceInfo {
   // split-K variants [dtype][log2 G][kind] (kind 0 dense, 1 dense + score
   // spill, 2 gather; +3 for a paged cache): resident workgroups per CU
   // without dynamic LDS (0 = not queried yet) and static LDS bytes
-  int splitk_bpc[2][4][6] = {};
-  size_t splitk_lds[2][4][6] = {};
+  int splitk_bpc[3][4][6] = {};
+  size_t splitk_lds[3][4][6] = {};
 };
 DeviceInfo g_dev[kMaxDevices];
 std::mutex g_dev_mu;
@@ -85,7 +85,7 @@ int splitk_slots(DeviceInfo* d, int dtype, int G, bool gather, bool spill, bool 
                  int* slots) {
   const int lg = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
   const int kind = (gather ? 2 : spill ? 1 : 0) + (paged ? 3 : 0);
-  const int dt = dtype == KASCADE_BF16 ? 1 : 0;
+  const int dt = dtype == KASCADE_F16 ? 2 : dtype == KASCADE_BF16 ? 1 : 0;
   int bpc;
   size_t st;
   {
@@ -165,7 +165,7 @@ int hip_status(hipError_t e) {
 }
 
 // ---- validation ---------------------------------------------------------------
-size_t elem_size(int dtype) { return dtype == KASCADE_BF16 ? 2 : 4; }
+size_t elem_size(int dtype) { return dtype == KASCADE_F32 ? 4 : 2; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -180,7 +180,7 @@ int check_shape(const kascade_shape* s, bool prefill, bool paged = false) {
   if (G != 1 && G != 2 && G != 4 && G != 8) return KASCADE_ERR_SHAPE;
   if (s->dtype == KASCADE_F32) {
     if (s->head_dim != 64 || prefill) return KASCADE_ERR_DTYPE;
-  } else if (s->dtype == KASCADE_BF16) {
+  } else if (s->dtype == KASCADE_BF16 || s->dtype == KASCADE_F16) {
     if (s->head_dim != 128) return KASCADE_ERR_DTYPE;
   } else {
     return KASCADE_ERR_DTYPE;
@@ -272,8 +272,8 @@ int decode_splits(int64_t n_keys, int64_t rows, int slots, int64_t max_kps, int*
 }
 
 int64_t decode_max_kps(const kascade_shape* s, bool spill) {
-  return spill && s->dtype == KASCADE_BF16 ? spill_max_keys(s->n_q_heads / s->n_kv_heads)
-                                           : kPlanMaxKeys;
+  return spill && s->dtype != KASCADE_F32 ? spill_max_keys(s->n_q_heads / s->n_kv_heads)
+                                          : kPlanMaxKeys;
 }
 
 DecodePlan plan_decode(const kascade_shape* s, int n_keys, bool spill, bool pooled_ws,
@@ -398,6 +398,7 @@ PrefillArgs prefill_args(const kascade_shape* s, const void* q, const void* k, c
   a.N = s->ctx_len;
   a.T = (s->ctx_len + 127) / 128;
   a.scale_log2 = scale_log2(s);
+  a.half = s->dtype == KASCADE_F16 ? 1 : 0;
   a.out = out;
   return a;
 }
@@ -452,7 +453,7 @@ static int check_paged(const kascade_shape* s, const kascade_paged_kv* pg) {
   if (!pg) return KASCADE_OK;
   if (!pg->block_table) return KASCADE_ERR_NULL;
   if (pg->reserved != 0) return KASCADE_ERR_ARG;
-  if (s->dtype != KASCADE_BF16) return KASCADE_ERR_DTYPE;
+  if (s->dtype == KASCADE_F32) return KASCADE_ERR_DTYPE;
   const int bs = pg->block_size;
   if (bs < 1 || bs > (1 << 20) || (bs & (bs - 1)) != 0 || pg->num_blocks < 1) return KASCADE_ERR_SHAPE;
   if ((int64_t)pg->table_stride < ((int64_t)s->ctx_len + bs - 1) / bs) return KASCADE_ERR_SHAPE;
@@ -666,7 +667,7 @@ int kascade_layer_weight(const void* x, const void* y, int32_t tokens, int32_t d
                          float* w_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!x || !y || !w_out) return KASCADE_ERR_NULL;
   if (tokens < 1 || dim < 1) return KASCADE_ERR_SHAPE;
-  if (dtype != KASCADE_F32 && dtype != KASCADE_BF16) return KASCADE_ERR_DTYPE;
+  if (dtype != KASCADE_F32 && dtype != KASCADE_BF16 && dtype != KASCADE_F16) return KASCADE_ERR_DTYPE;
   if (!workspace || workspace_bytes < kascade_layer_weight_workspace_bytes(tokens))
     return KASCADE_ERR_WORKSPACE;
   return hip_status(launch_layer_weight(x, y, tokens, dim, dtype, reinterpret_cast<double*>(workspace),

@@ -17,6 +17,8 @@
 // order (no atomics): results are deterministic.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -92,7 +94,10 @@ __global__ __launch_bounds__(kCalThreads) void k_cosine_partial(const T* __restr
     if (t < tokens) {
       for (int i = tid; i < dim; i += kCalThreads) {
         double xv, yv;
-        if constexpr (sizeof(T) == 2) {
+        if constexpr (std::is_same<T, _Float16>::value) {
+          xv = (double)x[(int64_t)t * dim + i];
+          yv = (double)y[(int64_t)t * dim + i];
+        } else if constexpr (sizeof(T) == 2) {
           xv = (double)bf16_lo((uint32_t)x[(int64_t)t * dim + i]);
           yv = (double)bf16_lo((uint32_t)y[(int64_t)t * dim + i]);
         } else {
@@ -139,7 +144,11 @@ hipError_t launch_calib_sim(const float* pooled, const int32_t* idx, int L, int 
 hipError_t launch_layer_weight(const void* x, const void* y, int tokens, int dim, int dtype,
                                double* part, float* w, hipStream_t s) {
   const int nparts = (tokens + 63) / 64;
-  if (dtype == 1)
+  if (dtype == 2)
+    hipLaunchKernelGGL(k_cosine_partial<_Float16>, dim3(nparts), dim3(kCalThreads), 0, s,
+                       reinterpret_cast<const _Float16*>(x), reinterpret_cast<const _Float16*>(y),
+                       tokens, dim, part);
+  else if (dtype == 1)
     hipLaunchKernelGGL(k_cosine_partial<uint16_t>, dim3(nparts), dim3(kCalThreads), 0, s,
                        reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(y),
                        tokens, dim, part);

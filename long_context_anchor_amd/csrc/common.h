@@ -39,6 +39,44 @@ KC_INLINE float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// fp16 counterparts (IEEE half): v_dot2c_f32_f16 and round-to-nearest-even
+// packing on the hardware converter.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+KC_INLINE float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
+                                false);
+}
+KC_INLINE uint32_t pack_f16x2(float lo, float hi) {
+  const f32x2_t x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2_t));
+}
+KC_INLINE float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2_t, w).x;
+}
+
+// 16-bit element formats of the bf16/fp16 kernels.
+template <bool HALF>
+struct Fmt16;
+template <>
+struct Fmt16<false> {   // bf16
+  typedef bf16x8_t v8;
+  static KC_INLINE float dot2(uint32_t a, uint32_t b, float c) { return dot2_bf16(a, b, c); }
+  static KC_INLINE uint32_t pack(float lo, float hi) { return pack_bf16x2(lo, hi); }
+  static KC_INLINE f32x16_t mfma(const v8& a, const v8& b, const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Fmt16<true> {    // fp16
+  typedef f16x8_t v8;
+  static KC_INLINE float dot2(uint32_t a, uint32_t b, float c) { return dot2_f16(a, b, c); }
+  static KC_INLINE uint32_t pack(float lo, float hi) { return pack_f16x2(lo, hi); }
+  static KC_INLINE f32x16_t mfma(const v8& a, const v8& b, const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
 // Cross-lane moves inside a 16-lane DPP row (GFX9 DPP controls).
 enum : int {
   DPP_XOR1 = 0xB1,          // quad_perm [1,0,3,2]

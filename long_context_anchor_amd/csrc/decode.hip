@@ -41,6 +41,11 @@ struct Elem<uint16_t> {
   static constexpr int EPL = 8;    // bf16 per 16 bytes
   static constexpr int D = 128;
 };
+template <>
+struct Elem<_Float16> {
+  static constexpr int EPL = 8;    // fp16 per 16 bytes
+  static constexpr int D = 128;
+};
 
 // Partial dot of a 16-byte slice with a query slice.
 KC_INLINE float slice_dot(const uint4& kk, const uint4& qq, float acc, uint16_t) {
@@ -331,8 +336,9 @@ KC_INLINE void slots_from_own(uint32_t own_v, uint32_t (&out)[G]) {
   }
 }
 
-template <int G, bool GATHER, bool SPILL, bool PAGED = false, int kRows = 4>
+template <int G, bool GATHER, bool SPILL, bool PAGED = false, bool HALF = false, int kRows = 4>
 __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeArgs a) {
+  typedef Fmt16<HALF> F;   // bf16 or fp16 elements
   constexpr int D = 128;
   constexpr int LG = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
   static_assert(kRows % 4 == 0, "list entries are read four at a time");
@@ -460,7 +466,9 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
     for (int t = 0; t < kRows; ++t) {
       float part[G];
 #pragma unroll
-      for (int k = 0; k < G; ++k) part[k] = slice_dot(kr[t], qs[k], 0.f, uint16_t());
+      for (int k = 0; k < G; ++k)
+        part[k] = F::dot2(kr[t].w, qs[k].w, F::dot2(kr[t].z, qs[k].z,
+                  F::dot2(kr[t].y, qs[k].y, F::dot2(kr[t].x, qs[k].x, 0.f))));
       sc[t] = reduce_scatter<G>(part) * a.scale_log2;
     }
     if (!full) {
@@ -512,7 +520,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
 #pragma unroll
     for (int t = 0; t < kRows; t += 2) {
       uint32_t pk[G];
-      slots_from_own<G, LG>(pack_bf16x2(p[t], p[t + 1]), pk);
+      slots_from_own<G, LG>(F::pack(p[t], p[t + 1]), pk);
       const uint32_t w0v[4] = {vr[t].x, vr[t].y, vr[t].z, vr[t].w};
       const uint32_t w1v[4] = {vr[t + 1].x, vr[t + 1].y, vr[t + 1].z, vr[t + 1].w};
 #pragma unroll
@@ -522,8 +530,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
         const uint32_t od = __builtin_amdgcn_perm(w1v[j], w0v[j], 0x07060302u);
 #pragma unroll
         for (int k = 0; k < G; ++k) {
-          o[k][2 * j] = dot2_bf16(ev, pk[k], o[k][2 * j]);
-          o[k][2 * j + 1] = dot2_bf16(od, pk[k], o[k][2 * j + 1]);
+          o[k][2 * j] = F::dot2(ev, pk[k], o[k][2 * j]);
+          o[k][2 * j + 1] = F::dot2(od, pk[k], o[k][2 * j + 1]);
         }
       }
     }
@@ -679,7 +687,9 @@ __global__ __launch_bounds__(kCombineThreads) void k_decode_combine(const Combin
       }
     }
     const float r = Lt > 0.f ? Ot / Lt : 0.f;
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (std::is_same<T, _Float16>::value) {
+      reinterpret_cast<_Float16*>(a.out)[(int64_t)bh * D + tid] = (_Float16)r;
+    } else if constexpr (sizeof(T) == 2) {
       reinterpret_cast<uint16_t*>(a.out)[(int64_t)bh * D + tid] = (uint16_t)f32_to_bf16_bits(r);
     } else {
       reinterpret_cast<float*>(a.out)[(int64_t)bh * D + tid] = r;
@@ -748,7 +758,8 @@ __global__ __launch_bounds__(256) void k_decode_pool(const PoolDecodeArgs a) {
 // has no paged variant: the host rejects paged fp32).
 template <typename T, int G, bool GATHER, bool SPILL, bool PAGED = false>
 constexpr void (*splitk_kernel())(const DecodeArgs) {
-  if constexpr (sizeof(T) == 2) return k_decode_splitk_slots<G, GATHER, SPILL, PAGED>;
+  if constexpr (sizeof(T) == 2)
+    return k_decode_splitk_slots<G, GATHER, SPILL, PAGED, std::is_same<T, _Float16>::value>;
   else return k_decode_splitk<T, G, GATHER, SPILL>;
 }
 
@@ -782,14 +793,19 @@ hipError_t splitk_attrs_g(int G, bool gather, bool spill, bool paged, int* block
   return hipErrorInvalidValue;
 }
 
-template <int G>
-hipError_t spill_set_lds_g() {
-  hipError_t e = hipFuncSetAttribute((const void*)k_decode_splitk_slots<G, false, true>,
+template <int G, bool HALF>
+hipError_t spill_set_lds_gh() {
+  hipError_t e = hipFuncSetAttribute((const void*)k_decode_splitk_slots<G, false, true, false, HALF>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSpillMaxLds);
   if (e != hipSuccess) return e;
-  return hipFuncSetAttribute((const void*)k_decode_splitk_slots<G, false, true, true>,
+  return hipFuncSetAttribute((const void*)k_decode_splitk_slots<G, false, true, true, HALF>,
                              hipFuncAttributeMaxDynamicSharedMemorySize,
                              (int)(kSpillMaxLds + (kPlanMaxKeys + kListPad) * sizeof(int32_t)));
+}
+template <int G>
+hipError_t spill_set_lds_g() {
+  hipError_t e = spill_set_lds_gh<G, false>();
+  return e != hipSuccess ? e : spill_set_lds_gh<G, true>();
 }
 
 template <typename T, int G>
@@ -842,23 +858,27 @@ hipError_t decode_set_max_lds() {
 
 hipError_t decode_splitk_attrs(int dtype, int G, bool gather, bool spill, bool paged, int* blocks,
                                size_t* static_lds) {
+  if (dtype == 2) return splitk_attrs_g<_Float16>(G, gather, spill, paged, blocks, static_lds);
   return dtype == 1 ? splitk_attrs_g<uint16_t>(G, gather, spill, paged, blocks, static_lds)
                     : splitk_attrs_g<float>(G, gather, spill, paged, blocks, static_lds);
 }
 
 size_t decode_splitk_dyn_lds(int dtype, int G, bool gather, bool spill, bool paged, int kps) {
   size_t bytes = (gather || paged) ? (size_t)(kps + kListPad) * sizeof(int32_t) : 0;
-  if (spill && dtype == 1) bytes += spill_lds_bytes(G, kps);
+  if (spill && dtype != 0) bytes += spill_lds_bytes(G, kps);
   return bytes;
 }
 
 hipError_t launch_decode_splitk(const DecodeArgs& a, int dtype, bool gather, hipStream_t s) {
+  if (dtype == 2) return launch_splitk_g<_Float16>(a, gather, s);
   return dtype == 1 ? launch_splitk_g<uint16_t>(a, gather, s) : launch_splitk_g<float>(a, gather, s);
 }
 
 hipError_t launch_decode_combine(const CombineArgs& a, int dtype, hipStream_t s) {
   if (a.n_splits > kMaxSplits) return hipErrorInvalidValue;
-  if (dtype == 1)
+  if (dtype == 2)
+    hipLaunchKernelGGL(k_decode_combine<_Float16>, dim3(a.BH), dim3(kCombineThreads), 0, s, a);
+  else if (dtype == 1)
     hipLaunchKernelGGL(k_decode_combine<uint16_t>, dim3(a.BH), dim3(kCombineThreads), 0, s, a);
   else
     hipLaunchKernelGGL(k_decode_combine<float>, dim3(a.BH), dim3(kCombineThreads), 0, s, a);

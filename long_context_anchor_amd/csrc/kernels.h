@@ -80,7 +80,7 @@ struct PrefillArgs {
   int64_t kv_sb, kv_sh, kv_sn;
   int32_t B, Hq, Hkv, N, T;
   float scale_log2;
-  void* out;                     // [B,Hq,N,128] bf16
+  void* out;                     // [B,Hq,N,128] input dtype
   float* lse2;                   // [B,Hq,N] log2-domain lse (flash writes, pool reads)
   float* lse_out;                // [B,Hq,N] natural log, may be null
   float* pooled;                 // packed pooled rows
@@ -88,6 +88,7 @@ struct PrefillArgs {
   const int32_t* idx;            // sparse: anchor tile lists [B,T,Hkv,k_max]
   int32_t k_max;
   int32_t pct, round_to, k_min;  // tile k rule
+  int32_t half;                  // 1: fp16 q, k, v and out; 0: bf16
   HeadMap hm;
 };
 

@@ -1,4 +1,4 @@
-// Prefill kernels (bf16, head_dim 128, 128-query tiles) on gfx950 MFMA.
+// Prefill kernels (bf16 or fp16, head_dim 128, 128-query tiles) on gfx950 MFMA.
 //
 // Method: in prefill an anchor layer runs causal dense attention, pools the
 // post-softmax probabilities of each 128-query tile over the tile's rows and
@@ -14,7 +14,7 @@
 //   k_prefill_pool<G>      recomputes S = Q K^T per (tile, KV head) and sums
 //                          2^(S*c - lse2) over the G heads x 128 rows
 //
-// MFMA mapping (v_mfma_f32_32x32x16_bf16, wave64).  Operand A is 32x16 with
+// MFMA mapping (v_mfma_f32_32x32x16_bf16, or _f16 for fp16 inputs; wave64).  Operand A is 32x16 with
 // lane l holding row l%32, k = 8*(l/32)..+7; operand B is 16x32 with lane l
 // holding column l%32, the same k; the 32x32 fp32 result gives lane l column
 // l%32 and rows 8i + 4*(l/32) + j in register 4i+j.
@@ -42,16 +42,14 @@ constexpr int kVStride = kD + 32;      // bf16 per V row in LDS (320 B: conflict
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-KC_INLINE bf16x8_t as_bf16x8(const uint4& u) {
+template <bool HALF>
+KC_INLINE typename Fmt16<HALF>::v8 as_v8(const uint4& u) {
   u32x4 v = {u.x, u.y, u.z, u.w};
-  return __builtin_bit_cast(bf16x8_t, v);
+  return __builtin_bit_cast(typename Fmt16<HALF>::v8, v);
 }
 KC_INLINE uint4 lds16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 KC_INLINE void sts16(uint16_t* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
-KC_INLINE f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 // Register staging of one block of 64 key rows between their global loads
 // and their LDS store, so the loads of a later block are in flight while the
@@ -103,7 +101,8 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 // addresses keys kc + 4h + (j>>2) (and +8) at d = d0 + 16*g16 + 4*(j&3), so
 // it receives d = d0 + l%32 for keys kc + 4h + {0..3, 8..11}: the order of
 // the B operand P^T taken from the S^T accumulator layout.
-KC_INLINE bf16x8_t v_frag(const uint16_t* sv, int kc, int d0, int lane) {
+template <bool HALF>
+KC_INLINE typename Fmt16<HALF>::v8 v_frag(const uint16_t* sv, int kc, int d0, int lane) {
   const int h = lane >> 5, g16 = (lane >> 4) & 1, j = lane & 15;
   const uint16_t* p0 = sv + (kc + 4 * h + (j >> 2)) * kVStride + d0 + 16 * g16 + 4 * (j & 3);
   typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
@@ -111,7 +110,7 @@ KC_INLINE bf16x8_t v_frag(const uint16_t* sv, int kc, int d0, int lane) {
   const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 8 * kVStride));
   typedef short i16x8_t __attribute__((ext_vector_type(8)));
   const i16x8_t v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return __builtin_bit_cast(bf16x8_t, v);
+  return __builtin_bit_cast(typename Fmt16<HALF>::v8, v);
 }
 
 // XCD-aware work order.  Workgroups are dispatched round-robin over the 8
@@ -140,15 +139,17 @@ inline int xcd_grid(int total) { return (total + kXcds - 1) / kXcds * kXcds; }
 // S^T = K_block Q^T for the wave's 32 queries: two 32-key tiles.
 // The two key tiles are independent accumulation chains; alternating them
 // keeps a dependent MFMA one issue away from its predecessor.
-KC_INLINE void qk_block(const uint16_t* sk, const bf16x8_t* qf, int l32, int hf, f32x16_t* s) {
+template <bool HALF>
+KC_INLINE void qk_block(const uint16_t* sk, const typename Fmt16<HALF>::v8* qf, int l32, int hf,
+                        f32x16_t* s) {
   s[0] = f32x16_t{};
   s[1] = f32x16_t{};
 #pragma unroll
   for (int ds = 0; ds < 8; ++ds) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const bf16x8_t kf = as_bf16x8(lds16(sk + (kt * 32 + l32) * kKStride + ds * 16 + hf * 8));
-      s[kt] = mfma32(kf, qf[ds], s[kt]);
+      const auto kf = as_v8<HALF>(lds16(sk + (kt * 32 + l32) * kKStride + ds * 16 + hf * 8));
+      s[kt] = Fmt16<HALF>::mfma(kf, qf[ds], s[kt]);
     }
   }
 }
@@ -162,8 +163,10 @@ KC_INLINE void qk_block(const uint16_t* sk, const bf16x8_t* qf, int l32, int hf,
 // K is double-buffered in LDS (K_{j+1} is written one block ahead), V is
 // single-buffered (V_j is written at the start of step j); global loads of
 // K_{j+2} and V_{j+1} are in flight during step j.
-template <bool GATHER, int WAVES>
+template <bool GATHER, int WAVES, bool HALF>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const PrefillArgs a) {
+  typedef Fmt16<HALF> F;   // bf16 or fp16 elements
+  typedef typename F::v8 v8;
   constexpr int NT = 64 * WAVES;
   __shared__ __align__(16) uint16_t sk[2][kKB * kKStride];
   __shared__ __align__(16) uint16_t sv[kKB * kVStride];
@@ -201,14 +204,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const Pr
   const float c = a.scale_log2;
 
   // queries as the B operand: lane holds row r, d = 16*ds + 8*hf + 0..7
-  bf16x8_t qf[8];
+  v8 qf[8];
   {
     const char* qp = reinterpret_cast<const char*>(a.q) +
                      ((int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)min(r, N - 1) * a.q_sn) * 2;
 #pragma unroll
     for (int ds = 0; ds < 8; ++ds) {
       const uint4 u = ld16(qp + (ds * 16 + hf * 8) * 2);
-      qf[ds] = as_bf16x8(r < N ? u : make_uint4(0, 0, 0, 0));
+      qf[ds] = as_v8<HALF>(r < N ? u : make_uint4(0, 0, 0, 0));
     }
   }
   int nkeys = kend;
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const Pr
   if (nb > 1) load_blk(kr, 1);
   __syncthreads();
   f32x16_t sA[2], sB[2];
-  qk_block(sk[0], qf, l32, hf, sA);
+  qk_block<HALF>(sk[0], qf, l32, hf, sA);
 
   // One pipeline step on block j: s_cur holds S_j; S_{j+1} goes to s_next.
   auto step = [&](int j, f32x16_t* s_cur, f32x16_t* s_next) {
@@ -311,8 +314,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const Pr
     // softmax of S_j, and O^T += V_j^T P_j^T, so the scheduler can interleave
     // VALU work with the matrix pipe.  Row sums stay fp32 on the unrounded P
     // (the log-sum-exp feeds the pooling pass).
-    qk_block(sk[(j + 1) & 1], qf, l32, hf, s_next);
-    bf16x8_t pb[4];
+    qk_block<HALF>(sk[(j + 1) & 1], qf, l32, hf, s_next);
+    v8 pb[4];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int kt = q4 >> 1, c2 = q4 & 1;
@@ -321,16 +324,17 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const Pr
       for (int e = 0; e < 8; ++e) p[e] = exp2f_fast(fmaf(s_cur[kt][8 * c2 + e], c, -mn));
       l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       uint4 pk;
-      pk.x = pack_bf16x2(p[0], p[1]);
-      pk.y = pack_bf16x2(p[2], p[3]);
-      pk.z = pack_bf16x2(p[4], p[5]);
-      pk.w = pack_bf16x2(p[6], p[7]);
-      pb[q4] = as_bf16x8(pk);
+      pk.x = F::pack(p[0], p[1]);
+      pk.y = F::pack(p[2], p[3]);
+      pk.z = F::pack(p[4], p[5]);
+      pk.w = F::pack(p[6], p[7]);
+      pb[q4] = as_v8<HALF>(pk);
     }
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] = mfma32(v_frag(sv, ch * 16, db * 32, lane), pb[ch], o[db]);
+      for (int db = 0; db < 4; ++db)
+        o[db] = F::mfma(v_frag<HALF>(sv, ch * 16, db * 32, lane), pb[ch], o[db]);
     }
   };
   for (int j = 0; j < nb; j += 2) {
@@ -348,8 +352,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const Pr
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint2 w;
-        w.x = pack_bf16x2(o[db][4 * i + 0] * inv, o[db][4 * i + 1] * inv);
-        w.y = pack_bf16x2(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
+        w.x = F::pack(o[db][4 * i + 0] * inv, o[db][4 * i + 1] * inv);
+        w.y = F::pack(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
         *reinterpret_cast<uint2*>(op + db * 32 + 8 * i + 4 * hf) = w;
       }
     }
@@ -365,8 +369,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const Pr
 // One workgroup = one (query tile, KV head, batch): 4*WH waves; wave w takes
 // the 32-row slice w%4 of the tile for heads (w/4) + WH*i of the group, one
 // head at a time (i outer), so a wave holds one head's queries.
-template <int G>
+template <int G, bool HALF>
 __global__ __launch_bounds__(256 * (G < 4 ? G : 4)) void k_prefill_pool(const PrefillArgs a) {
+  typedef Fmt16<HALF> F;   // bf16 or fp16 elements
   constexpr int WH = G < 4 ? G : 4;          // head lanes of waves
   constexpr int HPW = G / WH;                // heads per wave
   constexpr int NT = 256 * WH;
@@ -389,7 +394,7 @@ __global__ __launch_bounds__(256 * (G < 4 ? G : 4)) void k_prefill_pool(const Pr
   float* prow = a.pooled + (int64_t)b * a.packed_per_batch + packed_row_offset(t, g, a.Hkv, kTileQ, N);
 
   for (int hi = 0; hi < HPW; ++hi) {
-    bf16x8_t qf[8];
+    typename F::v8 qf[8];
     float lse[16];
     {
       const int h = g * G + hw + WH * hi;
@@ -400,7 +405,7 @@ __global__ __launch_bounds__(256 * (G < 4 ? G : 4)) void k_prefill_pool(const Pr
       for (int ds = 0; ds < 8; ++ds) {
         uint4 u = make_uint4(0, 0, 0, 0);
         if (r < N) u = ld16(qp + (ds * 16 + hf * 8) * 2);
-        qf[ds] = as_bf16x8(u);
+        qf[ds] = as_v8<HALF>(u);
       }
       const float* lp = a.lse2 + ((int64_t)b * a.Hq + h) * N;
 #pragma unroll
@@ -422,8 +427,8 @@ __global__ __launch_bounds__(256 * (G < 4 ? G : 4)) void k_prefill_pool(const Pr
       for (int ds = 0; ds < 8; ++ds) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          const bf16x8_t kf = as_bf16x8(lds16(sk + (kt * 32 + l32) * kKStride + ds * 16 + hf * 8));
-          acc[kt] = mfma32(qf[ds], kf, acc[kt]);
+          const auto kf = as_v8<HALF>(lds16(sk + (kt * 32 + l32) * kKStride + ds * 16 + hf * 8));
+          acc[kt] = F::mfma(qf[ds], kf, acc[kt]);
         }
       }
 #pragma unroll
@@ -455,12 +460,52 @@ __global__ __launch_bounds__(256 * (G < 4 ? G : 4)) void k_prefill_pool(const Pr
   }
 }
 
+template <bool HALF>
+hipError_t flash_h(const PrefillArgs& a, hipStream_t s) {
+  const int Tp = (a.T + 1) / 2;
+  hipLaunchKernelGGL((k_prefill_attn<false, 8, HALF>), dim3(xcd_grid(Tp * a.Hq * a.B)), dim3(512), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
+template <bool HALF>
+hipError_t sparse_h(const PrefillArgs& a, hipStream_t s) {
+  const size_t lds = (size_t)a.k_max * sizeof(int32_t);
+  if ((a.Hq / a.Hkv) % 2 == 0)
+    hipLaunchKernelGGL((k_prefill_attn<true, 8, HALF>), dim3(xcd_grid(a.T * (a.Hq / 2) * a.B)),
+                       dim3(512), lds, s, a);
+  else
+    hipLaunchKernelGGL((k_prefill_attn<true, 4, HALF>), dim3(xcd_grid(a.T * a.Hq * a.B)), dim3(256),
+                       lds, s, a);
+  return hipGetLastError();
+}
+
+template <bool HALF>
+hipError_t pool_h(const PrefillArgs& a, hipStream_t s) {
+  dim3 grid(xcd_grid(a.T * a.Hkv * a.B));
+  switch (a.Hq / a.Hkv) {
+    case 1: hipLaunchKernelGGL((k_prefill_pool<1, HALF>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_prefill_pool<2, HALF>), grid, dim3(512), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_prefill_pool<4, HALF>), grid, dim3(1024), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_prefill_pool<8, HALF>), grid, dim3(1024), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <bool HALF>
+hipError_t set_lds_h(int bytes) {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill_attn<true, 8, HALF>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill_attn<true, 4, HALF>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
 }  // namespace
 
 hipError_t launch_prefill_flash(const PrefillArgs& a, hipStream_t s) {
-  const int Tp = (a.T + 1) / 2;
-  hipLaunchKernelGGL((k_prefill_attn<false, 8>), dim3(xcd_grid(Tp * a.Hq * a.B)), dim3(512), 0, s, a);
-  return hipGetLastError();
+  return a.half ? flash_h<true>(a, s) : flash_h<false>(a, s);
 }
 
 // The reuse prefill keeps the tile's key list in dynamic LDS (k_max int32).
@@ -468,34 +513,16 @@ size_t prefill_sparse_max_list() { return 24576; }
 
 hipError_t prefill_set_max_lds() {
   const int bytes = (int)(prefill_sparse_max_list() * sizeof(int32_t));
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill_attn<true, 8>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill_attn<true, 4>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  hipError_t e = set_lds_h<false>(bytes);
+  return e != hipSuccess ? e : set_lds_h<true>(bytes);
 }
 
 hipError_t launch_prefill_sparse(const PrefillArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)a.k_max * sizeof(int32_t);
-  if ((a.Hq / a.Hkv) % 2 == 0)
-    hipLaunchKernelGGL((k_prefill_attn<true, 8>), dim3(xcd_grid(a.T * (a.Hq / 2) * a.B)), dim3(512),
-                       lds, s, a);
-  else
-    hipLaunchKernelGGL((k_prefill_attn<true, 4>), dim3(xcd_grid(a.T * a.Hq * a.B)), dim3(256), lds,
-                       s, a);
-  return hipGetLastError();
+  return a.half ? sparse_h<true>(a, s) : sparse_h<false>(a, s);
 }
 
 hipError_t launch_prefill_pool(const PrefillArgs& a, hipStream_t s) {
-  dim3 grid(xcd_grid(a.T * a.Hkv * a.B));
-  switch (a.Hq / a.Hkv) {
-    case 1: hipLaunchKernelGGL(k_prefill_pool<1>, grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(k_prefill_pool<2>, grid, dim3(512), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(k_prefill_pool<4>, grid, dim3(1024), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(k_prefill_pool<8>, grid, dim3(1024), 0, s, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return a.half ? pool_h<true>(a, s) : pool_h<false>(a, s);
 }
 
 }  // namespace kc

@@ -19,7 +19,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkascade.so")
 
-KASCADE_F32, KASCADE_BF16 = 0, 1
+KASCADE_F32, KASCADE_BF16, KASCADE_F16 = 0, 1, 2
 OP_ANCHOR_DECODE, OP_REUSE_DECODE, OP_ANCHOR_PREFILL, OP_REUSE_PREFILL = 0, 1, 2, 3
 OP_DENSE_DECODE, OP_DENSE_PREFILL = 4, 5
 K_DECODE_SPLITK, K_DECODE_COMBINE, K_DECODE_POOL, K_TOPK_SELECT = 0, 1, 2, 3
@@ -293,6 +293,8 @@ def _dtype_code(t: torch.Tensor) -> int:
         return KASCADE_F32
     if t.dtype == torch.bfloat16:
         return KASCADE_BF16
+    if t.dtype == torch.float16:
+        return KASCADE_F16
     raise TypeError("unsupported dtype %s" % t.dtype)
 
 

@@ -7,7 +7,7 @@ gets them copied to host memory and upcast exactly to float64).
 Workload shape (stand-in for the pages' long-context model workloads, which
 need weights and datasets that are not available):
   * Q, K, V entries are N(0, 1), drawn in fp32 and rounded to the working
-    dtype (bf16 rounding is round-to-nearest-even, done by torch).
+    dtype (bf16 and fp16 rounding is round-to-nearest-even, done by torch).
   * About 10% of key positions per KV head are "heavy": their keys get a
     planted component alpha * u along a direction u that the queries share,
     so that they carry most of the softmax mass (the pages report that about
@@ -25,7 +25,7 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 import torch
 
-_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def torch_dtype(name: str) -> torch.dtype:
