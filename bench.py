@@ -19,6 +19,7 @@ HIP events on its launch stream inside the timed steps.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -33,14 +34,16 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode attn µs/layer + HBM GB/s at 32k/128k ctx; prefill attn TFLOP/s"
 HBM_PEAK_GBS = 8000.0
-BF16_PEAK_TFLOPS = 2500.0
+MFMA16_PEAK_TFLOPS = 2500.0  # dense bf16 and fp16 MFMA peak
 # HBM traffic of the kernels, read by rocprofv3 counters and stored as text
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_kernels_llama8b.md")
 CSRC = os.path.join(ROOT, "long_context_anchor_amd", "csrc")
 KERNEL_SOURCES = {"prefill_flash": "prefill.hip", "prefill_pool": "prefill.hip",
                   "prefill_sparse": "prefill.hip", "decode_splitk": "decode.hip",
                   "decode_combine": "decode.hip", "decode_pool": "decode.hip",
-                  "reuse_decode": "decode.hip", "topk_select": "select.hip"}
+                  "reuse_decode": "decode.hip", "topk_select": "select.hip",
+                  "topk_select_wide_a": "select.hip", "topk_select_wide_b": "select.hip",
+                  "topk_select_wide_c": "select.hip"}
 COPY_BYTES = 1 << 30  # the calibration copy reads and writes this many bytes
 
 
@@ -52,8 +55,8 @@ def log(*a):
 # workload construction (synthetic, seeded)
 # ---------------------------------------------------------------------------
 
-def build_decode(cfg_id, torch, K, synth, configs):
-    cfg = configs.CONFIGS[cfg_id]
+def build_decode(cfg_id, torch, K, synth, configs, dtype="bf16"):
+    cfg = dataclasses.replace(configs.CONFIGS[cfg_id], dtype=dtype)
     N, L = cfg.ctx_len, cfg.n_layers
     lin = synth.heavy_lineages(cfg.seed, L, cfg.n_kv_heads, N, cfg.heavy, cfg.drift)
     maps = synth.head_maps(cfg.seed, L, cfg.anchors, cfg.n_kv_heads, cfg.head_map_kind)
@@ -100,8 +103,8 @@ def build_decode(cfg_id, torch, K, synth, configs):
                 bytes_reuse=bytes_reuse, bytes_dense=bytes_dense, layers=layers, maps=maps)
 
 
-def build_prefill(torch, K, synth, configs):
-    cfg = configs.CONFIGS[4]
+def build_prefill(torch, K, synth, configs, dtype="bf16"):
+    cfg = dataclasses.replace(configs.CONFIGS[4], dtype=dtype)
     N, L = cfg.ctx_len, cfg.n_layers
     lin = synth.heavy_lineages(cfg.seed, L, cfg.n_kv_heads, N, cfg.heavy, cfg.drift)
     maps = synth.head_maps(cfg.seed, L, cfg.anchors, cfg.n_kv_heads, cfg.head_map_kind)
@@ -457,6 +460,8 @@ def main():
                     help="one launch of each kernel plus a calibration copy, for rocprofv3 --pmc")
     ap.add_argument("--calibration", action="store_true",
                     help="time the offline calibration path (layer-pair similarities, DP, head maps)")
+    ap.add_argument("--dtype", choices=["bf16", "f16"], default="bf16",
+                    help="element type of q, k, v and outputs (the workloads are defined in bf16)")
     ap.add_argument("--paged", action="store_true",
                     help="time decode over paged KV caches against contiguous caches")
     args = ap.parse_args()
@@ -489,11 +494,11 @@ def main():
     t_build = time.perf_counter()
     work = {}
     if "decode32k" in sections or not args.no_cpu_baseline:
-        work["decode32k"] = build_decode(2, torch, K, synth, configs)
+        work["decode32k"] = build_decode(2, torch, K, synth, configs, args.dtype)
     if "decode128k" in sections:
-        work["decode128k"] = build_decode(3, torch, K, synth, configs)
+        work["decode128k"] = build_decode(3, torch, K, synth, configs, args.dtype)
     if "prefill" in sections:
-        work["prefill"] = build_prefill(torch, K, synth, configs)
+        work["prefill"] = build_prefill(torch, K, synth, configs, args.dtype)
     torch.cuda.synchronize()
     log("built in %.1f s" % (time.perf_counter() - t_build))
 
@@ -583,9 +588,9 @@ def main():
             "anchor_ms": per["anchor"], "reuse_ms": per["reuse"],
             "anchor_TFLOPs": (w["flops_flash"] + w["flops_pool"]) / (per["anchor"] * 1e-3) / 1e12,
             "reuse_TFLOPs": rf / w["n_reuse"] / (per["reuse"] * 1e-3) / 1e12,
-            "mfma_frac": fl / (sec_ms["prefill"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "mfma_frac": fl / (sec_ms["prefill"] * 1e-3) / 1e12 / MFMA16_PEAK_TFLOPS,
             "anchor_mfma_frac": (w["flops_flash"] + w["flops_pool"]) / (per["anchor"] * 1e-3) / 1e12
-            / BF16_PEAK_TFLOPS,
+            / MFMA16_PEAK_TFLOPS,
             "dense_ms_per_layer": per["dense"],
             "dense_TFLOPs": w["flops_flash"] / (per["dense"] * 1e-3) / 1e12,
             "speedup_vs_dense": per["dense"] * w["cfg"].n_layers / sec_ms["prefill"],
@@ -605,8 +610,8 @@ def main():
         else:
             per_launch = w["reuse_flops"]() / w["n_reuse"]
         ach = per_launch / (avg_ms * 1e-3) / 1e12
-        roof.update({"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": ach / BF16_PEAK_TFLOPS, "algorithmic_per_launch": per_launch,
+        roof.update({"bound": "mfma", "achieved": ach, "peak": MFMA16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ach / MFMA16_PEAK_TFLOPS, "algorithmic_per_launch": per_launch,
                      "traffic": stored_traffic(names[dom], "prefill32k")})
     else:
         # decode kernels: algorithmic bytes of the launch (cache K+V or gathered rows)
@@ -623,7 +628,7 @@ def main():
     line = {
         "metric": METRIC, "value": value, "unit": "us/layer", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": False,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
         "config": {"workload": "Llama-3.1-8B-shaped attention, 32 layers, 32q/8kv heads, d=128, "
                                "anchors [0,2,8,13,14]: decode 32K ctx B=1 k=3264 + decode 128K ctx "
                                "B=4 k=13120 + prefill 32K tokens (tile 128, k_t min 256)",
