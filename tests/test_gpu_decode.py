@@ -271,3 +271,29 @@ def test_decode_deterministic_and_workspace_poison_proof():
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1, l2) and torch.equal(i1, i2) and torch.equal(p1, p2)
+
+
+def test_reuse_and_dense_decode_repeat_with_poisoned_workspace():
+    """Reuse and dense decode at the 32K shape: repeated calls, and calls
+    after the workspace was filled with garbage, give bit-identical outputs
+    (no state carries over in the workspace)."""
+    g = torch.Generator(device=DEV).manual_seed(21)
+    q = torch.randn((1, 32, 128), generator=g, device=DEV).bfloat16()
+    k = torch.randn((1, 8, 32768, 128), generator=g, device=DEV).bfloat16()
+    v = torch.randn((1, 8, 32768, 128), generator=g, device=DEV).bfloat16()
+    idx = synth.random_index_lists(3, 1, 8, 32768, 3264, device=DEV)
+    hm = [3, 1, 0, 2, 7, 6, 5, 4]
+    sh = K.make_shape(q, k, 32768)
+    ws = K.workspace(K.OP_DENSE_DECODE, sh)
+    outs = []
+    for fill in (None, float("nan"), None, 1.0e30):
+        if fill is not None:
+            ws.view(torch.float32)[: ws.numel() // 4].fill_(fill)
+        outs.append((K.reuse_decode(q, k, v, idx, hm, ws=ws).clone(), K.dense_decode(q, k, v, ws=ws)))
+    torch.cuda.synchronize()
+    for o, (d, l) in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(d.view(torch.int16), outs[0][1][0].view(torch.int16))
+        assert torch.equal(l, outs[0][1][1])
+    ref, _ = oracle.sparse_decode(np64(q), np64(k), np64(v), idx.cpu().numpy(), hm)
+    assert np.max(np.abs(np64(outs[0][0]) - ref)) <= 2e-2
