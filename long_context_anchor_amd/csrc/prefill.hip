@@ -168,8 +168,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const Pr
   typedef Fmt16<HALF> F;   // bf16 or fp16 elements
   typedef typename F::v8 v8;
   constexpr int NT = 64 * WAVES;
+  // dense: K and V double-buffered (one barrier per block); gather: V
+  // single-buffered, which leaves LDS for the staged key list
+  constexpr int NVB = GATHER ? 1 : 2;
   __shared__ __align__(16) uint16_t sk[2][kKB * kKStride];
-  __shared__ __align__(16) uint16_t sv[kKB * kVStride];
+  __shared__ __align__(16) uint16_t sv[NVB][kKB * kVStride];
   extern __shared__ int32_t slist[];
   const int G = a.Hq / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -248,23 +251,50 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const Pr
   for (int i = 0; i < 4; ++i) o[i] = f32x16_t{};
   float m = kNegInf, l = 0.f;
 
-  load_blk(kr, 0);
-  load_vblk(vr, 0);
-  kr.store(sk[0]);
-  if (nb > 1) load_blk(kr, 1);
-  __syncthreads();
   f32x16_t sA[2], sB[2];
-  qk_block<HALF>(sk[0], qf, l32, hf, sA);
+  if constexpr (GATHER) {
+    load_blk(kr, 0);
+    load_vblk(vr, 0);
+    kr.store(sk[0]);
+    if (nb > 1) load_blk(kr, 1);
+    __syncthreads();
+    qk_block<HALF>(sk[0], qf, l32, hf, sA);
+  } else {
+    // K_0, V_0 and K_1 in LDS; K_2 and V_1 in flight into the stagers
+    load_blk(kr, 0);
+    load_vblk(vr, 0);
+    kr.store(sk[0]);
+    vr.store(sv[0]);
+    if (nb > 1) {
+      load_blk(kr, 1);
+      kr.store(sk[1]);
+    }
+    __syncthreads();
+    qk_block<HALF>(sk[0], qf, l32, hf, sA);
+    if (nb > 2) load_blk(kr, 2);
+    if (nb > 1) load_vblk(vr, 1);
+    __syncthreads();   // sk[0] is rewritten in step 0
+  }
 
   // One pipeline step on block j: s_cur holds S_j; S_{j+1} goes to s_next.
   auto step = [&](int j, f32x16_t* s_cur, f32x16_t* s_next) {
     const int kb = j * kKB;
-    __syncthreads();   // every wave is done with V_{j-1} and K_j's LDS reads
-    if (j + 1 < nb) kr.store(sk[(j + 1) & 1]);
-    vr.store(sv);
-    __syncthreads();
-    if (j + 2 < nb) load_blk(kr, j + 2);
-    if (j + 1 < nb) load_vblk(vr, j + 1);
+    if constexpr (GATHER) {
+      __syncthreads();   // every wave is done with V_{j-1} and K_j's LDS reads
+      if (j + 1 < nb) kr.store(sk[(j + 1) & 1]);
+      vr.store(sv[0]);
+      __syncthreads();
+      if (j + 2 < nb) load_blk(kr, j + 2);
+      if (j + 1 < nb) load_vblk(vr, j + 1);
+    } else {
+      // Step j reads K_{j+1} and V_j, stored in step j-1; it stores K_{j+2}
+      // over K_j and V_{j+1} over V_{j-1}, whose last readers finished
+      // before the barrier that ended step j-1.
+      if (j + 2 < nb) kr.store(sk[j & 1]);
+      if (j + 1 < nb) vr.store(sv[(j + 1) & 1]);
+      if (j + 3 < nb) load_blk(kr, j + 3);
+      if (j + 2 < nb) load_vblk(vr, j + 2);
+    }
 
     // causal mask inside the block (key position > query row) and empty slots
     // (a scalar, wave-uniform decision; the masked path is branch-free)
@@ -334,8 +364,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const Pr
     for (int ch = 0; ch < 4; ++ch) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        o[db] = F::mfma(v_frag<HALF>(sv, ch * 16, db * 32, lane), pb[ch], o[db]);
+        o[db] = F::mfma(v_frag<HALF>(sv[GATHER ? 0 : (j & 1)], ch * 16, db * 32, lane), pb[ch], o[db]);
     }
+    if constexpr (!GATHER) __syncthreads();
   };
   for (int j = 0; j < nb; j += 2) {
     step(j, sA, sB);
