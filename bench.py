@@ -55,8 +55,8 @@ def log(*a):
 # workload construction (synthetic, seeded)
 # ---------------------------------------------------------------------------
 
-def build_decode(cfg_id, torch, K, synth, configs, dtype="bf16"):
-    cfg = dataclasses.replace(configs.CONFIGS[cfg_id], dtype=dtype)
+def build_decode(workload, torch, K, synth, configs, dtype="bf16"):
+    cfg = dataclasses.replace(workload, dtype=dtype)
     N, L = cfg.ctx_len, cfg.n_layers
     lin = synth.heavy_lineages(cfg.seed, L, cfg.n_kv_heads, N, cfg.heavy, cfg.drift)
     maps = synth.head_maps(cfg.seed, L, cfg.anchors, cfg.n_kv_heads, cfg.head_map_kind)
@@ -104,7 +104,7 @@ def build_decode(cfg_id, torch, K, synth, configs, dtype="bf16"):
 
 
 def build_prefill(torch, K, synth, configs, dtype="bf16"):
-    cfg = dataclasses.replace(configs.CONFIGS[4], dtype=dtype)
+    cfg = dataclasses.replace(configs.LLAMA_PREFILL_32K, dtype=dtype)
     N, L = cfg.ctx_len, cfg.n_layers
     lin = synth.heavy_lineages(cfg.seed, L, cfg.n_kv_heads, N, cfg.heavy, cfg.drift)
     maps = synth.head_maps(cfg.seed, L, cfg.anchors, cfg.n_kv_heads, cfg.head_map_kind)
@@ -252,7 +252,7 @@ def traffic_probe(torch, K, synth, configs):
     torch.cuda.synchronize()
     log("copy done")
     # prefill: one anchor layer and one reuse layer of the 32K prompt
-    cfg = configs.CONFIGS[4]
+    cfg = configs.LLAMA_PREFILL_32K
     N = cfg.ctx_len
     lin = synth.heavy_lineages(cfg.seed, cfg.n_layers, cfg.n_kv_heads, N, cfg.heavy, cfg.drift)
     maps = synth.head_maps(cfg.seed, cfg.n_layers, cfg.anchors, cfg.n_kv_heads, cfg.head_map_kind)
@@ -273,7 +273,7 @@ def traffic_probe(torch, K, synth, configs):
     del lay, out, ws, idx
     log("prefill done")
     # decode: one anchor and one reuse layer at 128K context, batch 4
-    cfg = configs.CONFIGS[3]
+    cfg = configs.LLAMA_DECODE_128K
     N = cfg.ctx_len
     lin = synth.heavy_lineages(cfg.seed, cfg.n_layers, cfg.n_kv_heads, N, cfg.heavy, cfg.drift)
     maps = synth.head_maps(cfg.seed, cfg.n_layers, cfg.anchors, cfg.n_kv_heads, cfg.head_map_kind)
@@ -302,7 +302,7 @@ def calibration_bench(torch, K, synth, configs, args):
     weighted similarity, the anchor DP and the head maps.  Prints one JSON
     line; the oracle's similarity of one layer pair is timed beside it."""
     import oracle
-    cfg = configs.CONFIGS[2]
+    cfg = configs.LLAMA_DECODE_32K
     L, Hkv, N, k, S = cfg.n_layers, cfg.n_kv_heads, cfg.ctx_len, cfg.topk, 4
     lin = synth.heavy_lineages(cfg.seed, L, Hkv, N, cfg.heavy, cfg.drift)
     maps = synth.head_maps(cfg.seed, L, cfg.anchors, Hkv, cfg.head_map_kind)
@@ -377,14 +377,13 @@ def paged_bench(torch, K, synth, configs, args):
     (B=1) and 128K (B=4) Llama-shaped workloads with 8 distinct layers each.
     Prints one JSON line."""
     res = {}
-    for cid, name in ((2, "decode32k"), (3, "decode128k")):
-        cfg = configs.CONFIGS[cid]
+    for cfg, name in ((configs.LLAMA_DECODE_32K, "decode32k"), (configs.LLAMA_DECODE_128K, "decode128k")):
         N, B, Hkv, k = cfg.ctx_len, cfg.batch, cfg.n_kv_heads, cfg.topk
         bs, nl = 16, 8
         lin = synth.heavy_lineages(cfg.seed, nl, Hkv, N, cfg.heavy, cfg.drift)
         maps = synth.head_maps(cfg.seed, nl, (0,), Hkv, cfg.head_map_kind)
         nb = N // bs
-        rng = np.random.default_rng(cid)
+        rng = np.random.default_rng(cfg.seed)
         layers = []
         for l in range(nl):
             q, kk, v = synth.decode_layer(cfg.seed, l, B, cfg.n_q_heads, Hkv, cfg.head_dim, N,
@@ -466,7 +465,7 @@ def main():
                     help="time decode over paged KV caches against contiguous caches")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
@@ -494,9 +493,9 @@ def main():
     t_build = time.perf_counter()
     work = {}
     if "decode32k" in sections or not args.no_cpu_baseline:
-        work["decode32k"] = build_decode(2, torch, K, synth, configs, args.dtype)
+        work["decode32k"] = build_decode(configs.LLAMA_DECODE_32K, torch, K, synth, configs, args.dtype)
     if "decode128k" in sections:
-        work["decode128k"] = build_decode(3, torch, K, synth, configs, args.dtype)
+        work["decode128k"] = build_decode(configs.LLAMA_DECODE_128K, torch, K, synth, configs, args.dtype)
     if "prefill" in sections:
         work["prefill"] = build_prefill(torch, K, synth, configs, args.dtype)
     torch.cuda.synchronize()

@@ -45,15 +45,18 @@ class Workload:
         return self.n_heavy or int(round(self.heavy_frac * self.ctx_len))
 
 
-CONFIGS = {
-    1: Workload("tiny-decode-f32", "decode", "f32", 2, 1, 4, 2, 64, 1024, (0,), topk=128,
-                head_map_kind="identity", n_heavy=64, drift=0.10, alpha=3.0, seed=1, tol=1e-4),
-    2: Workload("llama8b-decode-32k", "decode", "bf16", 32, 1, 32, 8, 128, 32768,
-                LLAMA_ANCHORS, topk=3264, alpha=10.7, seed=2),
-    3: Workload("llama8b-decode-128k", "decode", "bf16", 32, 4, 32, 8, 128, 131072,
-                LLAMA_ANCHORS, topk=13120, alpha=10.7, seed=3),
-    4: Workload("llama8b-prefill-32k", "prefill", "bf16", 32, 1, 32, 8, 128, 32768,
-                LLAMA_ANCHORS, alpha=17.5, seed=4),
-    5: Workload("qwen3-8b-e2e-64k", "e2e", "bf16", 36, 1, 32, 8, 128, 65536, (),
-                head_map_kind="learned", alpha=17.5, seed=5, decode_steps=512, n_anchor_dp=6),
-}
+TINY_DECODE = Workload("tiny-decode-f32", "decode", "f32", 2, 1, 4, 2, 64, 1024, (0,), topk=128,
+                       head_map_kind="identity", n_heavy=64, drift=0.10, alpha=3.0, seed=1,
+                       tol=1e-4)
+LLAMA_DECODE_32K = Workload("llama8b-decode-32k", "decode", "bf16", 32, 1, 32, 8, 128, 32768,
+                            LLAMA_ANCHORS, topk=3264, alpha=10.7, seed=2)
+LLAMA_DECODE_128K = Workload("llama8b-decode-128k", "decode", "bf16", 32, 4, 32, 8, 128, 131072,
+                             LLAMA_ANCHORS, topk=13120, alpha=10.7, seed=3)
+LLAMA_PREFILL_32K = Workload("llama8b-prefill-32k", "prefill", "bf16", 32, 1, 32, 8, 128, 32768,
+                             LLAMA_ANCHORS, alpha=17.5, seed=4)
+QWEN3_E2E_64K = Workload("qwen3-8b-e2e-64k", "e2e", "bf16", 36, 1, 32, 8, 128, 65536, (),
+                         head_map_kind="learned", alpha=17.5, seed=5, decode_steps=512,
+                         n_anchor_dp=6)
+
+WORKLOADS = {w.name: w for w in (TINY_DECODE, LLAMA_DECODE_32K, LLAMA_DECODE_128K,
+                                 LLAMA_PREFILL_32K, QWEN3_E2E_64K)}

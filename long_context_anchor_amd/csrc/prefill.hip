@@ -163,14 +163,14 @@ KC_INLINE void qk_block(const uint16_t* sk, const typename Fmt16<HALF>::v8* qf, 
 // K is double-buffered in LDS (K_{j+1} is written one block ahead), V is
 // single-buffered (V_j is written at the start of step j); global loads of
 // K_{j+2} and V_{j+1} are in flight during step j.
-template <bool GATHER, int WAVES, bool HALF>
+template <bool GATHER, int WAVES, bool HALF, bool DB>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const PrefillArgs a) {
   typedef Fmt16<HALF> F;   // bf16 or fp16 elements
   typedef typename F::v8 v8;
   constexpr int NT = 64 * WAVES;
-  // dense: K and V double-buffered (one barrier per block); gather: V
-  // single-buffered, which leaves LDS for the staged key list
-  constexpr int NVB = GATHER ? 1 : 2;
+  // DB: K and V double-buffered (one barrier per block); otherwise V is
+  // single-buffered, which leaves more LDS for a long staged key list
+  constexpr int NVB = DB ? 2 : 1;
   __shared__ __align__(16) uint16_t sk[2][kKB * kKStride];
   __shared__ __align__(16) uint16_t sv[NVB][kKB * kVStride];
   extern __shared__ int32_t slist[];
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const Pr
   float m = kNegInf, l = 0.f;
 
   f32x16_t sA[2], sB[2];
-  if constexpr (GATHER) {
+  if constexpr (!DB) {
     load_blk(kr, 0);
     load_vblk(vr, 0);
     kr.store(sk[0]);
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const Pr
   // One pipeline step on block j: s_cur holds S_j; S_{j+1} goes to s_next.
   auto step = [&](int j, f32x16_t* s_cur, f32x16_t* s_next) {
     const int kb = j * kKB;
-    if constexpr (GATHER) {
+    if constexpr (!DB) {
       __syncthreads();   // every wave is done with V_{j-1} and K_j's LDS reads
       if (j + 1 < nb) kr.store(sk[(j + 1) & 1]);
       vr.store(sv[0]);
@@ -364,9 +364,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const Pr
     for (int ch = 0; ch < 4; ++ch) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        o[db] = F::mfma(v_frag<HALF>(sv[GATHER ? 0 : (j & 1)], ch * 16, db * 32, lane), pb[ch], o[db]);
+        o[db] = F::mfma(v_frag<HALF>(sv[DB ? (j & 1) : 0], ch * 16, db * 32, lane), pb[ch], o[db]);
     }
-    if constexpr (!GATHER) __syncthreads();
+    if constexpr (DB) __syncthreads();
   };
   for (int j = 0; j < nb; j += 2) {
     step(j, sA, sB);
@@ -407,8 +407,9 @@ __global__ __launch_bounds__(256 * (G < 4 ? G : 4)) void k_prefill_pool(const Pr
   constexpr int HPW = G / WH;                // heads per wave
   constexpr int NT = 256 * WH;
   constexpr int NW = NT / 64;
-  __shared__ __align__(16) uint16_t sk[kKB * kKStride];
-  __shared__ float red[NW][kKB];
+  // key blocks and column sums double-buffered: one barrier per block
+  __shared__ __align__(16) uint16_t sk[2][kKB * kKStride];
+  __shared__ float red[2][NW][kKB];
 
   int t, g, b;
   if (!xcd_work_item(a.T * a.Hkv * a.B, 1, a.T, a.Hkv, t, g, b)) return;
@@ -446,19 +447,37 @@ __global__ __launch_bounds__(256 * (G < 4 ? G : 4)) void k_prefill_pool(const Pr
       }
     }
     RowStager<NT> regs;
+    const int nblk = (P + kKB - 1) / kKB;
     regs.load_dense(kbase, row_bytes, P);
-    for (int kb = 0; kb < P; kb += kKB) {
-      __syncthreads();
-      regs.store(sk);
-      __syncthreads();
-      if (kb + kKB < P) regs.load_dense(kbase + (int64_t)(kb + kKB) * row_bytes, row_bytes, P - kb - kKB);
+    regs.store(sk[0]);
+    if (nblk > 1) regs.load_dense(kbase + (int64_t)kKB * row_bytes, row_bytes, P - kKB);
+    __syncthreads();
+    // column sums of the G heads x 128 rows of block jb - 1 (complete once
+    // the barrier after its step has passed) added into the pooled row
+    auto fold = [&](int jb) {
+      const int kb = jb * kKB;
+      if (tid < kKB && kb + tid < P) {
+        float sum = hi == 0 ? 0.f : prow[kb + tid];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sum += red[jb & 1][w][tid];
+        prow[kb + tid] = sum;
+      }
+    };
+    for (int jb = 0; jb < nblk; ++jb) {
+      const int kb = jb * kKB;
+      // block jb + 1 goes over block jb - 1, whose readers finished before
+      // the barrier that ended step jb - 1
+      if (jb + 1 < nblk) regs.store(sk[(jb + 1) & 1]);
+      if (jb + 2 < nblk)
+        regs.load_dense(kbase + (int64_t)(kb + 2 * kKB) * row_bytes, row_bytes, P - kb - 2 * kKB);
       const bool need_mask = (kb + kKB - 1 > row0) || (kb + kKB > P) || (row0 + 32 > N);
+      const uint16_t* skb = sk[jb & 1];
       f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
       for (int ds = 0; ds < 8; ++ds) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          const auto kf = as_v8<HALF>(lds16(sk + (kt * 32 + l32) * kKStride + ds * 16 + hf * 8));
+          const auto kf = as_v8<HALF>(lds16(skb + (kt * 32 + l32) * kKStride + ds * 16 + hf * 8));
           acc[kt] = F::mfma(qf[ds], kf, acc[kt]);
         }
       }
@@ -478,36 +497,35 @@ __global__ __launch_bounds__(256 * (G < 4 ? G : 4)) void k_prefill_pool(const Pr
           for (int ri = 0; ri < 16; ++ri) cs += exp2f_fast(fmaf(acc[kt][ri], c, -lse[ri]));
         }
         cs += __shfl_xor(cs, 32, 64);
-        if (hf == 0) red[wave][kt * 32 + l32] = cs;
+        if (hf == 0) red[jb & 1][wave][kt * 32 + l32] = cs;
       }
+      if (jb > 0) fold(jb - 1);
       __syncthreads();
-      if (tid < kKB && kb + tid < P) {
-        float sum = hi == 0 ? 0.f : prow[kb + tid];
-#pragma unroll
-        for (int w = 0; w < NW; ++w) sum += red[w][tid];
-        prow[kb + tid] = sum;
-      }
     }
+    fold(nblk - 1);
+    __syncthreads();   // red and sk are reused by the next head pass
   }
 }
 
 template <bool HALF>
 hipError_t flash_h(const PrefillArgs& a, hipStream_t s) {
   const int Tp = (a.T + 1) / 2;
-  hipLaunchKernelGGL((k_prefill_attn<false, 8, HALF>), dim3(xcd_grid(Tp * a.Hq * a.B)), dim3(512), 0,
-                     s, a);
+  hipLaunchKernelGGL((k_prefill_attn<false, 8, HALF, true>), dim3(xcd_grid(Tp * a.Hq * a.B)), dim3(512),
+                     0, s, a);
   return hipGetLastError();
 }
 
 template <bool HALF>
 hipError_t sparse_h(const PrefillArgs& a, hipStream_t s) {
+  // gathered variants keep V single-buffered: double buffering measured no
+  // faster here and would take LDS from the staged list
   const size_t lds = (size_t)a.k_max * sizeof(int32_t);
   if ((a.Hq / a.Hkv) % 2 == 0)
-    hipLaunchKernelGGL((k_prefill_attn<true, 8, HALF>), dim3(xcd_grid(a.T * (a.Hq / 2) * a.B)),
+    hipLaunchKernelGGL((k_prefill_attn<true, 8, HALF, false>), dim3(xcd_grid(a.T * (a.Hq / 2) * a.B)),
                        dim3(512), lds, s, a);
   else
-    hipLaunchKernelGGL((k_prefill_attn<true, 4, HALF>), dim3(xcd_grid(a.T * a.Hq * a.B)), dim3(256),
-                       lds, s, a);
+    hipLaunchKernelGGL((k_prefill_attn<true, 4, HALF, false>), dim3(xcd_grid(a.T * a.Hq * a.B)),
+                       dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
@@ -526,10 +544,10 @@ hipError_t pool_h(const PrefillArgs& a, hipStream_t s) {
 
 template <bool HALF>
 hipError_t set_lds_h(int bytes) {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill_attn<true, 8, HALF>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill_attn<true, 8, HALF, false>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill_attn<true, 4, HALF>),
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill_attn<true, 4, HALF, false>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 

@@ -21,7 +21,7 @@ Sources.  The method is described on the web pages about the paper
   exact Top-k in anchor layers, reuse in intermediate layers, head-aware
   selection, tile-level operations in prefill and decode.
 
-Readings adopted where the pages are silent (each is listed in the design doc):
+Readings adopted where the pages are silent:
 pooling is the SUM of post-softmax probabilities over the pooled queries;
 query head h uses KV head h // G; softmax scale 1/sqrt(d); a reuse layer uses
 the nearest preceding anchor; sparse softmax is renormalised over the selected

@@ -139,7 +139,7 @@ def _check_anchor(q, k, v, topk, tol):
 
 
 def test_anchor_decode_tiny_fp32():
-    cfg = configs.CONFIGS[1]
+    cfg = configs.TINY_DECODE
     say("anchor decode tiny fp32")
     q, k, v, _ = _decode_layer(cfg, 0)
     _check_anchor(q, k, v, cfg.topk, cfg.tol)
@@ -147,7 +147,7 @@ def test_anchor_decode_tiny_fp32():
 
 @pytest.mark.parametrize("N,topk", [(1, 1), (130, 129), (1000, 128), (5000, 4999), (20000, 2048)])
 def test_anchor_decode_ragged_bf16(N, topk):
-    cfg = configs.CONFIGS[2]
+    cfg = configs.LLAMA_DECODE_32K
     say("anchor decode ragged", N, topk)
     q, k, v, _ = _decode_layer(cfg, 0, n=N, batch=2, n_kv=2)
     _check_anchor(q, k, v, topk, cfg.tol)
@@ -211,7 +211,7 @@ def test_reuse_full_list_equals_dense():
 # ---------------------------------------------------------------------------
 
 def test_llama_32k_anchor_and_reuse_layer():
-    cfg = configs.CONFIGS[2]
+    cfg = configs.LLAMA_DECODE_32K
     say("32K anchor layer 0 + reuse layer 1")
     q, k, v, maps = _decode_layer(cfg, 0)
     out, idx, ridx, ndiff = _check_anchor(q, k, v, cfg.topk, cfg.tol)
@@ -226,7 +226,7 @@ def test_llama_32k_anchor_and_reuse_layer():
 
 def test_llama_128k_sampled():
     # full-size launch (B=4, N=131072); the oracle checks batch row 3 and KV heads 0 and 5
-    cfg = configs.CONFIGS[3]
+    cfg = configs.LLAMA_DECODE_128K
     say("128K anchor + reuse, sampled rows")
     q, k, v, maps = _decode_layer(cfg, 0)
     out, lse, idx, pooled = K.anchor_decode(q, k, v, cfg.topk, want_pooled=True)
@@ -261,7 +261,7 @@ def test_llama_128k_sampled():
 # ---------------------------------------------------------------------------
 
 def test_decode_deterministic_and_workspace_poison_proof():
-    cfg = configs.CONFIGS[2]
+    cfg = configs.LLAMA_DECODE_32K
     q, k, v, _ = _decode_layer(cfg, 0, n=20000, batch=1, n_kv=8)
     sh = K.make_shape(q, k, 20000)
     ws = K.workspace(K.OP_ANCHOR_DECODE, sh, 2048)

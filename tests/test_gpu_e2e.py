@@ -26,7 +26,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
 RULE = K.PREFILL_RULE
-CFG = configs.CONFIGS[5]
+CFG = configs.QWEN3_E2E_64K
 N0 = CFG.ctx_len                       # prompt length
 N_MAX = N0 + CFG.decode_steps          # cache rows
 TILES = [0, 1, 20, 300, N0 // 128 - 1]

@@ -68,7 +68,7 @@ def test_fp16_dense_decode(B, Hq, Hkv, N):
 @pytest.mark.parametrize("N,topk", [(1, 1), (1000, 128), (20000, 2048), (70001, 7000)])
 def test_fp16_anchor_decode(N, topk):
     say("fp16 anchor decode", N, topk)
-    cfg = configs.CONFIGS[2]
+    cfg = configs.LLAMA_DECODE_32K
     lin = synth.heavy_lineages(cfg.seed, 1, 2, N, max(1, N // 10), cfg.drift)
     q, k, v = synth.decode_layer(cfg.seed, 0, 2, 8, 2, 128, N, lin[0], cfg.alpha, "f16", device=DEV)
     _check_anchor_decode(q, k, v, topk, K.anchor_decode(q, k, v, topk, want_pooled=True))
@@ -130,7 +130,7 @@ def test_fp16_dense_prefill(B, Hq, Hkv, N):
                                            (2, 4, 4, 640, [3, 0, 1, 2])])
 def test_fp16_anchor_and_reuse_prefill(B, Hq, Hkv, N, hm):
     say("fp16 anchor+reuse prefill", B, Hq, Hkv, N, hm)
-    cfg = configs.CONFIGS[4]
+    cfg = configs.LLAMA_PREFILL_32K
     lin = synth.heavy_lineages(N, 1, Hkv, N, max(1, N // 10), cfg.drift)
     q, k, v = synth.prefill_layer(N, 0, B, Hq, Hkv, 128, N, lin[0], cfg.alpha, cfg.gamma, "f16",
                                   device=DEV)

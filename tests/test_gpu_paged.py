@@ -50,7 +50,7 @@ def _paged(k, v, bs, seed, spare=3):
 @pytest.mark.parametrize("N,bs,topk", [(1000, 16, 128), (5000, 64, 500), (20001, 128, 2048)])
 def test_paged_anchor_decode(N, bs, topk):
     say("paged anchor decode", N, bs, topk)
-    cfg = configs.CONFIGS[2]
+    cfg = configs.LLAMA_DECODE_32K
     lin = synth.heavy_lineages(cfg.seed, 1, 2, N, max(1, N // 10), cfg.drift)
     q, k, v = synth.decode_layer(cfg.seed, 0, 2, 8, 2, 128, N, lin[0], cfg.alpha, "bf16", device=DEV)
     kc, vc, table = _paged(k, v, bs, seed=N)

@@ -33,7 +33,7 @@ def np64(t):
 
 def _rand_layer(B, Hq, Hkv, N, seed, planted=False):
     if planted:
-        cfg = configs.CONFIGS[4]
+        cfg = configs.LLAMA_PREFILL_32K
         lin = synth.heavy_lineages(seed, 1, Hkv, N, max(1, N // 10), cfg.drift)
         return synth.prefill_layer(seed, 0, B, Hq, Hkv, 128, N, lin[0], cfg.alpha, cfg.gamma,
                                    "bf16", device=DEV)
@@ -146,7 +146,7 @@ def test_reuse_prefill_full_lists_equal_dense():
 def test_llama_prefill_32k_sampled():
     """Full-size anchor + reuse layer pair of the 32K-token prefill workload;
     the oracle checks sampled tiles (0, 1, 20, 131, 255) of KV heads 0 and 6."""
-    cfg = configs.CONFIGS[4]
+    cfg = configs.LLAMA_PREFILL_32K
     N = cfg.ctx_len
     say("32K prefill anchor + reuse, sampled tiles")
     lin = synth.heavy_lineages(cfg.seed, 2, cfg.n_kv_heads, N, cfg.heavy, cfg.drift)

@@ -11,10 +11,9 @@ from long_context_anchor_amd import configs, synth
 
 
 def test_config_k_values_follow_the_k_rule():
-    for i in (2, 3):
-        c = configs.CONFIGS[i]
+    for c in (configs.LLAMA_DECODE_32K, configs.LLAMA_DECODE_128K):
         assert c.topk == oracle.topk_for_len(c.ctx_len)
-    assert configs.CONFIGS[1].topk == oracle.topk_for_len(1024)
+    assert configs.TINY_DECODE.topk == oracle.topk_for_len(1024)
 
 
 def test_lineage_drift_and_head_maps():
@@ -31,7 +30,7 @@ def test_lineage_drift_and_head_maps():
 
 
 def test_decode_heavy_mass_near_95_percent():
-    c = configs.CONFIGS[2]
+    c = configs.LLAMA_DECODE_32K
     n, n_kv = 4096, 2
     lin = synth.heavy_lineages(9, 1, n_kv, n, int(0.1 * n), c.drift)
     q, k, v = synth.decode_layer(9, 0, 1, c.group * n_kv, n_kv, c.head_dim, n, lin[0], c.alpha, "bf16")
@@ -41,7 +40,7 @@ def test_decode_heavy_mass_near_95_percent():
 
 
 def test_prefill_heavy_mass_near_95_percent():
-    c = configs.CONFIGS[4]
+    c = configs.LLAMA_PREFILL_32K
     n = 1024
     lin = synth.heavy_lineages(9, 1, 1, n, int(0.1 * n), c.drift)
     q, k, v = synth.prefill_layer(9, 0, 1, c.group, 1, c.head_dim, n, lin[0], c.alpha, c.gamma, "bf16")
