@@ -297,3 +297,22 @@ def test_reuse_and_dense_decode_repeat_with_poisoned_workspace():
         assert torch.equal(l, outs[0][1][1])
     ref, _ = oracle.sparse_decode(np64(q), np64(k), np64(v), idx.cpu().numpy(), hm)
     assert np.max(np.abs(np64(outs[0][0]) - ref)) <= 2e-2
+
+
+@pytest.mark.parametrize("N", [1 << 20, 2_100_000])
+def test_anchor_and_reuse_decode_million_key_context(N):
+    """Decode rows of 1M keys (the many-workgroup select, 512 chunks) and of
+    2.1M keys (past the chunked select's 1024-chunk bound: the one-workgroup
+    select streams the row), with the k rule's k, against the oracle."""
+    say("million-key decode", N)
+    g = torch.Generator(device=DEV).manual_seed(N)
+    q = torch.randn((1, 4, 128), generator=g, device=DEV).bfloat16()
+    k = torch.randn((1, 1, N, 128), generator=g, device=DEV).bfloat16()
+    v = torch.randn((1, 1, N, 128), generator=g, device=DEV).bfloat16()
+    topk = oracle.topk_for_len(N)
+    _, idx, ridx, _ = _check_anchor(q, k, v, topk, 2e-2)
+    q2 = torch.randn((1, 4, 128), generator=g, device=DEV).bfloat16()
+    out = K.reuse_decode(q2, k, v, torch.as_tensor(ridx.astype(np.int32), device=DEV), [0])
+    torch.cuda.synchronize()
+    ref, _ = oracle.sparse_decode(np64(q2), np64(k), np64(v), ridx, [0])
+    assert np.max(np.abs(np64(out) - ref)) <= 2e-2
