@@ -316,3 +316,25 @@ def test_anchor_and_reuse_decode_million_key_context(N):
     torch.cuda.synchronize()
     ref, _ = oracle.sparse_decode(np64(q2), np64(k), np64(v), ridx, [0])
     assert np.max(np.abs(np64(out) - ref)) <= 2e-2
+
+
+def test_decode_sharp_softmax_and_late_max():
+    """Sharp distributions (query scaled by 3) and a late key whose score
+    sits tens above every other one, so the running reference max moves in
+    the last split and every earlier partial is rescaled at the merge."""
+    say("decode sharp softmax, late max")
+    N = 20000
+    g = torch.Generator(device=DEV).manual_seed(99)
+    q = (3.0 * torch.randn((1, 8, 128), generator=g, device=DEV)).bfloat16()
+    k = torch.randn((1, 2, N, 128), generator=g, device=DEV)
+    v = torch.randn((1, 2, N, 128), generator=g, device=DEV).bfloat16()
+    for gg in range(2):
+        u = q[0, 4 * gg:4 * gg + 4].float().mean(0)
+        k[0, gg, N - 3] = u / u.norm() * 40.0
+    k = k.bfloat16()
+    _, idx, ridx, _ = _check_anchor(q, k, v, 2048, 2e-2)
+    assert all((N - 3) in set(ridx[0, gg].tolist()) for gg in range(2))
+    out = K.reuse_decode(q, k, v, torch.as_tensor(ridx.astype(np.int32), device=DEV), [1, 0])
+    torch.cuda.synchronize()
+    ref, _ = oracle.sparse_decode(np64(q), np64(k), np64(v), ridx, [1, 0])
+    assert np.max(np.abs(np64(out) - ref)) <= 2e-2

@@ -187,3 +187,21 @@ def test_prefill_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1, l2) and torch.equal(i1, i2) and torch.equal(p1, p2)
+
+
+def test_prefill_sharp_softmax_and_late_max():
+    """Sharp distributions and late maxima: every query has a component of 30
+    along one unit direction w (plus 3 x N(0,1) noise), and the last key of
+    every tile is 12 w, so those keys score about 30 above the rest and each
+    row's reference max jumps when its key sequence reaches key 127."""
+    say("prefill sharp softmax, late max")
+    B, Hq, Hkv, N = 1, 8, 2, 700
+    g = torch.Generator(device=DEV).manual_seed(98)
+    w = torch.randn((128,), generator=g, device=DEV)
+    w = w / w.norm()
+    q = 3.0 * torch.randn((B, Hq, N, 128), generator=g, device=DEV) + 30.0 * w
+    k = torch.randn((B, Hkv, N, 128), generator=g, device=DEV)
+    v = torch.randn((B, Hkv, N, 128), generator=g, device=DEV).bfloat16()
+    k[:, :, 127::128] = 12.0 * w
+    q, k = q.bfloat16(), k.bfloat16()
+    _check_anchor_prefill(q, k, v)
