@@ -338,3 +338,48 @@ def test_decode_sharp_softmax_and_late_max():
     torch.cuda.synchronize()
     ref, _ = oracle.sparse_decode(np64(q), np64(k), np64(v), ridx, [1, 0])
     assert np.max(np.abs(np64(out) - ref)) <= 2e-2
+
+
+def test_decode_on_two_streams_from_two_threads():
+    """Calls on distinct streams with distinct workspaces, issued from two
+    host threads at once, give the same bits as the same calls run one after
+    the other on the current stream."""
+    import threading
+    say("decode on two streams")
+    cfg = configs.LLAMA_DECODE_32K
+    layers = [_decode_layer(cfg, l, n=20000, batch=1, n_kv=4) for l in (0, 1)]
+    serial = []
+    for q, k, v, maps in layers:
+        out, lse, idx, pooled = K.anchor_decode(q, k, v, 2048, want_pooled=True)
+        serial.append((out, idx, pooled, K.reuse_decode(q, k, v, idx, [3, 2, 1, 0])))
+    torch.cuda.synchronize()
+    results = [None, None]
+
+    def run(i):
+        q, k, v, _ = layers[i]
+        st = torch.cuda.Stream()
+        with torch.cuda.stream(st):
+            sh = K.make_shape(q, k, 20000)
+            ws_a = K.workspace(K.OP_ANCHOR_DECODE, sh, 2048)
+            ws_r = K.workspace(K.OP_REUSE_DECODE, sh, 2048)
+            out = torch.empty_like(q)
+            idx = torch.empty((1, 4, 2048), dtype=torch.int32, device=DEV)
+            pooled = torch.empty((1, 4, 20000), dtype=torch.float32, device=DEV)
+            out2 = torch.empty_like(q)
+            for _ in range(3):
+                K.check(K.kascade_anchor_decode(sh, q, k, v, 2048, out, None, idx, pooled, ws_a,
+                                                ws_a.numel(), stream=st.cuda_stream), "anchor")
+                K.check(K.kascade_reuse_decode(sh, q, k, v, 2048, idx, [3, 2, 1, 0], out2, ws_r,
+                                               ws_r.numel(), stream=st.cuda_stream), "reuse")
+        st.synchronize()
+        results[i] = (out, idx, pooled, out2)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in (0, 1)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for (o, i, p, o2), (so, si, sp, so2) in zip(results, serial):
+        assert torch.equal(o.view(torch.int16), so.view(torch.int16))
+        assert torch.equal(i, si) and torch.equal(p, sp)
+        assert torch.equal(o2.view(torch.int16), so2.view(torch.int16))
