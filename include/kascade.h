@@ -18,9 +18,10 @@
  *             workspace (size from kascade_workspace_bytes).  The library
  *             never allocates device memory, never frees, never synchronises.
  * Streams.    Work is enqueued asynchronously on `stream` (0 = null stream).
- * Layouts.    K and V caches are [B, Hkv, N_cap, d] addressed through the
- *             element strides in kascade_shape (rows of d contiguous
- *             elements).  Queries are [B, Hq, d] (decode) or [B, Hq, N, d]
+ * Layouts.    K and V caches are addressed through the element strides in
+ *             kascade_shape (rows of d contiguous elements, 16-byte aligned;
+ *             K and V share the strides): [B, Hkv, N_cap, d] and
+ *             [B, N_cap, Hkv, d] both work.  Queries are [B, Hq, d] (decode) or [B, Hq, N, d]
  *             (prefill) through the q strides.  Outputs are CONTIGUOUS:
  *             out [B, Hq, d] / [B, Hq, N, d] in the input dtype, lse
  *             [B, Hq] / [B, Hq, N] fp32 (natural log).

@@ -188,14 +188,13 @@ int check_shape(const kascade_shape* s, bool prefill, bool paged = false) {
   if (!(s->scale >= 0.f) || isinf(s->scale)) return KASCADE_ERR_ARG;
   const int64_t es = (int64_t)elem_size(s->dtype);
   const int64_t d = s->head_dim;
-  // every row must be 16-byte aligned and rows must not overlap
+  // every row must be 16-byte aligned and hold d elements; K/V rows are only
+  // read, so any head/position interleaving works ([B,Hkv,N,d], [B,N,Hkv,d])
   if (s->kv_stride_n < d || s->q_stride_h < (prefill ? 0 : d)) return KASCADE_ERR_SHAPE;
   if ((s->kv_stride_n * es) % 16 || (s->kv_stride_h * es) % 16 || (s->kv_stride_b * es) % 16 ||
       (s->q_stride_h * es) % 16 || (s->q_stride_b * es) % 16 || (s->q_stride_n * es) % 16)
     return KASCADE_ERR_SHAPE;
   if (s->kv_stride_h < 0 || s->kv_stride_b < 0 || s->q_stride_b < 0 || s->q_stride_n < 0)
-    return KASCADE_ERR_SHAPE;
-  if (!paged && s->kv_stride_h < (int64_t)s->ctx_len * s->kv_stride_n && s->n_kv_heads > 1)
     return KASCADE_ERR_SHAPE;
   if (prefill && s->q_stride_n < d) return KASCADE_ERR_SHAPE;
   // decode kernels address a head's rows with 32-bit byte offsets

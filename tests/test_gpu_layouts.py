@@ -1,0 +1,88 @@
+"""GPU parity with non-default memory layouts, through the C ABI: K/V caches
+stored [B, N, Hkv, d] (heads interleaved per position, as many serving
+stacks keep them) with rows padded to 192 elements, and queries taken as
+strided views.  The oracle sees the same logical [B, Hkv, N, d] arrays.
+Tolerances as for the contiguous tests (outputs 2e-2 max-abs, lse 1e-4
+decode / 1e-3 prefill, indices within the oracle's 1e-5 tie band)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_anchor_amd import kascade as K
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def np64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _bshd(B, Hkv, N, gen, pad=192):
+    """A [B, Hkv, N, 128] view of a [B, N, Hkv, pad] bf16 buffer."""
+    buf = torch.randn((B, N, Hkv, pad), generator=gen, device=DEV).bfloat16()
+    view = buf[..., :128].permute(0, 2, 1, 3)
+    assert view.stride() == (N * Hkv * pad, pad, Hkv * pad, 1)
+    return view
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,topk", [(2, 8, 2, 3000, 333), (1, 32, 8, 20000, 2048)])
+def test_decode_interleaved_heads_and_padded_rows(B, Hq, Hkv, N, topk):
+    say("decode BSHD", B, Hq, Hkv, N, topk)
+    g = torch.Generator(device=DEV).manual_seed(N)
+    k, v = _bshd(B, Hkv, N, g), _bshd(B, Hkv, N, g)
+    qbuf = torch.randn((B, Hq, 160), generator=g, device=DEV).bfloat16()
+    q = qbuf[..., :128]
+    out, lse, idx, pooled = K.anchor_decode(q, k, v, topk, want_pooled=True)
+    torch.cuda.synchronize()
+    ro, rl, rpool, ridx = oracle.anchor_decode(np64(q), np64(k), np64(v), topk)
+    assert np.max(np.abs(np64(out) - ro)) <= 2e-2
+    assert np.max(np.abs(np64(lse) - rl)) <= 1e-4
+    gp, gi = np64(pooled), idx.cpu().numpy()
+    for b in range(B):
+        for gg in range(Hkv):
+            assert np.array_equal(gi[b, gg], oracle.topk_full_sort(gp[b, gg], topk))
+            ok, nd = oracle.index_sets_agree(gi[b, gg], ridx[b, gg], rpool[b, gg])
+            assert ok, (b, gg, nd)
+    hm = list(reversed(range(Hkv)))
+    out2 = K.reuse_decode(q, k, v, torch.as_tensor(ridx.astype(np.int32), device=DEV), hm)
+    torch.cuda.synchronize()
+    ref, _ = oracle.sparse_decode(np64(q), np64(k), np64(v), ridx, hm)
+    assert np.max(np.abs(np64(out2) - ref)) <= 2e-2
+
+
+def test_prefill_interleaved_heads_and_strided_queries():
+    B, Hq, Hkv, N = 1, 8, 2, 520
+    say("prefill BSHD", B, Hq, Hkv, N)
+    g = torch.Generator(device=DEV).manual_seed(5)
+    k, v = _bshd(B, Hkv, N, g), _bshd(B, Hkv, N, g)
+    # queries [B, N, Hq, 128] viewed as [B, Hq, N, 128]
+    q = torch.randn((B, N, Hq, 128), generator=g, device=DEV).bfloat16().permute(0, 2, 1, 3)
+    out, lse, idx, pooled = K.anchor_prefill(q, k, v, K.PREFILL_RULE, want_pooled=True)
+    torch.cuda.synchronize()
+    qn, kn, vn = np64(q), np64(k), np64(v)
+    ro, rl = oracle.dense_prefill(qn, kn, vn)
+    assert np.max(np.abs(np64(out) - ro)) <= 2e-2
+    assert np.max(np.abs(np64(lse) - rl)) <= 1e-3
+    T = -(-N // 128)
+    gidx, gpool = idx.cpu().numpy(), pooled.cpu().numpy()
+    for t in range(T):
+        _, kt = oracle.prefill_tile_k(t, N)
+        for gg in range(Hkv):
+            rp = oracle.tile_pool_one(qn, kn, 0, t, gg)
+            gp = K.packed_row(torch.as_tensor(gpool[0]), t, gg, N, Hkv).numpy().astype(np.float64)
+            assert np.max(np.abs(gp - rp) / np.maximum(rp, 1e-6)) <= 1e-3
+            ok, _ = oracle.index_sets_agree(gidx[0, t, gg, :kt], oracle.topk_full_sort(rp, kt), rp)
+            assert ok, (t, gg)
+    out2 = K.reuse_prefill(q, k, v, idx, [1, 0], K.PREFILL_RULE)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_prefill(qn, kn, vn, gidx, [1, 0])
+    assert np.max(np.abs(np64(out2) - ref)) <= 2e-2
