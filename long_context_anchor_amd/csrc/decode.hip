@@ -8,7 +8,7 @@
 // head_map[g] (page "論文解説: Kascade …", sections "アンカーレイヤーと再利用
 // レイヤー" and "ヘッドリマッピング").
 //
-// Layout on gfx950.  One K/V row is 256 bytes (bf16 x 128 or fp32 x 64).  A
+// Layout on gfx950.  One K/V row is 256 bytes (bf16 or fp16 x 128, fp32 x 64).  A
 // 16-lane DPP row of a wave64 covers one K/V row with 16-byte loads, so one
 // load instruction of a wave reads 4 consecutive rows (1 KiB contiguous).
 // Each lane keeps its 16-byte slice of the group's G query heads in
@@ -47,14 +47,8 @@ struct Elem<_Float16> {
   static constexpr int D = 128;
 };
 
-// Partial dot of a 16-byte slice with a query slice.
-KC_INLINE float slice_dot(const uint4& kk, const uint4& qq, float acc, uint16_t) {
-  acc = dot2_bf16(kk.x, qq.x, acc);
-  acc = dot2_bf16(kk.y, qq.y, acc);
-  acc = dot2_bf16(kk.z, qq.z, acc);
-  acc = dot2_bf16(kk.w, qq.w, acc);
-  return acc;
-}
+// Partial dot of a 16-byte fp32 slice with a query slice (the fp32 kernel;
+// 16-bit caches run the head-slot kernel below).
 KC_INLINE float slice_dot(const uint4& kk, const uint4& qq, float acc, float) {
   acc = fmaf(__uint_as_float(kk.x), __uint_as_float(qq.x), acc);
   acc = fmaf(__uint_as_float(kk.y), __uint_as_float(qq.y), acc);
@@ -62,13 +56,7 @@ KC_INLINE float slice_dot(const uint4& kk, const uint4& qq, float acc, float) {
   acc = fmaf(__uint_as_float(kk.w), __uint_as_float(qq.w), acc);
   return acc;
 }
-// Unpack a 16-byte slice to fp32.
-KC_INLINE void slice_unpack(const uint4& w, float* f, uint16_t) {
-  f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
-  f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
-  f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z);
-  f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
-}
+// Unpack a 16-byte fp32 slice.
 KC_INLINE void slice_unpack(const uint4& w, float* f, float) {
   f[0] = __uint_as_float(w.x); f[1] = __uint_as_float(w.y);
   f[2] = __uint_as_float(w.z); f[3] = __uint_as_float(w.w);
@@ -257,17 +245,17 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk(const DecodeArgs a) 
   }
 }
 
-// ---- bf16 split-K kernel with head slots ---------------------------------------
+// ---- 16-bit (bf16 / fp16) split-K kernel with head slots -------------------------
 //
-// The same work as k_decode_splitk for bf16 caches, laid out so that the
+// The same work as k_decode_splitk for 16-bit caches, laid out so that the
 // per-row softmax runs once per head instead of once per head per lane.
 // Lane li of a 16-lane row "owns" head own = li / (16/G) of the group and
 // keeps its partial dots in slot order: slot k holds head k ^ own.  A
 // reduce-scatter over the row (mirror, half mirror, xor 2, xor 1) then
 // leaves every lane with the full score of its own head for the row.  The
 // probabilities of the other heads come back through the same lane
-// exchanges, and P.V runs on pairs of rows with v_dot2c_f32_bf16 (P rounded
-// to bf16, fp32 accumulation), so a row costs 16 dot2 for the scores, 5 DPP
+// exchanges, and P.V runs on pairs of rows with v_dot2c_f32_bf16 / _f16 (P
+// rounded to the cache's type, fp32 accumulation), so a row costs 16 dot2 for the scores, 5 DPP
 // adds, one exp and 16 dot2 for the output per lane.
 
 // Lane moves within 16-lane rows; every control used here reads a lane of
@@ -756,7 +744,7 @@ __global__ __launch_bounds__(256) void k_decode_pool(const PoolDecodeArgs a) {
   }
 }
 
-// bf16 caches run the head-slot kernel, fp32 caches the plain one (which
+// 16-bit caches run the head-slot kernel, fp32 caches the plain one (which
 // has no paged variant: the host rejects paged fp32).
 template <typename T, int G, bool GATHER, bool SPILL, bool PAGED = false>
 constexpr void (*splitk_kernel())(const DecodeArgs) {
