@@ -40,7 +40,8 @@
  * Supported.  dtype F32 with head_dim 64, dtype BF16 or F16 with head_dim
  *             128 (one 256-byte K/V row in every case).  Prefill: BF16 or
  *             F16, head_dim 128, tile 128, batch 1..65535, Hq/Hkv in
- *             {1,2,4,8}.  Decode: ctx_len * kv_stride_n * element size below
+ *             {1,2,4,8}, kv_stride_n * element size at most 32 MiB (64 rows
+ *             span under 2 GiB).  Decode: ctx_len * kv_stride_n * element size below
  *             4 GiB (one head's rows; 16.7M keys at 256 bytes per row); a
  *             16-bit anchor decode also needs ctx_len <= 2048 * spill split (about
  *             8.6M keys for Hq/Hkv <= 4, 4.3M for 8), else KASCADE_ERR_SHAPE.

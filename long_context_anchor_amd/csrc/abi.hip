@@ -2,6 +2,7 @@
 // sequencing and per-kernel event timing.  Every check happens before the
 // first launch, so a rejected call leaves all outputs untouched.
 #include <math.h>
+#include <atomic>
 #include <mutex>
 #include <string.h>
 #include <vector>
@@ -116,7 +117,7 @@ int splitk_slots(DeviceInfo* d, int dtype, int G, bool gather, bool spill, bool 
 
 // ---- per-kernel event timing ------------------------------------------------
 struct Timer {
-  bool on = false;
+  std::atomic<bool> on{false};   // read by every launch, from any thread
   double total_ms = 0.0;
   int64_t launches = 0;
   std::vector<hipEvent_t> pool;   // pairs
@@ -142,7 +143,7 @@ hipError_t timer_drain(Timer& t) {
 template <typename F>
 hipError_t timed(int id, hipStream_t s, F&& launch) {
   Timer& t = g_timer[id];
-  if (!t.on) return launch();
+  if (!t.on.load(std::memory_order_relaxed)) return launch();
   if (t.used == kTimerPairs) {
     hipError_t e = timer_drain(t);
     if (e != hipSuccess) return e;
@@ -166,6 +167,9 @@ int hip_status(hipError_t e) {
 
 // ---- validation ---------------------------------------------------------------
 size_t elem_size(int dtype) { return dtype == KASCADE_F32 ? 4 : 2; }
+
+// 64 rows of this many bytes span less than 2^31 bytes
+constexpr int64_t kMaxPrefillRowBytes = ((int64_t)1 << 31) / 64;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -200,6 +204,9 @@ int check_shape(const kascade_shape* s, bool prefill, bool paged = false) {
   // decode kernels address a head's rows with 32-bit byte offsets
   if (!prefill && !paged && (int64_t)s->ctx_len * s->kv_stride_n * es > (int64_t)0xFFFFFF00)
     return KASCADE_ERR_SHAPE;
+  // prefill kernels address the rows of a 64-key block with 32-bit byte
+  // offsets from the block's first row
+  if (prefill && s->kv_stride_n * es > kMaxPrefillRowBytes) return KASCADE_ERR_SHAPE;
   return KASCADE_OK;
 }
 
@@ -928,7 +935,7 @@ int kascade_kernel_timer_enable(int id, int enable) {
     t.total_ms = 0.0;
     t.launches = 0;
   }
-  t.on = enable != 0;
+  t.on.store(enable != 0, std::memory_order_relaxed);
   return KASCADE_OK;
 }
 

@@ -107,6 +107,16 @@ def test_prefill_validation():
     assert call(rule=K.TopkRule(128, 10, 64, 64)) == -4     # k_min below the tile
     assert call(ws=ws_n - 1) == -6
     assert call(shape=_shape(N=1000, d=64, prefill=True)) == -3  # fp32 prefill unsupported
+    wide = _shape(N=64, d=128, Hq=8, Hkv=2, dtype=K.KASCADE_BF16, prefill=True)
+    wide.kv_stride_n = (1 << 24) + 8       # rows of 32 MiB + 16 B: a 64-row block spans 2 GiB
+    wide.kv_stride_h = wide.kv_stride_n * 64
+    wide.kv_stride_b = wide.kv_stride_h * 2
+    assert call(shape=wide) == -2
+    wide.kv_stride_n = 1 << 24              # exactly 32 MiB rows pass the shape check: the call
+    wide.kv_stride_h = wide.kv_stride_n * 64  # then stops at the (short) workspace, before any launch
+    wide.kv_stride_b = wide.kv_stride_h * 2
+    need = K.kascade_workspace_bytes(K.OP_ANCHOR_PREFILL, wide, 0, K.PREFILL_RULE)
+    assert need > 0 and call(shape=wide, ws=need - 1) == -6
     assert K.kascade_reuse_prefill(sp, FAKE, FAKE, FAKE, K.PREFILL_RULE, FAKE, [0, 5], FAKE,
                                    None, 0, 0) == -5
 
