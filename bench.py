@@ -438,11 +438,63 @@ def paged_bench(torch, K, synth, configs, args):
         res[name] = row
         del layers
         torch.cuda.empty_cache()
-    print(json.dumps({"metric": "paged-KV decode attention us/layer (block size 16) vs contiguous",
+    res["prefill32k"] = paged_prefill_row(torch, K, synth, configs, args)
+    print(json.dumps({"metric": "paged-KV attention (block size 16) vs contiguous: decode us/layer, "
+                                "reuse prefill ms/layer",
                       "unit": "us/layer", "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
-                      "config": {"workload": "Llama-3.1-8B-shaped decode layers, 32q/8kv heads, d=128, "
-                                             "32K B=1 k=3264 and 128K B=4 k=13120, 8 distinct layers"},
+                      "config": {"workload": "Llama-3.1-8B-shaped layers, 32q/8kv heads, d=128: decode "
+                                             "32K B=1 k=3264 and 128K B=4 k=13120 (8 distinct layers), "
+                                             "reuse prefill of a 32K-token prompt (tile 128, k_t min 256)"},
                       "components": res}), flush=True)
+
+
+def paged_prefill_row(torch, K, synth, configs, args):
+    """Reuse prefill of the 32K-token prompt over a paged cache (block size
+    16, blocks scattered by a seeded permutation) against the contiguous
+    cache, on the tile lists of the anchor layer before it; the two outputs
+    must be bitwise identical."""
+    cfg = configs.LLAMA_PREFILL_32K
+    N, Hkv, d, bs = cfg.ctx_len, cfg.n_kv_heads, cfg.head_dim, 16
+    lin = synth.heavy_lineages(cfg.seed, 2, Hkv, N, cfg.heavy, cfg.drift)
+    maps = synth.head_maps(cfg.seed, 2, (0,), Hkv, cfg.head_map_kind)
+    lay = [synth.prefill_layer(cfg.seed, l, 1, cfg.n_q_heads, Hkv, d, N, synth.layer_heavy_sets(lin, l, (0,), maps),
+                               cfg.alpha, cfg.gamma, cfg.dtype, device="cuda") for l in (0, 1)]
+    _, _, tidx, _ = K.anchor_prefill(*lay[0])
+    q, kk, v = lay[1]
+    nb = N // bs
+    perm = torch.as_tensor(np.random.default_rng(cfg.seed).permutation(nb), dtype=torch.int64, device="cuda")
+    kc = torch.empty((nb, Hkv, bs, d), dtype=kk.dtype, device="cuda")
+    vc = torch.empty_like(kc)
+    kc[perm] = kk.view(Hkv, nb, bs, d).permute(1, 0, 2, 3)
+    vc[perm] = v.view(Hkv, nb, bs, d).permute(1, 0, 2, 3)
+    tab = perm.to(torch.int32).view(1, nb).contiguous()
+    sh = K.make_shape(q, kk, N)
+    shp = K.paged_shape(q, kc, N)
+    pg = K.paged_kv(tab, kc)
+    outs = {False: torch.empty_like(q), True: torch.empty_like(q)}
+
+    def run(paged):
+        if paged:
+            K.check(K.kascade_reuse_prefill_paged(shp, pg, q, kc, vc, K.PREFILL_RULE, tidx, maps[1], outs[True]),
+                    "reuse_prefill_paged")
+        else:
+            K.check(K.kascade_reuse_prefill(sh, q, kk, v, K.PREFILL_RULE, tidx, maps[1], outs[False], None, 0),
+                    "reuse_prefill")
+
+    row = {}
+    for paged in (False, True):
+        for _ in range(args.warmup):
+            run(paged)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            run(paged)
+        e1.record()
+        torch.cuda.synchronize()
+        row["reuse_%s_ms" % ("paged" if paged else "contig")] = e0.elapsed_time(e1) / args.steps
+    row["identical"] = bool(torch.equal(outs[False].view(torch.int16), outs[True].view(torch.int16)))
+    return row
 
 
 # ---------------------------------------------------------------------------
@@ -462,7 +514,7 @@ def main():
     ap.add_argument("--dtype", choices=["bf16", "f16"], default="bf16",
                     help="element type of q, k, v and outputs (the workloads are defined in bf16)")
     ap.add_argument("--paged", action="store_true",
-                    help="time decode over paged KV caches against contiguous caches")
+                    help="time decode and the reuse prefill over paged KV caches against contiguous caches")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "

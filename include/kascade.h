@@ -187,6 +187,21 @@ int kascade_reuse_decode_paged(const kascade_shape* shape, const kascade_paged_k
                                const int32_t* head_map, void* out, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
+/* kascade_reuse_prefill over paged caches ([Explainer] "アンカーレイヤーと再利用
+ * レイヤー" and "ヘッドリマッピング" as for the contiguous call): the same
+ * results for the same logical keys.  shape->ctx_len is the prompt length N
+ * (logical rows 0..N-1 of every batch, reached through the block table);
+ * queries [B,Hq,N,d] through the q strides; positions in
+ * anchor_tile_topk_idx are logical.  The tile's key list and its physical
+ * rows are both staged in LDS, so k of the last tile is at most 12288
+ * (prompts up to about 122K tokens at pct 10), else KASCADE_ERR_SHAPE.
+ * No workspace is used (pass NULL, 0). */
+int kascade_reuse_prefill_paged(const kascade_shape* shape, const kascade_paged_kv* paged,
+                                const void* q, const void* k_cache, const void* v_cache,
+                                const kascade_topk_rule* rule, const int32_t* anchor_tile_topk_idx,
+                                const int32_t* head_map, void* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
 /* ---- calibration (offline: choosing anchors and head maps) -------------- */
 
 /* Per-KV-head similarity of every pair of layers a <= b over S calibration

@@ -874,21 +874,20 @@ int kascade_anchor_prefill(const kascade_shape* s, const void* q, const void* k,
   return hip_status(e);
 }
 
-int kascade_reuse_prefill(const kascade_shape* s, const void* q, const void* k, const void* v,
-                          const kascade_topk_rule* rule, const int32_t* idx,
-                          const int32_t* head_map, void* out, void* ws, size_t ws_bytes,
-                          hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
-  int st = check_shape(s, true);
+static int reuse_prefill_impl(const kascade_shape* s, const kascade_paged_kv* pg, const void* q,
+                              const void* k, const void* v, const kascade_topk_rule* rule,
+                              const int32_t* idx, const int32_t* head_map, void* out,
+                              hipStream_t stream) {
+  int st = check_shape(s, true, pg != nullptr);
   if (st) return st;
+  if ((st = check_paged(s, pg))) return st;
   if ((st = check_rule(rule))) return st;
   if (!q || !k || !v || !out || !idx) return KASCADE_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return KASCADE_ERR_ARG;
   HeadMap hm;
   if ((st = check_head_map(head_map, s->n_kv_heads, &hm))) return st;
-  if ((size_t)tile_k_for_len(s->ctx_len, rule->pct, rule->round_to, rule->k_min) >
-      prefill_sparse_max_list())
+  const size_t max_list = pg ? prefill_sparse_paged_max_list() : prefill_sparse_max_list();
+  if ((size_t)tile_k_for_len(s->ctx_len, rule->pct, rule->round_to, rule->k_min) > max_list)
     return KASCADE_ERR_SHAPE;
   DeviceInfo* dev = nullptr;
   if ((st = device_setup(&dev))) return st;
@@ -899,8 +898,37 @@ int kascade_reuse_prefill(const kascade_shape* s, const void* q, const void* k, 
   a.round_to = rule->round_to;
   a.k_min = rule->k_min;
   a.hm = hm;
+  if (pg) {
+    a.table = pg->block_table;
+    a.table_stride = pg->table_stride;
+    int sh = 0;
+    while ((1 << sh) < pg->block_size) ++sh;
+    a.blk_shift = sh;
+    a.num_blocks = pg->num_blocks;
+    a.blk_rows = (uint32_t)(pg->block_stride / s->kv_stride_n);
+  }
   return hip_status(timed(KASCADE_K_PREFILL_SPARSE, stream,
                           [&] { return launch_prefill_sparse(a, stream); }));
+}
+
+int kascade_reuse_prefill(const kascade_shape* s, const void* q, const void* k, const void* v,
+                          const kascade_topk_rule* rule, const int32_t* idx,
+                          const int32_t* head_map, void* out, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return reuse_prefill_impl(s, nullptr, q, k, v, rule, idx, head_map, out, stream);
+}
+
+int kascade_reuse_prefill_paged(const kascade_shape* s, const kascade_paged_kv* pg, const void* q,
+                                const void* k_cache, const void* v_cache,
+                                const kascade_topk_rule* rule, const int32_t* idx,
+                                const int32_t* head_map, void* out, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!pg) return KASCADE_ERR_NULL;
+  return reuse_prefill_impl(s, pg, q, k_cache, v_cache, rule, idx, head_map, out, stream);
 }
 
 int kascade_dense_prefill(const kascade_shape* s, const void* q, const void* k, const void* v,

@@ -90,6 +90,13 @@ struct PrefillArgs {
   int32_t pct, round_to, k_min;  // tile k rule
   int32_t half;                  // 1: fp16 q, k, v and out; 0: bf16
   HeadMap hm;
+  // paged K/V (sparse only; table == null: contiguous caches).  Logical
+  // position j of batch b is row j % 2^blk_shift of physical block
+  // table[b * table_stride + (j >> blk_shift)], whose first row is physical
+  // row block * blk_rows (rows of kv_sn elements from the cache base).
+  const int32_t* table;
+  int32_t table_stride, blk_shift, num_blocks;
+  uint32_t blk_rows;
 };
 
 // Launchers: return hipSuccess or the launch error.
@@ -139,6 +146,7 @@ hipError_t launch_prefill_flash(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_pool(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_sparse(const PrefillArgs& a, hipStream_t s);
 size_t prefill_sparse_max_list();
+size_t prefill_sparse_paged_max_list();
 hipError_t prefill_set_max_lds();
 
 // The per-tile k rule, identical on host and device.

@@ -85,6 +85,16 @@ struct RowStager {
       k[i] = ld16(base + (int64_t)(p < 0 ? 0 : p) * row_bytes + chunk(i) * 16);
     }
   }
+  // Physical rows rows[rr] of a paged cache (block-relative rows rr <
+  // nvalid); missing rows load physical row 0 and are masked the same way.
+  KC_INLINE void load_rows(const char* base, int64_t row_bytes, const int32_t* rows, int nvalid) {
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int rr = row(i);
+      const uint32_t p = rr < nvalid ? (uint32_t)rows[rr] : 0u;
+      k[i] = ld16(base + (uint64_t)p * (uint64_t)row_bytes + chunk(i) * 16);
+    }
+  }
   // rows as [key][d] (padded rows of STRIDE bf16)
   KC_INLINE void store(uint16_t* sk) const {
 #pragma unroll
@@ -163,8 +173,9 @@ KC_INLINE void qk_block(const uint16_t* sk, const typename Fmt16<HALF>::v8* qf, 
 // K is double-buffered in LDS (K_{j+1} is written one block ahead), V is
 // single-buffered (V_j is written at the start of step j); global loads of
 // K_{j+2} and V_{j+1} are in flight during step j.
-template <bool GATHER, int WAVES, bool HALF, bool DB>
+template <bool GATHER, int WAVES, bool HALF, bool DB, bool PAGED = false>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const PrefillArgs a) {
+  static_assert(GATHER || !PAGED, "paged caches are read through a key list");
   typedef Fmt16<HALF> F;   // bf16 or fp16 elements
   typedef typename F::v8 v8;
   constexpr int NT = 64 * WAVES;
@@ -218,18 +229,34 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const Pr
     }
   }
   int nkeys = kend;
+  // PAGED: the physical row of every listed key follows the list in LDS
+  // (logical positions stay in slist for the causal mask)
+  int32_t* const sphys = slist + a.k_max;
   if (GATHER) {
     nkeys = tile_k_for_len(kend, a.pct, a.round_to, a.k_min);
     const int32_t* list = a.idx + ((int64_t)(b * a.T + t) * a.Hkv + a.hm.m[g]) * a.k_max;
     for (int i = tid; i < nkeys; i += NT) {
       const int p = list[i];
-      slist[i] = (p >= 0 && p < N) ? p : -1;
+      const int lp = (p >= 0 && p < N) ? p : -1;
+      slist[i] = lp;
+      if (PAGED) {
+        // block clamped into the cache so a bad table cannot fault
+        uint32_t phys = 0;
+        if (lp >= 0) {
+          const int blk = min(max(a.table[(int64_t)b * a.table_stride + (lp >> a.blk_shift)], 0),
+                              a.num_blocks - 1);
+          phys = (uint32_t)blk * a.blk_rows + (uint32_t)(lp & ((1 << a.blk_shift) - 1));
+        }
+        sphys[i] = (int32_t)phys;
+      }
     }
     __syncthreads();
   }
   const int64_t row_bytes = a.kv_sn * 2;
-  const char* kbase = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh) * 2;
-  const char* vbase = reinterpret_cast<const char*>(a.v) + ((int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh) * 2;
+  // paged caches hold every batch's blocks: no batch offset
+  const int64_t head_off = ((PAGED ? 0 : (int64_t)b * a.kv_sb) + (int64_t)g * a.kv_sh) * 2;
+  const char* kbase = reinterpret_cast<const char*>(a.k) + head_off;
+  const char* vbase = reinterpret_cast<const char*>(a.v) + head_off;
   const int nb = (nkeys + kKB - 1) / kKB;
 
   RowStager<NT> kr;
@@ -237,12 +264,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const Pr
   // loads of block jb (K or V) into a stager
   auto load_blk = [&](RowStager<NT>& st, int jb) {
     const int kb = jb * kKB;
-    if (GATHER) st.load_gather(kbase, row_bytes, slist + kb, nkeys - kb);
+    if (PAGED) st.load_rows(kbase, row_bytes, sphys + kb, nkeys - kb);
+    else if (GATHER) st.load_gather(kbase, row_bytes, slist + kb, nkeys - kb);
     else st.load_dense(kbase + (int64_t)kb * row_bytes, row_bytes, nkeys - kb);
   };
   auto load_vblk = [&](RowStager<NT, kVStride>& st, int jb) {
     const int kb = jb * kKB;
-    if (GATHER) st.load_gather(vbase, row_bytes, slist + kb, nkeys - kb);
+    if (PAGED) st.load_rows(vbase, row_bytes, sphys + kb, nkeys - kb);
+    else if (GATHER) st.load_gather(vbase, row_bytes, slist + kb, nkeys - kb);
     else st.load_dense(vbase + (int64_t)kb * row_bytes, row_bytes, nkeys - kb);
   };
 
@@ -515,16 +544,16 @@ hipError_t flash_h(const PrefillArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool HALF>
+template <bool HALF, bool PAGED>
 hipError_t sparse_h(const PrefillArgs& a, hipStream_t s) {
   // gathered variants keep V single-buffered: double buffering measured no
   // faster here and would take LDS from the staged list
-  const size_t lds = (size_t)a.k_max * sizeof(int32_t);
+  const size_t lds = (size_t)a.k_max * sizeof(int32_t) * (PAGED ? 2 : 1);
   if ((a.Hq / a.Hkv) % 2 == 0)
-    hipLaunchKernelGGL((k_prefill_attn<true, 8, HALF, false>), dim3(xcd_grid(a.T * (a.Hq / 2) * a.B)),
+    hipLaunchKernelGGL((k_prefill_attn<true, 8, HALF, false, PAGED>), dim3(xcd_grid(a.T * (a.Hq / 2) * a.B)),
                        dim3(512), lds, s, a);
   else
-    hipLaunchKernelGGL((k_prefill_attn<true, 4, HALF, false>), dim3(xcd_grid(a.T * a.Hq * a.B)),
+    hipLaunchKernelGGL((k_prefill_attn<true, 4, HALF, false, PAGED>), dim3(xcd_grid(a.T * a.Hq * a.B)),
                        dim3(256), lds, s, a);
   return hipGetLastError();
 }
@@ -542,12 +571,12 @@ hipError_t pool_h(const PrefillArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool HALF>
+template <bool HALF, bool PAGED>
 hipError_t set_lds_h(int bytes) {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill_attn<true, 8, HALF, false>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill_attn<true, 8, HALF, false, PAGED>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill_attn<true, 4, HALF, false>),
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill_attn<true, 4, HALF, false, PAGED>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
@@ -557,17 +586,23 @@ hipError_t launch_prefill_flash(const PrefillArgs& a, hipStream_t s) {
   return a.half ? flash_h<true>(a, s) : flash_h<false>(a, s);
 }
 
-// The reuse prefill keeps the tile's key list in dynamic LDS (k_max int32).
+// The reuse prefill keeps the tile's key list in dynamic LDS (k_max int32;
+// over a paged cache also the k_max physical rows, so half as many keys).
 size_t prefill_sparse_max_list() { return 24576; }
+size_t prefill_sparse_paged_max_list() { return prefill_sparse_max_list() / 2; }
 
 hipError_t prefill_set_max_lds() {
   const int bytes = (int)(prefill_sparse_max_list() * sizeof(int32_t));
-  hipError_t e = set_lds_h<false>(bytes);
-  return e != hipSuccess ? e : set_lds_h<true>(bytes);
+  hipError_t e = set_lds_h<false, false>(bytes);
+  if (e == hipSuccess) e = set_lds_h<true, false>(bytes);
+  if (e == hipSuccess) e = set_lds_h<false, true>(bytes);
+  if (e == hipSuccess) e = set_lds_h<true, true>(bytes);
+  return e;
 }
 
 hipError_t launch_prefill_sparse(const PrefillArgs& a, hipStream_t s) {
-  return a.half ? sparse_h<true>(a, s) : sparse_h<false>(a, s);
+  if (a.table) return a.half ? sparse_h<true, true>(a, s) : sparse_h<false, true>(a, s);
+  return a.half ? sparse_h<true, false>(a, s) : sparse_h<false, false>(a, s);
 }
 
 hipError_t launch_prefill_pool(const PrefillArgs& a, hipStream_t s) {

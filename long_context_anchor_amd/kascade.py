@@ -31,7 +31,7 @@ EXPORTS = [
     "kascade_topk_select_f32", "kascade_dense_decode", "kascade_dense_prefill",
     "kascade_kernel_timer_enable", "kascade_kernel_timer_read", "kascade_status_str",
     "kascade_last_hip_error", "kascade_version",
-    "kascade_anchor_decode_paged", "kascade_reuse_decode_paged",
+    "kascade_anchor_decode_paged", "kascade_reuse_decode_paged", "kascade_reuse_prefill_paged",
     "kascade_calib_head_similarity", "kascade_layer_weight", "kascade_layer_weight_workspace_bytes",
     "kascade_weighted_similarity", "kascade_select_anchors", "kascade_head_maps",
 ]
@@ -91,6 +91,7 @@ _SIGS = {
     "kascade_version": (ctypes.c_char_p, []),
     "kascade_anchor_decode_paged": (_i32, [ctypes.POINTER(Shape), ctypes.POINTER(PagedKV), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kascade_reuse_decode_paged": (_i32, [ctypes.POINTER(Shape), ctypes.POINTER(PagedKV), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kascade_reuse_prefill_paged": (_i32, [ctypes.POINTER(Shape), ctypes.POINTER(PagedKV), _vp, _vp, _vp, ctypes.POINTER(TopkRule), _vp, _vp, _vp, _vp, _sz, _vp]),
     "kascade_calib_head_similarity": (_i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "kascade_layer_weight": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "kascade_layer_weight_workspace_bytes": (_sz, [_i32]),
@@ -217,6 +218,15 @@ def kascade_reuse_decode_paged(shape, paged, q, k_cache, v_cache, topk, anchor_t
                                             _p(v_cache), topk, _p(anchor_topk_idx),
                                             ctypes.cast(hm, _vp) if hm is not None else None, _p(out),
                                             _p(workspace), workspace_bytes, _stream(stream))
+
+
+def kascade_reuse_prefill_paged(shape, paged, q, k_cache, v_cache, rule, anchor_tile_topk_idx, head_map, out,
+                                workspace=None, workspace_bytes=0, stream=None) -> int:
+    hm = (ctypes.c_int32 * len(head_map))(*[int(x) for x in head_map]) if head_map is not None else None
+    return lib().kascade_reuse_prefill_paged(ctypes.byref(shape), ctypes.byref(paged), _p(q), _p(k_cache),
+                                             _p(v_cache), ctypes.byref(rule), _p(anchor_tile_topk_idx),
+                                             ctypes.cast(hm, _vp) if hm is not None else None, _p(out),
+                                             _p(workspace), workspace_bytes, _stream(stream))
 
 
 def kascade_calib_head_similarity(L, S, n_kv_heads, n, k, pooled, topk_idx, sim, stream=None) -> int:
@@ -444,9 +454,11 @@ def layer_weight(x, y):
 
 
 def paged_shape(q, k_cache, n_ctx: int, scale: float = 0.0) -> Shape:
-    """Shape for a paged cache [num_blocks, Hkv, block_size, d] (vLLM-style layout)."""
+    """Shape for a paged cache [num_blocks, Hkv, block_size, d] (vLLM-style layout); q is
+    [B,Hq,d] (decode) or [B,Hq,N,d] (prefill)."""
+    qsn = q.stride(2) if q.dim() == 4 else 0
     return Shape(q.shape[0], q.shape[1], k_cache.shape[1], q.shape[-1], n_ctx, _dtype_code(q), scale, 0,
-                 q.stride(0), q.stride(1), 0, 0, k_cache.stride(1), k_cache.stride(2))
+                 q.stride(0), q.stride(1), qsn, 0, k_cache.stride(1), k_cache.stride(2))
 
 
 def paged_kv(block_table, k_cache) -> PagedKV:
@@ -481,3 +493,14 @@ def reuse_decode_paged(q, k_cache, v_cache, block_table, n_ctx: int, anchor_idx,
                                      ws.numel()), "kascade_reuse_decode_paged")
     return out
 
+
+def reuse_prefill_paged(q, k_cache, v_cache, block_table, anchor_tile_idx, head_map: Sequence[int],
+                        rule: TopkRule = PREFILL_RULE):
+    """Paged reuse prefill: q [B,Hq,N,d], caches [num_blocks,Hkv,block_size,d]; returns out [B,Hq,N,d]."""
+    N = q.shape[2]
+    sh = paged_shape(q, k_cache, N)
+    pg = paged_kv(block_table, k_cache)
+    out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    check(kascade_reuse_prefill_paged(sh, pg, q, k_cache, v_cache, rule, anchor_tile_idx, head_map, out),
+          "kascade_reuse_prefill_paged")
+    return out

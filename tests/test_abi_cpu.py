@@ -159,3 +159,36 @@ def test_paged_decode_validation_errors():
     assert anchor(desc(block_size=32), shape=_shape(N=1000)) == -3   # fp32 caches are not paged
     assert K.kascade_reuse_decode_paged(sh, desc(block_table=None), FAKE, FAKE, FAKE, 10, FAKE, [0, 1], FAKE,
                                         FAKE, ws, 0) == -1
+
+
+def test_paged_reuse_prefill_validation_errors():
+    """The paged reuse prefill checks the descriptor, rule, head map and list
+    length on the host; every call below stops before a launch."""
+    sp = _shape(N=1000, d=128, Hq=8, Hkv=2, dtype=K.KASCADE_BF16, prefill=True)
+    sp.kv_stride_b = 0
+    sp.kv_stride_h = 16 * 128
+
+    def desc(**kw):
+        pg = K.PagedKV(FAKE, 70, 16, 200, 0, 2 * 16 * 128)
+        for f, v in kw.items():
+            setattr(pg, f, v)
+        return pg
+
+    def call(pg, shape=sp, rule=K.PREFILL_RULE, hm=(0, 1)):
+        return K.kascade_reuse_prefill_paged(shape, pg, FAKE, FAKE, FAKE, rule, FAKE, list(hm), FAKE, None, 0, 0)
+
+    assert K.lib().kascade_reuse_prefill_paged(None, None, None, None, None, None, None, None, None,
+                                               None, 0, None) == -1
+    assert call(desc(block_table=None)) == -1
+    assert call(desc(block_size=24)) == -2            # not a power of two
+    assert call(desc(table_stride=10)) == -2          # table shorter than ceil(N / block_size)
+    assert call(desc(block_stride=16 * 128)) == -2    # second head's rows outside the block
+    assert call(desc(reserved=1)) == -8
+    assert call(desc(), rule=K.TopkRule(128, 10, 64, 64)) == -4
+    assert call(desc(), hm=(0, 2)) == -5
+    # k of the last tile above the paged list bound (12288 keys): 10% of 130000 tokens
+    long = _shape(N=130000, d=128, Hq=8, Hkv=2, dtype=K.KASCADE_BF16, prefill=True)
+    long.kv_stride_b = 0
+    long.kv_stride_h = 16 * 128
+    assert K.kascade_topk_for_len(130000, K.PREFILL_RULE) > 12288
+    assert call(desc(table_stride=-(-130000 // 16), num_blocks=20000), shape=long) == -2

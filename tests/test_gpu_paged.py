@@ -1,9 +1,11 @@
-"""GPU parity of decode over paged KV caches (block tables, layout
-[num_blocks, Hkv, block_size, d], blocks scattered by a seeded permutation,
-ragged last block) against the oracle on the logical caches.  Tolerances as
-for contiguous decode: outputs 2e-2 max-abs (bf16), lse 1e-4, pooled 1e-4
-relative, indices bit-exact against a full sort of the GPU's own pooled row
-and within the 1e-5 tie band of the oracle's."""
+"""GPU parity of decode and of the gathered reuse prefill over paged KV caches
+(block tables, layout [num_blocks, Hkv, block_size, d], blocks scattered by a
+seeded permutation, ragged last block) against the oracle on the logical
+caches.  Tolerances as for the contiguous calls: outputs 2e-2 max-abs (bf16),
+lse 1e-4, pooled 1e-4 relative, indices bit-exact against a full sort of the
+GPU's own pooled row and within the 1e-5 tie band of the oracle's.  The paged
+reuse prefill reads the same rows with the same arithmetic as the contiguous
+one, so the two must agree bit for bit."""
 import sys
 
 import numpy as np
@@ -86,3 +88,74 @@ def test_paged_reuse_decode(N, bs, topk, hm):
     out_c = K.reuse_decode(q, k, v, idx, hm)
     torch.cuda.synchronize()
     assert np.max(np.abs(np64(out) - np64(out_c))) <= 1e-2
+
+
+def _tile_lists(seed, B, T, Hkv, N):
+    """Seeded prefill tile lists [B,T,Hkv,k_max]: k_t ascending distinct
+    positions below P_t per (batch, tile, KV head), -1 padded."""
+    kmax = oracle.prefill_tile_k(T - 1, N)[1]
+    rng = np.random.default_rng(seed)
+    out = -np.ones((B, T, Hkv, kmax), dtype=np.int32)
+    for b in range(B):
+        for t in range(T):
+            P, kt = oracle.prefill_tile_k(t, N)
+            for g in range(Hkv):
+                out[b, t, g, :kt] = np.sort(rng.choice(P, size=kt, replace=False))
+    return out
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,bs,hm", [
+    (1, 8, 2, 1000, 16, [1, 0]),          # ragged last block and tile, swapped heads
+    (2, 8, 2, 2049, 64, [1, 1]),          # two batches, many-to-one map, one-row last tile
+    (1, 16, 4, 3000, 32, [3, 0, 0, 2]),   # group of 4
+    (1, 2, 2, 600, 128, [1, 0]),          # group of 1 (the four-wave kernel)
+])
+def test_paged_reuse_prefill(B, Hq, Hkv, N, bs, hm):
+    say("paged reuse prefill", B, Hq, Hkv, N, bs, hm)
+    g = torch.Generator(device=DEV).manual_seed(N + bs)
+    q = torch.randn((B, Hq, N, 128), generator=g, device=DEV).bfloat16()
+    k = torch.randn((B, Hkv, N, 128), generator=g, device=DEV).bfloat16()
+    v = torch.randn((B, Hkv, N, 128), generator=g, device=DEV).bfloat16()
+    T = -(-N // 128)
+    lists = _tile_lists(N + 3, B, T, Hkv, N)
+    idx = torch.as_tensor(lists, device=DEV)
+    kc, vc, table = _paged(k, v, bs, seed=N + 2)
+    out = K.reuse_prefill_paged(q, kc, vc, table, idx, hm)
+    out_c = K.reuse_prefill(q, k, v, idx, hm)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_c.view(torch.int16))
+    qn, kn, vn, on = np64(q), np64(k), np64(v), np64(out)
+    rows = sorted({0, 1, 127, 128, N // 2, N - 2, N - 1})
+    for b in {0, B - 1}:
+        for h in {0, Hq // 2, Hq - 1}:
+            ref = oracle.sparse_prefill_rows(qn, kn, vn, lists, hm, b, h, rows)
+            assert np.max(np.abs(on[b, h, rows] - ref)) <= 2e-2, (b, h)
+
+
+def test_paged_reuse_prefill_32k():
+    """Full-size reuse layer of the 32K-token prompt workload (32 q / 8 KV
+    heads, bf16, block size 16, blocks scattered): bit-identical to the
+    contiguous call (which the 32K prefill test checks against the oracle),
+    and the oracle checks sampled rows of two tiles directly."""
+    cfg = configs.LLAMA_PREFILL_32K
+    N, Hkv, d, bs = cfg.ctx_len, cfg.n_kv_heads, cfg.head_dim, 16
+    say("paged reuse prefill 32K", N, bs)
+    lin = synth.heavy_lineages(cfg.seed, 2, Hkv, N, cfg.heavy, cfg.drift)
+    maps = synth.head_maps(cfg.seed, 2, (0,), Hkv, cfg.head_map_kind)
+    q, k, v = synth.prefill_layer(cfg.seed, 1, 1, cfg.n_q_heads, Hkv, d, N,
+                                  synth.layer_heavy_sets(lin, 1, (0,), maps), cfg.alpha, cfg.gamma, "bf16",
+                                  device=DEV)
+    T = N // 128
+    lists = _tile_lists(cfg.seed, 1, T, Hkv, N)
+    idx = torch.as_tensor(lists, device=DEV)
+    kc, vc, table = _paged(k, v, bs, seed=cfg.seed)
+    out = K.reuse_prefill_paged(q, kc, vc, table, idx, maps[1])
+    out_c = K.reuse_prefill(q, k, v, idx, maps[1])
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_c.view(torch.int16))
+    qn, kn, vn = np64(q), np64(k), np64(v)
+    for t in (3, T - 1):
+        rows = [128 * t, 128 * t + 77, 128 * t + 127]
+        for h in (0, cfg.n_q_heads - 1):
+            ref = oracle.sparse_prefill_rows(qn, kn, vn, lists, maps[1], 0, h, rows)
+            assert np.max(np.abs(np64(out[0, h, rows]) - ref)) <= 2e-2, (t, h)
