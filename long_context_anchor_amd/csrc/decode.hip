@@ -783,14 +783,22 @@ hipError_t splitk_attrs_g(int G, bool gather, bool spill, bool paged, int* block
   return hipErrorInvalidValue;
 }
 
+// Largest dynamic LDS of a 16-bit spilling launch: the score buffer of the
+// longest split (or the one-workgroup-per-CU floor), plus the row list when
+// the cache is paged.
+inline size_t spill_dyn_lds_cap(bool paged) {
+  const size_t scores = kSpillMaxLds > kSpillMinLds ? kSpillMaxLds : kSpillMinLds;
+  return scores + (paged ? (kPlanMaxKeys + kListPad) * sizeof(int32_t) : 0);
+}
+
 template <int G, bool HALF>
 hipError_t spill_set_lds_gh() {
   hipError_t e = hipFuncSetAttribute((const void*)k_decode_splitk_slots<G, false, true, false, HALF>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSpillMaxLds);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)spill_dyn_lds_cap(false));
   if (e != hipSuccess) return e;
   return hipFuncSetAttribute((const void*)k_decode_splitk_slots<G, false, true, true, HALF>,
-                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)(kSpillMaxLds + (kPlanMaxKeys + kListPad) * sizeof(int32_t)));
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)spill_dyn_lds_cap(true));
 }
 template <int G>
 hipError_t spill_set_lds_g() {
@@ -807,7 +815,7 @@ hipError_t launch_splitk_t(const DecodeArgs& a, bool gather, hipStream_t s) {
   const bool spill = !gather && a.scores;
   const size_t lds = decode_splitk_dyn_lds(sizeof(T) == 2 ? 1 : 0, G, gather, spill, paged,
                                            a.keys_per_split);
-  if (spill && lds > kSpillMaxLds + (paged ? (kPlanMaxKeys + kListPad) * sizeof(int32_t) : 0))
+  if (spill && lds > spill_dyn_lds_cap(paged))
     return hipErrorInvalidValue;
   dim3 grid(a.n_splits, a.Hkv, a.B);
   void (*k)(const DecodeArgs) = paged ? splitk_pick<T, G, true>(gather, spill)
@@ -855,7 +863,10 @@ hipError_t decode_splitk_attrs(int dtype, int G, bool gather, bool spill, bool p
 
 size_t decode_splitk_dyn_lds(int dtype, int G, bool gather, bool spill, bool paged, int kps) {
   size_t bytes = (gather || paged) ? (size_t)(kps + kListPad) * sizeof(int32_t) : 0;
-  if (spill && dtype != 0) bytes += spill_lds_bytes(G, kps);
+  if (spill && dtype != 0) {
+    bytes += spill_lds_bytes(G, kps);
+    if (bytes < kSpillMinLds) bytes = kSpillMinLds;   // one spilling workgroup per CU
+  }
   return bytes;
 }
 

@@ -108,6 +108,12 @@ constexpr int kPlanMaxKeys = 4096;
 // A bf16 anchor split keeps its scores in LDS until it ends: at most
 // kSpillMaxLds bytes of them, i.e. spill_max_keys(G) keys per split.
 constexpr size_t kSpillMaxLds = 66 * 1024 + 1024;
+// A 16-bit spilling workgroup asks for at least kSpillMinLds bytes of
+// dynamic LDS: with its static LDS that is more than half of a CU's 160 KiB,
+// so one spilling workgroup runs per CU (the planner's slot count sees it).
+// Measured against two per CU: 131072 keys x 4 batches 407 -> 386 us per
+// anchor layer, 32768 x 1 49.7 -> 49.2 us, identical results.
+constexpr size_t kSpillMinLds = 80 * 1024;
 size_t spill_lds_bytes(int G, int keys_per_split);
 int spill_max_keys(int G);
 hipError_t decode_set_max_lds();
