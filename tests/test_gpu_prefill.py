@@ -205,3 +205,49 @@ def test_prefill_sharp_softmax_and_late_max():
     k[:, :, 127::128] = 12.0 * w
     q, k = q.bfloat16(), k.bfloat16()
     _check_anchor_prefill(q, k, v)
+
+
+def test_prefill_graph_replay():
+    """An anchor prefill and the reuse prefill that consumes its tile lists,
+    captured as one HIP graph (workspace and outputs preallocated): each of
+    three replays, with the outputs poisoned and eager work in between,
+    equals the eager run bit for bit."""
+    N, Hq, Hkv = 1000, 8, 2
+    say("prefill graph replay", N, Hq, Hkv)
+    qa, ka, va = _rand_layer(1, Hq, Hkv, N, seed=21, planted=True)
+    qr, kr, vr = _rand_layer(1, Hq, Hkv, N, seed=22, planted=True)
+    sh = K.make_shape(qa, ka, N)
+    T, kmax = -(-N // 128), K.prefill_k_max(N, RULE)
+    ws = K.workspace(K.OP_ANCHOR_PREFILL, sh, 0, RULE)
+    out_a = torch.empty_like(qa)
+    lse = torch.empty(qa.shape[:3], dtype=torch.float32, device=DEV)
+    idx = torch.empty((1, T, Hkv, kmax), dtype=torch.int32, device=DEV)
+    out_r = torch.empty_like(qr)
+
+    def layer_pair():
+        K.check(K.kascade_anchor_prefill(sh, qa, ka, va, RULE, out_a, lse, idx, None, ws, ws.numel()), "anchor")
+        K.check(K.kascade_reuse_prefill(sh, qr, kr, vr, RULE, idx, [1, 0], out_r, None, 0), "reuse")
+
+    layer_pair()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (out_a, lse, idx, out_r)]
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            layer_pair()
+    torch.cuda.current_stream().wait_stream(st)
+    for rep in range(3):
+        out_a.zero_()
+        lse.fill_(float("nan"))
+        idx.fill_(-7)
+        out_r.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((out_a, lse, idx, out_r), eager):
+            assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got,
+                               want.view(torch.int16) if want.dtype == torch.bfloat16 else want), rep
+        layer_pair()   # eager work between replays
+        torch.cuda.synchronize()
