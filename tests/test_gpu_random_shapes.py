@@ -6,7 +6,9 @@ ragged), Top-k (decode), dtype (fp32 with d 64, bf16 or fp16 with d 128)
 and a random many-to-one head map.
 Anchor layers are checked in full (outputs, lse, pooled values, index
 lists); reuse layers run on the ORACLE's index lists, so both sides consume
-the same lists.  Tolerances as in the other GPU tests: outputs 1e-4 (fp32) /
+the same lists.  16-bit cases also run over paged caches (random block size,
+blocks scattered): paged decode against the oracle, paged reuse prefill bit
+for bit against the contiguous call.  Tolerances as in the other GPU tests: outputs 1e-4 (fp32) /
 2e-2 (16-bit) max-abs, decode lse 1e-4, prefill lse 1e-3, pooled 1e-4
 (decode) / 1e-3 (prefill tile rows) relative, index sets bit-exact against a
 full sort of the GPU's own pooled row and within the 1e-5 tie band of the
@@ -20,6 +22,7 @@ import torch
 import oracle
 from long_context_anchor_amd import synth
 from long_context_anchor_amd import kascade as K
+from test_gpu_paged import _paged
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -99,6 +102,23 @@ def test_random_decode(seed):
     torch.cuda.synchronize()
     r2, _ = oracle.sparse_decode(np64(q2), np64(k2), np64(v2), ridx, hm)
     assert np.max(np.abs(np64(o2) - r2)) <= tol
+    if dtype == "f32":
+        return   # paged caches are 16-bit only
+    # the same two layers over paged caches (random block size, blocks scattered)
+    bs = int(np.random.default_rng(3000 + seed).choice([16, 32, 64, 128]))
+    kc, vc, table = _paged(k, v, bs, seed=seed)
+    po, _, pidx, ppool = K.anchor_decode_paged(q, kc, vc, table, N, topk, want_pooled=True)
+    kc2, vc2, table2 = _paged(k2, v2, bs, seed=seed + 1)
+    po2 = K.reuse_decode_paged(q2, kc2, vc2, table2, N, lists, hm)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(np64(po) - ro)) <= tol
+    gpp, gpi = np64(ppool), pidx.cpu().numpy()
+    for b in range(B):
+        for g in range(Hkv):
+            assert np.array_equal(gpi[b, g], oracle.topk_full_sort(gpp[b, g], topk))
+            ok, nd = oracle.index_sets_agree(gpi[b, g], ridx[b, g], rpool[b, g])
+            assert ok, ("paged", b, g, nd)
+    assert np.max(np.abs(np64(po2) - r2)) <= tol
 
 
 @pytest.mark.parametrize("seed", range(16))
@@ -137,8 +157,15 @@ def test_random_prefill(seed):
     q2 = _randn((B, Hq, N, 128), 11 * seed + 1, dtype)
     k2 = _randn((B, Hkv, N, 128), 11 * seed + 2, dtype)
     v2 = _randn((B, Hkv, N, 128), 11 * seed + 3, dtype)
-    o2 = K.reuse_prefill(q2, k2, v2, torch.as_tensor(lists, device=DEV), hm, RULE)
+    lists_d = torch.as_tensor(lists, device=DEV)
+    o2 = K.reuse_prefill(q2, k2, v2, lists_d, hm, RULE)
+    # over a paged cache (random block size, blocks scattered): the same rows
+    # with the same arithmetic, so bit for bit the contiguous output
+    bs = int(np.random.default_rng(4000 + seed).choice([16, 32, 64, 128]))
+    kc2, vc2, table2 = _paged(k2, v2, bs, seed=seed)
+    po2 = K.reuse_prefill_paged(q2, kc2, vc2, table2, lists_d, hm, RULE)
     torch.cuda.synchronize()
+    assert torch.equal(po2.view(torch.int16), o2.view(torch.int16))
     q2n, k2n, v2n, o2n = np64(q2), np64(k2), np64(v2), np64(o2)
     rows = sorted({0, N // 3, N // 2, N - 1} | {min(N - 1, 128 * t + 127) for t in range(T)})
     for b in range(B):
