@@ -383,3 +383,26 @@ def test_decode_on_two_streams_from_two_threads():
         assert torch.equal(o.view(torch.int16), so.view(torch.int16))
         assert torch.equal(i, si) and torch.equal(p, sp)
         assert torch.equal(o2.view(torch.int16), so2.view(torch.int16))
+
+
+def test_reuse_decode_lists_in_any_order_and_with_repeats():
+    """The reuse decode takes the anchor's lists in any order: a shuffled list
+    gives the oracle's result for that list, and so does a list in which
+    some positions appear twice (each entry is one term of the softmax on
+    both sides)."""
+    B, Hq, Hkv, N, k = 2, 8, 2, 3000, 400
+    say("reuse decode shuffled / repeated lists", B, Hq, Hkv, N, k)
+    g = torch.Generator(device=DEV).manual_seed(77)
+    q = torch.randn((B, Hq, 128), generator=g, device=DEV).bfloat16()
+    kk = torch.randn((B, Hkv, N, 128), generator=g, device=DEV).bfloat16()
+    v = torch.randn((B, Hkv, N, 128), generator=g, device=DEV).bfloat16()
+    base = synth.random_index_lists(78, B, Hkv, N, k).numpy()
+    rng = np.random.default_rng(79)
+    shuffled = np.stack([np.stack([rng.permutation(base[b, h]) for h in range(Hkv)]) for b in range(B)])
+    repeated = shuffled.copy()
+    repeated[:, :, k // 2:] = shuffled[:, :, : k - k // 2]     # second half repeats the first
+    for lists, hm in ((shuffled, [1, 0]), (repeated, [0, 0])):
+        out = K.reuse_decode(q, kk, v, torch.as_tensor(lists.astype(np.int32), device=DEV), hm)
+        torch.cuda.synchronize()
+        ref, _ = oracle.sparse_decode(np64(q), np64(kk), np64(v), lists, hm)
+        assert np.max(np.abs(np64(out) - ref)) <= 2e-2
