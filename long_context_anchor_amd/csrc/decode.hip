@@ -38,12 +38,10 @@ struct Elem<float> {
 };
 template <>
 struct Elem<uint16_t> {
-  static constexpr int EPL = 8;    // bf16 per 16 bytes
   static constexpr int D = 128;
 };
 template <>
 struct Elem<_Float16> {
-  static constexpr int EPL = 8;    // fp16 per 16 bytes
   static constexpr int D = 128;
 };
 
