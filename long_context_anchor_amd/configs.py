@@ -15,7 +15,7 @@ LLAMA_ANCHORS: Tuple[int, ...] = (0, 2, 8, 13, 14)
 class Workload:
     name: str
     kind: str                 # "decode" | "prefill" | "e2e"
-    dtype: str                # "f32" | "bf16"
+    dtype: str                # "f32" | "bf16" | "f16"
     n_layers: int
     batch: int
     n_q_heads: int

@@ -6,6 +6,7 @@ indices bit-exact when the select sees the same fp32 scores, otherwise every
 element of the symmetric difference must have an oracle pooled score within
 1e-5 (relative) of the oracle's k-th value.
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -210,9 +211,10 @@ def test_reuse_full_list_equals_dense():
 # full-size layers of the Llama-shaped 32K workload and the 128K workload
 # ---------------------------------------------------------------------------
 
-def test_llama_32k_anchor_and_reuse_layer():
-    cfg = configs.LLAMA_DECODE_32K
-    say("32K anchor layer 0 + reuse layer 1")
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_llama_32k_anchor_and_reuse_layer(dtype):
+    cfg = dataclasses.replace(configs.LLAMA_DECODE_32K, dtype=dtype)
+    say("32K anchor layer 0 + reuse layer 1", dtype)
     q, k, v, maps = _decode_layer(cfg, 0)
     out, idx, ridx, ndiff = _check_anchor(q, k, v, cfg.topk, cfg.tol)
     say("  index symmetric-difference total", ndiff)
@@ -224,10 +226,11 @@ def test_llama_32k_anchor_and_reuse_layer():
     assert np.max(np.abs(np64(out1) - ref1)) <= cfg.tol
 
 
-def test_llama_128k_sampled():
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_llama_128k_sampled(dtype):
     # full-size launch (B=4, N=131072); the oracle checks batch row 3 and KV heads 0 and 5
-    cfg = configs.LLAMA_DECODE_128K
-    say("128K anchor + reuse, sampled rows")
+    cfg = dataclasses.replace(configs.LLAMA_DECODE_128K, dtype=dtype)
+    say("128K anchor + reuse, sampled rows", dtype)
     q, k, v, maps = _decode_layer(cfg, 0)
     out, lse, idx, pooled = K.anchor_decode(q, k, v, cfg.topk, want_pooled=True)
     q1, k1, v1, _ = _decode_layer(cfg, 1)

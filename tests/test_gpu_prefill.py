@@ -143,23 +143,25 @@ def test_reuse_prefill_full_lists_equal_dense():
     assert torch.max(torch.abs(sp.float() - dense.float())).item() <= 1e-2
 
 
-def test_llama_prefill_32k_sampled():
-    """Full-size anchor + reuse layer pair of the 32K-token prefill workload;
-    the oracle checks sampled tiles (0, 1, 20, 131, 255) of KV heads 0 and 6."""
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_llama_prefill_32k_sampled(dtype):
+    """Full-size anchor + reuse layer pair of the 32K-token prefill workload
+    (bf16, and the same workload in fp16); the oracle checks sampled tiles
+    (0, 1, 20, 131, 255) of KV heads 0 and 6."""
     cfg = configs.LLAMA_PREFILL_32K
     N = cfg.ctx_len
-    say("32K prefill anchor + reuse, sampled tiles")
+    say("32K prefill anchor + reuse, sampled tiles", dtype)
     lin = synth.heavy_lineages(cfg.seed, 2, cfg.n_kv_heads, N, cfg.heavy, cfg.drift)
     maps = synth.head_maps(cfg.seed, 2, cfg.anchors, cfg.n_kv_heads, cfg.head_map_kind)
     qa, ka, va = synth.prefill_layer(cfg.seed, 0, 1, cfg.n_q_heads, cfg.n_kv_heads, 128, N,
                                      synth.layer_heavy_sets(lin, 0, cfg.anchors, maps),
-                                     cfg.alpha, cfg.gamma, "bf16", device=DEV)
+                                     cfg.alpha, cfg.gamma, dtype, device=DEV)
     tiles = [0, 1, 20, 131, 255]
     _, idx, ref_idx = _check_anchor_prefill(qa, ka, va, tiles=tiles, heads_g=[0, 6])
     hm = maps[1]
     q, k, v = synth.prefill_layer(cfg.seed, 1, 1, cfg.n_q_heads, cfg.n_kv_heads, 128, N,
                                   synth.layer_heavy_sets(lin, 1, cfg.anchors, maps),
-                                  cfg.alpha, cfg.gamma, "bf16", device=DEV)
+                                  cfg.alpha, cfg.gamma, dtype, device=DEV)
     out = K.reuse_prefill(q, k, v, idx, hm, RULE)
     torch.cuda.synchronize()
     qn, kn, vn = np64(q), np64(k), np64(v)
