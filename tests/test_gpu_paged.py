@@ -159,3 +159,53 @@ def test_paged_reuse_prefill_32k():
         for h in (0, cfg.n_q_heads - 1):
             ref = oracle.sparse_prefill_rows(qn, kn, vn, lists, maps[1], 0, h, rows)
             assert np.max(np.abs(np64(out[0, h, rows]) - ref)) <= 2e-2, (t, h)
+
+
+def _paged_fast(k, v, bs, seed):
+    """Vectorised _paged for large caches (N a multiple of bs, no spare blocks)."""
+    B, Hkv, N, d = k.shape
+    nb = N // bs
+    perm = torch.as_tensor(np.random.default_rng(seed).permutation(B * nb).reshape(B, nb), dtype=torch.int64,
+                           device=DEV)
+    kc = torch.empty((B * nb, Hkv, bs, d), dtype=k.dtype, device=DEV)
+    vc = torch.empty_like(kc)
+    kc[perm.reshape(-1)] = k.view(B, Hkv, nb, bs, d).permute(0, 2, 1, 3, 4).reshape(B * nb, Hkv, bs, d)
+    vc[perm.reshape(-1)] = v.view(B, Hkv, nb, bs, d).permute(0, 2, 1, 3, 4).reshape(B * nb, Hkv, bs, d)
+    return kc, vc, perm.to(torch.int32).contiguous()
+
+
+def test_paged_decode_128k_sampled():
+    """Full-size paged anchor and reuse decode of the 128K x 4 workload (block
+    size 16, blocks scattered); the oracle checks batch row 2 and KV heads 1
+    and 7 on the logical caches."""
+    cfg = configs.LLAMA_DECODE_128K
+    N, B, Hkv, G, k = cfg.ctx_len, cfg.batch, cfg.n_kv_heads, cfg.group, cfg.topk
+    say("paged decode 128K x 4, sampled rows")
+    lin = synth.heavy_lineages(cfg.seed, 2, Hkv, N, cfg.heavy, cfg.drift)
+    maps = synth.head_maps(cfg.seed, 2, (0,), Hkv, cfg.head_map_kind)
+    q, kk, v = synth.decode_layer(cfg.seed, 0, B, cfg.n_q_heads, Hkv, cfg.head_dim, N,
+                                  synth.layer_heavy_sets(lin, 0, (0,), maps), cfg.alpha, "bf16", device=DEV)
+    kc, vc, table = _paged_fast(kk, v, 16, seed=5)
+    out, _, idx, pooled = K.anchor_decode_paged(q, kc, vc, table, N, k, want_pooled=True)
+    q1, k1, v1 = synth.decode_layer(cfg.seed, 1, B, cfg.n_q_heads, Hkv, cfg.head_dim, N,
+                                    synth.layer_heavy_sets(lin, 1, (0,), maps), cfg.alpha, "bf16", device=DEV)
+    kc1, vc1, table1 = _paged_fast(k1, v1, 16, seed=6)
+    hm = maps[1]
+    out1 = K.reuse_decode_paged(q1, kc1, vc1, table1, N, idx, hm)
+    torch.cuda.synchronize()
+    b = 2
+    for g in (1, 7):
+        hs = slice(g * G, (g + 1) * G)
+        ro, _, p = oracle.dense_decode(np64(q[b:b + 1, hs]), np64(kk[b:b + 1, g:g + 1]), np64(v[b:b + 1, g:g + 1]))
+        assert np.max(np.abs(np64(out[b:b + 1, hs]) - ro)) <= 2e-2
+        rpool = oracle.pool_decode(p, 1)[0, 0]
+        ridx = oracle.topk_full_sort(rpool, k)
+        gi = idx[b, g].cpu().numpy()
+        assert np.array_equal(gi, oracle.topk_full_sort(np64(pooled[b, g]), k))
+        ok, nd = oracle.index_sets_agree(gi, ridx, rpool)
+        assert ok, (g, nd)
+        for g2 in [x for x in range(Hkv) if hm[x] == g]:
+            hs2 = slice(g2 * G, (g2 + 1) * G)
+            r1, _ = oracle.sparse_decode(np64(q1[b:b + 1, hs2]), np64(k1[b:b + 1, g2:g2 + 1]),
+                                         np64(v1[b:b + 1, g2:g2 + 1]), ridx[None, None, :], [0])
+            assert np.max(np.abs(np64(out1[b:b + 1, hs2]) - r1)) <= 2e-2
