@@ -795,6 +795,10 @@ hipError_t spill_set_lds_gh() {
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)spill_dyn_lds_cap(false));
   if (e != hipSuccess) return e;
+  // the dense pass with long splits asks for the one-workgroup-per-CU floor
+  e = hipFuncSetAttribute((const void*)k_decode_splitk_slots<G, false, false, false, HALF>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSpillMinLds);
+  if (e != hipSuccess) return e;
   return hipFuncSetAttribute((const void*)k_decode_splitk_slots<G, false, true, true, HALF>,
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)spill_dyn_lds_cap(true));
 }
@@ -865,6 +869,8 @@ size_t decode_splitk_dyn_lds(int dtype, int G, bool gather, bool spill, bool pag
     bytes += spill_lds_bytes(G, kps);
     if (bytes < kSpillMinLds) bytes = kSpillMinLds;   // one spilling workgroup per CU
   }
+  if (!spill && !gather && !paged && dtype != 0 && kps >= kDenseOneWgKeys && bytes < kSpillMinLds)
+    bytes = kSpillMinLds;   // long dense splits: one workgroup per CU too
   return bytes;
 }
 

@@ -114,6 +114,11 @@ constexpr size_t kSpillMaxLds = 66 * 1024 + 1024;
 // Measured against two per CU: 131072 keys x 4 batches 407 -> 386 us per
 // anchor layer, 32768 x 1 49.7 -> 49.2 us, identical results.
 constexpr size_t kSpillMinLds = 80 * 1024;
+// The dense (no spill, no list) pass takes the same floor when its splits
+// are long (at least kDenseOneWgKeys keys, i.e. many rows of long context):
+// 131072 keys x 4 batches 334 -> 316 us; at 32768 x 1 (short splits) one
+// workgroup per CU was slower, so short splits keep two or more.
+constexpr int kDenseOneWgKeys = 4096;
 size_t spill_lds_bytes(int G, int keys_per_split);
 int spill_max_keys(int G);
 hipError_t decode_set_max_lds();

@@ -82,6 +82,8 @@ DENSE_CASES = [
     (torch.float32, 1, 4, 2, 64, 1024), (torch.float32, 2, 8, 8, 64, 257),
     (torch.float32, 1, 8, 1, 64, 1), (torch.bfloat16, 1, 32, 8, 128, 4099),
     (torch.bfloat16, 3, 16, 2, 128, 700), (torch.bfloat16, 1, 8, 1, 128, 70000),
+    # long splits (4096 keys): the dense pass's one-workgroup-per-CU launch
+    (torch.bfloat16, 2, 16, 8, 128, 131072),
 ]
 
 
