@@ -296,23 +296,24 @@ int decode_splits_target(int64_t n_keys, int64_t rows, int64_t target, int64_t m
   return (int)((n_keys + kps - 1) / kps);
 }
 
-int64_t decode_max_kps(const kascade_shape* s, bool spill) {
-  return spill && s->dtype != KASCADE_F32 ? spill_max_keys(s->n_q_heads / s->n_kv_heads)
+int64_t decode_max_kps(const kascade_shape* s, bool spill, bool paged) {
+  return spill && s->dtype != KASCADE_F32 ? spill_max_keys(s->n_q_heads / s->n_kv_heads, paged)
                                           : kPlanMaxKeys;
 }
 
 // target > 0: the split count of decode_splits_target for that many
 // workgroups (max_kps_target keys at most), else the slot-based rule.
 DecodePlan plan_decode(const kascade_shape* s, int n_keys, bool spill, bool pooled_ws,
-                       int slots, int64_t target = 0, int64_t max_kps_target = 0) {
+                       int slots, int64_t target = 0, int64_t max_kps_target = 0, bool paged = false) {
   DecodePlan p;
   const int64_t rows = (int64_t)s->batch * s->n_kv_heads;
-  const int64_t max_kps = decode_max_kps(s, spill);
+  const int64_t max_kps = decode_max_kps(s, spill, paged);
   p.splits = target > 0 ? decode_splits_target(n_keys, rows, target, max_kps_target, &p.kps)
                         : decode_splits(n_keys, rows, slots, max_kps, &p.kps);
-  // the workspace always has room for the largest plan
+  // the workspace always has room for the largest plan: the most splits come
+  // with the smaller (paged) split cap, so a workspace sized here serves both
   int kps_max = 0;
-  const int splits_ws = decode_splits(n_keys, rows, 0, max_kps, &kps_max);
+  const int splits_ws = decode_splits(n_keys, rows, 0, decode_max_kps(s, spill, true), &kps_max);
   const int splits_room = splits_ws > p.splits ? splits_ws : p.splits;
   const int64_t BH = (int64_t)s->batch * s->n_q_heads;
   size_t off = 0;
@@ -360,13 +361,13 @@ int plan_decode_dev(DeviceInfo* d, const kascade_shape* s, int n_keys, bool gath
     return KASCADE_OK;
   }
   int slots = 0, st;
-  if ((st = splitk_slots(d, s->dtype, G, gather, spill, paged, (int)decode_max_kps(s, spill),
+  if ((st = splitk_slots(d, s->dtype, G, gather, spill, paged, (int)decode_max_kps(s, spill, paged),
                          &slots)))
     return st;
-  *p = plan_decode(s, n_keys, spill, pooled_ws, slots);
+  *p = plan_decode(s, n_keys, spill, pooled_ws, slots, 0, 0, paged);
   int slots2 = 0;
   if ((st = splitk_slots(d, s->dtype, G, gather, spill, paged, p->kps, &slots2))) return st;
-  if (slots2 > slots) *p = plan_decode(s, n_keys, spill, pooled_ws, slots2);
+  if (slots2 > slots) *p = plan_decode(s, n_keys, spill, pooled_ws, slots2, 0, 0, paged);
   return KASCADE_OK;
 }
 
@@ -532,7 +533,7 @@ static int anchor_decode_impl(const kascade_shape* s, const kascade_paged_kv* pg
   if ((st = device_setup(&dev))) return st;
   DecodePlan p;
   if ((st = plan_decode_dev(dev, s, s->ctx_len, false, true, true, pg != nullptr, &p))) return st;
-  if (p.kps > decode_max_kps(s, true)) return KASCADE_ERR_SHAPE;   // LDS score buffer
+  if (p.kps > decode_max_kps(s, true, pg != nullptr)) return KASCADE_ERR_SHAPE;   // LDS score buffer
   char* w = reinterpret_cast<char*>(ws);
   DecodeArgs a = decode_args(s, q, k, v, s->ctx_len, p, w);
   set_paged(a, s, pg);

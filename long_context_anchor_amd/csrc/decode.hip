@@ -785,7 +785,8 @@ hipError_t splitk_attrs_g(int G, bool gather, bool spill, bool paged, int* block
 // longest split (or the one-workgroup-per-CU floor), plus the row list when
 // the cache is paged.
 inline size_t spill_dyn_lds_cap(bool paged) {
-  const size_t scores = kSpillMaxLds > kSpillMinLds ? kSpillMaxLds : kSpillMinLds;
+  const size_t most = paged ? kSpillMaxLds : kSpillMaxLdsOne;
+  const size_t scores = most > kSpillMinLds ? most : kSpillMinLds;
   return scores + (paged ? (kPlanMaxKeys + kListPad) * sizeof(int32_t) : 0);
 }
 
@@ -843,9 +844,11 @@ size_t spill_lds_bytes(int G, int keys_per_split) {
   return (size_t)G * (size_t)(keys_per_split + kSpillPad) * sizeof(float);
 }
 
-int spill_max_keys(int G) {
-  const int k = (int)(kSpillMaxLds / ((size_t)G * sizeof(float))) - kSpillPad;
-  return (k < kPlanMaxKeys ? k : kPlanMaxKeys) & ~15;
+int spill_max_keys(int G, bool paged) {
+  const size_t lds = paged ? kSpillMaxLds : kSpillMaxLdsOne;
+  const int cap = paged ? kPlanMaxKeys : kSpillMaxKeysOne;
+  const int k = (int)(lds / ((size_t)G * sizeof(float))) - kSpillPad;
+  return (k < cap ? k : cap) & ~15;
 }
 
 hipError_t decode_set_max_lds() {

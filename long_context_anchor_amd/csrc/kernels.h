@@ -105,9 +105,17 @@ struct PrefillArgs {
 constexpr int kMaxGatherKeys = 16384;
 constexpr int kPlanMaxKeys = 4096;
 
-// A bf16 anchor split keeps its scores in LDS until it ends: at most
-// kSpillMaxLds bytes of them, i.e. spill_max_keys(G) keys per split.
+// A 16-bit anchor split keeps its scores in LDS until it ends: over a paged
+// cache at most kSpillMaxLds bytes of them, i.e. spill_max_keys(G, true)
+// keys per split.
 constexpr size_t kSpillMaxLds = 66 * 1024 + 1024;
+// Over a contiguous cache a spilling workgroup runs alone on its CU (the
+// floor below), so its score buffer may take most of the CU's LDS: up to
+// kSpillMaxLdsOne bytes, i.e. 8192 keys per split for groups of up to 4
+// (4336 for 8).  A paged split also stages its row list and keeps the
+// smaller kSpillMaxLds.
+constexpr size_t kSpillMaxLdsOne = 136 * 1024;
+constexpr int kSpillMaxKeysOne = 8192;
 // A 16-bit spilling workgroup asks for at least kSpillMinLds bytes of
 // dynamic LDS: with its static LDS that is more than half of a CU's 160 KiB,
 // so one spilling workgroup runs per CU (the planner's slot count sees it).
@@ -120,7 +128,7 @@ constexpr size_t kSpillMinLds = 80 * 1024;
 // workgroup per CU was slower, so short splits keep two or more.
 constexpr int kDenseOneWgKeys = 4096;
 size_t spill_lds_bytes(int G, int keys_per_split);
-int spill_max_keys(int G);
+int spill_max_keys(int G, bool paged);
 hipError_t decode_set_max_lds();
 // Split-K kernel variant: workgroups per CU without dynamic LDS, its static
 // LDS, and the dynamic LDS of a split of kps keys.
