@@ -222,3 +222,68 @@ def test_oracle_rejects_non_finite():
         oracle.dense_decode(q, k, k)
     with pytest.raises(ValueError):
         oracle.topk_full_sort(np.array([1.0, np.inf]), 1)
+
+
+def _planted_stack(seed=21):
+    """A 5-layer decode stack, anchors [0, 3], 2 KV heads of 2 query heads,
+    whose anchors each put nearly all attention on one known key per KV head.
+
+    Every query is e_0 and anchor layer a's KV head c has key 40 e_0 at
+    position pos[a][c] (the other keys are below 0.05 in every entry), so the
+    pooled row's unique maximum is pos[a][c]."""
+    r = np.random.default_rng(seed)
+    L, B, Hq, Hkv, d, N = 5, 1, 4, 2, 8, 16
+    anchors = [0, 3]
+    pos = {0: [5, 11], 3: [2, 14]}
+    maps = {1: [1, 0], 2: [0, 0], 4: [1, 1]}
+    layers = []
+    for l in range(L):
+        q = np.zeros((B, Hq, d))
+        q[..., 0] = 1.0
+        k = r.uniform(-0.05, 0.05, (B, Hkv, N, d))
+        v = r.standard_normal((B, Hkv, N, d))
+        if l in anchors:
+            for c in range(Hkv):
+                k[0, c, pos[l][c]] = 0.0
+                k[0, c, pos[l][c], 0] = 40.0
+        layers.append({"q": q, "k": k, "v": v})
+    return layers, anchors, maps, pos
+
+
+def test_layer_stack_with_one_selected_key_is_closed_form():
+    """Layer stack ([Explainer] "アンカーレイヤーと再利用レイヤー": a reuse layer
+    attends only to the keys its nearest preceding anchor selected;
+    "ヘッドリマッピング": reuse KV head g takes anchor KV head head_map[g]'s list
+    and its own K/V).  With k = 1 a reuse layer's output for query head h is
+    exactly the row of ITS OWN V at the one selected position:
+      layer 1 (anchor 0, map [1,0]): head g -> v_1[g][pos[0][1-g]]
+      layer 2 (anchor 0, map [0,0]): both heads -> v_2[g][pos[0][0]]
+      layer 4 (anchor 3, map [1,1]): both heads -> v_4[g][pos[3][1]]."""
+    layers, anchors, maps, pos = _planted_stack()
+    outs, idx = oracle.run_decode_layerstack(layers, anchors, maps, topk=1)
+    assert sorted(idx) == anchors
+    for a in anchors:
+        assert idx[a][0, :, 0].tolist() == pos[a]
+    want_pos = {1: [pos[0][1], pos[0][0]], 2: [pos[0][0], pos[0][0]], 4: [pos[3][1], pos[3][1]]}
+    for l, wp in want_pos.items():
+        v = layers[l]["v"]
+        for h in range(4):
+            g = h // 2
+            assert np.max(np.abs(outs[l][0, h] - v[0, g, wp[g]])) == 0.0, (l, h)
+    # anchors are exact dense attention (torch SDPA in fp64)
+    for a in anchors:
+        lay = layers[a]
+        ref = _sdpa(lay["q"][:, :, None, :], lay["k"], lay["v"], 2)[:, :, 0, :]
+        assert np.max(np.abs(outs[a] - ref)) < 1e-12
+
+
+def test_layer_stack_with_full_lists_is_dense_everywhere():
+    """k = N: every reuse layer's list is the whole cache, so every layer of
+    the stack equals dense attention of its own q, k, v (torch SDPA)."""
+    layers, anchors, maps, _ = _planted_stack(seed=22)
+    for lay in layers:
+        lay["q"] = _rand(lay["q"].shape, 23)
+    outs, _ = oracle.run_decode_layerstack(layers, anchors, maps, topk=16)
+    for l, lay in enumerate(layers):
+        ref = _sdpa(lay["q"][:, :, None, :], lay["k"], lay["v"], 2)[:, :, 0, :]
+        assert np.max(np.abs(outs[l] - ref)) < 1e-12, l

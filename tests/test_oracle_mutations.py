@@ -247,6 +247,76 @@ def test_dp_segment_served_by_next_anchor_is_caught():
     check([tc.test_dp_matches_brute_force], coverage_score=coverage_score)
 
 
+# ---------------------------------------------------------------------------
+# tile Top-k and the decode layer stack
+# ---------------------------------------------------------------------------
+
+def _tile_topk_variant(k_of_tile=None, pad=-1, kmax_tile=None):
+    """tile_topk with one step changed (the rest as in the oracle)."""
+    def tile_topk(pooled_rows, n, tile=128, pct=10, round_to=64, k_min=256):
+        B, T, Hkv = len(pooled_rows), len(pooled_rows[0]), len(pooled_rows[0][0])
+        kt = (lambda t: ko.prefill_tile_k(t, n, tile, pct, round_to, k_min)[1])
+        k_max = kt(T - 1 if kmax_tile is None else kmax_tile(T))
+        idx = np.full((B, T, Hkv, k_max), pad, dtype=np.int64)
+        for b in range(B):
+            for t in range(T):
+                k_t = min(kt(t if k_of_tile is None else k_of_tile(t)), k_max)
+                for g in range(Hkv):
+                    idx[b, t, g, :k_t] = ko.topk_full_sort(pooled_rows[b][t][g], k_t)
+        return idx
+    return tile_topk
+
+
+TILE_PINS = [tt.test_tile_topk_brute_force_per_tile_k_and_padding,
+             tt.test_tile_topk_k_max_comes_from_the_last_tile]
+
+
+def test_tile_topk_with_next_tiles_k_is_caught():
+    check(TILE_PINS, tile_topk=_tile_topk_variant(k_of_tile=lambda t: t + 1))   # planted: k_{t+1}
+
+
+def test_tile_topk_without_minus_one_padding_is_caught():
+    check(TILE_PINS, tile_topk=_tile_topk_variant(pad=0))                       # planted: 0 padding
+
+
+def test_tile_topk_k_max_from_first_tile_is_caught():
+    check(TILE_PINS, tile_topk=_tile_topk_variant(kmax_tile=lambda T: 0))       # planted: k_max = k_0
+
+
+def _stack_variant(anchor_rule=None, own_map=False, anchor_values=False):
+    """run_decode_layerstack with one step changed."""
+    def run_decode_layerstack(layers, anchors, head_maps, topk, scale=None):
+        outs, idx_by_anchor = [], {}
+        for l, lay in enumerate(layers):
+            if l in anchors:
+                out, _, _, idx = ko.anchor_decode(lay["q"], lay["k"], lay["v"], topk, scale)
+                idx_by_anchor[l] = idx
+            else:
+                a = ko.anchor_of(l, anchors) if anchor_rule is None else anchor_rule(l, anchors)
+                hm = list(range(len(head_maps[l]))) if own_map else head_maps[l]
+                v = layers[a]["v"] if anchor_values else lay["v"]
+                out = ko.reuse_decode(lay["q"], lay["k"], v, idx_by_anchor[a], hm, scale)
+            outs.append(out)
+        return outs, idx_by_anchor
+    return run_decode_layerstack
+
+
+STACK_PINS = [ta.test_layer_stack_with_one_selected_key_is_closed_form,
+              ta.test_layer_stack_with_full_lists_is_dense_everywhere]
+
+
+def test_layer_stack_reusing_the_first_anchor_is_caught():
+    check(STACK_PINS, run_decode_layerstack=_stack_variant(anchor_rule=lambda l, A: A[0]))
+
+
+def test_layer_stack_ignoring_the_head_map_is_caught():
+    check(STACK_PINS, run_decode_layerstack=_stack_variant(own_map=True))
+
+
+def test_layer_stack_with_the_anchors_values_is_caught():
+    check(STACK_PINS, run_decode_layerstack=_stack_variant(anchor_values=True))
+
+
 def test_every_planted_mistake_is_restored():
     for name, fn in ORIG.items():
         assert getattr(ko, name) is fn

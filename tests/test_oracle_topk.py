@@ -92,3 +92,55 @@ def test_index_set_acceptance_rule():
     assert oracle.index_sets_agree([0, 1, 2], ref, s)[0]  # 2 and 3 are within 1e-5
     assert not oracle.index_sets_agree([0, 1, 4], ref, s)[0]
     assert not oracle.index_sets_agree([0, 1], ref, s)[0]
+
+
+def _brute_best_subset(s, k):
+    """The k-subset of positions with the largest total, by enumeration (the
+    maximiser is unique for rows of distinct values)."""
+    best, best_set = -np.inf, None
+    for c in itertools.combinations(range(len(s)), k):
+        tot = s[list(c)].sum()
+        if tot > best:
+            best, best_set = tot, c
+    return list(best_set)
+
+
+def test_tile_topk_brute_force_per_tile_k_and_padding():
+    """Tile Top-k ([Explainer] "Top-k設定", eq. k, with the query tiles of
+    "実装のポイント"): each pooled row (b, t, g) of prefix length P_t keeps its
+    best k_t-subset, ascending, then -1 up to k_max, the k of the LAST tile.
+
+    Rule {tile 4, pct 50, round_to 2, k_min 3} over a 20-token prompt makes
+    every tile's k different; by hand from eq. k:
+      P_t = 4, 8, 12, 16, 20
+      50% of P_t rounded to the nearest even number = 2, 4, 6, 8, 10
+      at least 3, at most P_t -> k_t = 3, 4, 6, 8, 10 and k_max = 10."""
+    n, tile = 20, 4
+    want_P = [4, 8, 12, 16, 20]
+    want_k = [3, 4, 6, 8, 10]
+    r = np.random.default_rng(11)
+    B, Hkv = 1, 2
+    rows = [[[r.permutation(P).astype(np.float64) + r.random(P) * 0.5 for _ in range(Hkv)]
+             for P in want_P] for _ in range(B)]
+    idx = oracle.tile_topk(rows, n, tile=tile, pct=50, round_to=2, k_min=3)
+    assert idx.shape == (B, len(want_P), Hkv, 10)
+    for b in range(B):
+        for t, (P, k_t) in enumerate(zip(want_P, want_k)):
+            for g in range(Hkv):
+                got = idx[b, t, g]
+                assert got[:k_t].tolist() == _brute_best_subset(rows[b][t][g], k_t), (t, g)
+                assert (got[k_t:] == -1).all(), (t, g)
+                assert (got[:k_t] < P).all()
+
+
+def test_tile_topk_k_max_comes_from_the_last_tile():
+    """With a prompt that ends mid-tile, the last tile's prefix is the whole
+    prompt: 10 tokens in tiles of 4 under {pct 50, round_to 2, k_min 1} give
+    P_t = 4, 8, 10 and k_t = 2, 4, 6 (by hand), so rows are padded to 6."""
+    r = np.random.default_rng(12)
+    rows = [[[r.random(P) for _ in range(1)] for P in (4, 8, 10)]]
+    idx = oracle.tile_topk(rows, 10, tile=4, pct=50, round_to=2, k_min=1)
+    assert idx.shape == (1, 3, 1, 6)
+    for t, k_t in enumerate((2, 4, 6)):
+        assert idx[0, t, 0, :k_t].tolist() == _brute_best_subset(rows[0][t][0], k_t)
+        assert (idx[0, t, 0, k_t:] == -1).all()
