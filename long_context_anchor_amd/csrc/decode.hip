@@ -19,6 +19,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "paged.h"
 
 namespace kc {
 
@@ -359,14 +360,11 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
     const int32_t* list = a.idx + (int64_t)b * a.idx_sb + (int64_t)a.hm.m[g] * a.idx_sg;
     for (int i = tid; i < k1 - k0; i += kThreads) {
       int j = GATHER ? list[k0 + i] : k0 + i;
-      if (PAGED) {
-        // logical position -> physical row (positions and blocks clamped so a
-        // bad list or table cannot fault)
-        j = min(max(j, 0), a.n_ctx - 1);
-        const int blk = min(max(a.table[(int64_t)b * a.table_stride + (j >> a.blk_shift)], 0),
-                            a.num_blocks - 1);
-        j = (int)((uint32_t)blk * (uint32_t)a.blk_rows + (uint32_t)(j & ((1 << a.blk_shift) - 1)));
-      }
+      // logical position -> physical row (positions and blocks clamped so a
+      // bad list or table cannot fault)
+      if (PAGED)
+        j = (int)paged_row(a.table, a.table_stride, b, j, a.n_ctx, a.blk_shift, a.num_blocks,
+                           (uint32_t)a.blk_rows);
       s_list[i] = j;
     }
     // a step may read up to 15 entries past the split's rows: make them row 0
@@ -389,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
       ((PAGED ? 0 : (int64_t)b * a.kv_sb) + (int64_t)g * a.kv_sh) * (int64_t)sizeof(uint16_t);
   // last valid row: head g's rows of the last block end at row bs-1 (the
   // head offset is added to every row address)
-  const uint32_t max_row = PAGED ? (uint32_t)((a.num_blocks - 1) * a.blk_rows + ((1 << a.blk_shift) - 1))
+  const uint32_t max_row = PAGED ? paged_max_row(a.num_blocks, (uint32_t)a.blk_rows, a.blk_shift)
                                  : (uint32_t)(a.n_ctx - 1);
   const char* kbase = reinterpret_cast<const char*>(a.k) + head_off;
   const char* vbase = reinterpret_cast<const char*>(a.v) + head_off;

@@ -29,6 +29,7 @@
 //     one key column and the pooled column sum is an in-lane sum.
 #include "common.h"
 #include "kernels.h"
+#include "paged.h"
 
 namespace kc {
 
@@ -241,12 +242,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const Pr
       slist[i] = lp;
       if (PAGED) {
         // block clamped into the cache so a bad table cannot fault
-        uint32_t phys = 0;
-        if (lp >= 0) {
-          const int blk = min(max(a.table[(int64_t)b * a.table_stride + (lp >> a.blk_shift)], 0),
-                              a.num_blocks - 1);
-          phys = (uint32_t)blk * a.blk_rows + (uint32_t)(lp & ((1 << a.blk_shift) - 1));
-        }
+        const uint32_t phys =
+            lp >= 0 ? paged_row(a.table, a.table_stride, b, lp, N, a.blk_shift, a.num_blocks, a.blk_rows)
+                    : 0u;
         sphys[i] = (int32_t)phys;
       }
     }
