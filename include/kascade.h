@@ -16,7 +16,9 @@
  *             passed to the kernels by value) and the shape/rule structs.
  * Ownership.  The caller allocates and frees every buffer, including the
  *             workspace (size from kascade_workspace_bytes).  The library
- *             never allocates device memory, never frees, never synchronises.
+ *             never allocates device memory, never frees, and never
+ *             synchronises (kascade_kernel_timer_read, a benchmark helper,
+ *             is the one call that waits for recorded events).
  * Streams.    Work is enqueued asynchronously on `stream` (0 = null stream).
  * Layouts.    K and V caches are addressed through the element strides in
  *             kascade_shape (rows of d contiguous elements, 16-byte aligned;
@@ -279,9 +281,11 @@ int kascade_dense_prefill(const kascade_shape* shape, const void* q, const void*
 
 /* Per-kernel timing with HIP events recorded on the launching stream around
  * every launch of kernel `kernel_id` (ids below) while enabled.  enable()
- * resets the totals; read() waits for the recorded events and returns the
- * summed milliseconds and the launch count.  Not thread-safe; meant for
- * benchmarks. */
+ * resets the totals; read() waits for the recorded events (it is the only
+ * call that waits) and returns the summed milliseconds and the launch
+ * count.  Launch calls never wait: the event pool grows on the host as
+ * needed.  Launches on a stream under graph capture are not timed.  Not
+ * thread-safe (one timing thread at a time); meant for benchmarks. */
 enum {
   KASCADE_K_DECODE_SPLITK = 0, KASCADE_K_DECODE_COMBINE = 1, KASCADE_K_DECODE_POOL = 2,
   KASCADE_K_TOPK_SELECT = 3, KASCADE_K_REUSE_DECODE = 4, KASCADE_K_PREFILL_FLASH = 5,

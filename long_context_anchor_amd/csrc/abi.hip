@@ -116,6 +116,11 @@ int splitk_slots(DeviceInfo* d, int dtype, int G, bool gather, bool spill, bool 
 }
 
 // ---- per-kernel event timing ------------------------------------------------
+// Events are recorded around the launches of an enabled kernel; they are only
+// waited for in kascade_kernel_timer_read, never in a launch call: when the
+// pool is used up it grows (event creation is a host call and does not wait
+// for the device).  A launch on a stream that is being captured into a graph
+// is not timed (the events would become graph nodes).
 struct Timer {
   std::atomic<bool> on{false};   // read by every launch, from any thread
   double total_ms = 0.0;
@@ -125,6 +130,20 @@ struct Timer {
 };
 Timer g_timer[KASCADE_K_COUNT];
 constexpr size_t kTimerPairs = 256;
+
+hipError_t timer_grow(Timer& t) {
+  const size_t old = t.pool.size();
+  t.pool.resize(old + 2 * kTimerPairs, nullptr);
+  for (size_t i = old; i < t.pool.size(); ++i) {
+    hipError_t e = hipEventCreate(&t.pool[i]);
+    if (e != hipSuccess) {
+      for (size_t j = old; j < i; ++j) (void)hipEventDestroy(t.pool[j]);
+      t.pool.resize(old);
+      return e;
+    }
+  }
+  return hipSuccess;
+}
 
 hipError_t timer_drain(Timer& t) {
   for (size_t i = 0; i < t.used; ++i) {
@@ -144,8 +163,11 @@ template <typename F>
 hipError_t timed(int id, hipStream_t s, F&& launch) {
   Timer& t = g_timer[id];
   if (!t.on.load(std::memory_order_relaxed)) return launch();
-  if (t.used == kTimerPairs) {
-    hipError_t e = timer_drain(t);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+    return launch();
+  if (2 * (t.used + 1) > t.pool.size()) {
+    hipError_t e = timer_grow(t);
     if (e != hipSuccess) return e;
   }
   hipEvent_t b = t.pool[2 * t.used], en = t.pool[2 * t.used + 1];
@@ -951,14 +973,8 @@ int kascade_kernel_timer_enable(int id, int enable) {
   Timer& t = g_timer[id];
   if (enable) {
     if (t.pool.empty()) {
-      t.pool.resize(2 * kTimerPairs);
-      for (auto& ev : t.pool) {
-        hipError_t e = hipEventCreate(&ev);
-        if (e != hipSuccess) {
-          t.pool.clear();
-          return hip_status(e);
-        }
-      }
+      hipError_t e = timer_grow(t);
+      if (e != hipSuccess) return hip_status(e);
     }
     t.used = 0;
     t.total_ms = 0.0;
