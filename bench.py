@@ -103,6 +103,27 @@ def build_decode(workload, torch, K, synth, configs, dtype="bf16"):
                 bytes_reuse=bytes_reuse, bytes_dense=bytes_dense, layers=layers, maps=maps)
 
 
+def prefill_reuse_flops(torch, K, idx_by_anchor, anchor_of, maps, layers_reuse, N, n_kv, group, d):
+    """4*d*sum_{h,r} |J_{h,r}| over the reuse layers, counted from the anchors' tile lists."""
+    rule = K.PREFILL_RULE
+    T = N // rule.tile
+    rows = torch.arange(N, device="cuda", dtype=torch.int64).view(T, rule.tile)
+    per_anchor = {}
+    for a, ix in idx_by_anchor.items():
+        cnt = torch.zeros(n_kv, dtype=torch.float64, device="cuda")
+        for t in range(T):
+            kt = K.kascade_topk_for_len(min(N, rule.tile * (t + 1)), rule)
+            lst = ix[0, t, :, :kt].to(torch.int64).contiguous()        # [Hkv, kt]
+            c = torch.searchsorted(lst, rows[t].expand(n_kv, -1).contiguous(), right=True)
+            cnt += c.sum(dim=1).double()
+        per_anchor[a] = cnt.cpu().numpy()
+    total = 0.0
+    for l in layers_reuse:
+        c = per_anchor[anchor_of[l]]
+        total += sum(c[int(maps[l][g])] for g in range(n_kv)) * group
+    return 4.0 * d * total
+
+
 def build_prefill(torch, K, synth, configs, dtype="bf16"):
     cfg = dataclasses.replace(configs.LLAMA_PREFILL_32K, dtype=dtype)
     N, L = cfg.ctx_len, cfg.n_layers
@@ -142,43 +163,132 @@ def build_prefill(torch, K, synth, configs, dtype="bf16"):
     d, Hq = cfg.head_dim, cfg.n_q_heads
     flops_flash = 4.0 * d * Hq * N * (N + 1) / 2
     flops_pool = 2.0 * d * Hq * N * (N + 1) / 2
+    reuse_layers = [l for l in range(L) if l not in cfg.anchors]
 
     def reuse_flops():
-        # 4*d*sum_{h,r} |J_{h,r}|, counted from the anchors' lists
-        total = 0.0
-        rows = torch.arange(N, device="cuda", dtype=torch.int64).view(T, rule.tile)
-        per_anchor = {}
-        for a, ix in idx.items():
-            cnt = torch.zeros(cfg.n_kv_heads, dtype=torch.float64, device="cuda")
-            for t in range(T):
-                P = min(N, rule.tile * (t + 1))
-                kt = K.kascade_topk_for_len(P, rule)
-                lst = ix[0, t, :, :kt].to(torch.int64).contiguous()        # [Hkv, kt]
-                c = torch.searchsorted(lst, rows[t].expand(cfg.n_kv_heads, -1).contiguous(), right=True)
-                cnt += c.sum(dim=1).double()
-            per_anchor[a] = cnt.cpu().numpy()
-        for l in range(L):
-            if l in cfg.anchors:
-                continue
-            c = per_anchor[anchor_of[l]]
-            total += sum(c[int(maps[l][g])] for g in range(cfg.n_kv_heads)) * cfg.group
-        return 4.0 * d * total
+        return prefill_reuse_flops(torch, K, idx, anchor_of, maps, reuse_layers, N, cfg.n_kv_heads,
+                                   cfg.group, d)
 
     return dict(cfg=cfg, run=run, n_anchor=len(cfg.anchors), n_reuse=L - len(cfg.anchors),
-                flops_flash=flops_flash, flops_pool=flops_pool, reuse_flops=reuse_flops)
+                flops_flash=flops_flash, flops_pool=flops_pool, reuse_flops=reuse_flops,
+                layers=layers, maps=maps)
+
+
+def build_qwen3(torch, K, synth, configs, dtype="bf16"):
+    """The Qwen3-8B-shaped end-to-end workload: 36 layers (32 query / 8 KV
+    heads, d 128), 6 anchors chosen by the library's DP on the seeded
+    similarity matrix, many-to-one head maps; a 65536-token causal prefill
+    through every layer, then 512 generated tokens whose K/V rows sit in
+    caches of 66048 rows (decode step s sees the first 65537 + s rows; its
+    row was written at set-up, which leaves every step's inputs as if it had
+    been appended)."""
+    cfg = dataclasses.replace(configs.QWEN3_E2E_64K, dtype=dtype)
+    L, Hq, Hkv, d, G = cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.group
+    N0, steps = cfg.ctx_len, cfg.decode_steps
+    n_max = N0 + steps
+    S = synth.similarity_matrix(cfg.seed, L)
+    anchors, _ = K.kascade_select_anchors(L, cfg.n_anchor_dp, S)
+    maps = synth.head_maps(cfg.seed, L, anchors, Hkv, cfg.head_map_kind)
+    lin = synth.heavy_lineages(cfg.seed, L, Hkv, N0, cfg.heavy, cfg.drift)
+    anchor_of = {l: max(a for a in anchors if a <= l) for l in range(L)}
+    layers, qs = [], [[None] * L for _ in range(steps)]
+    for l in range(L):
+        q, k, v = synth.prefill_layer(cfg.seed, l, 1, Hq, Hkv, d, N0,
+                                      synth.layer_heavy_sets(lin, l, anchors, maps),
+                                      cfg.alpha, cfg.gamma, cfg.dtype, device="cuda", n_max=n_max)
+        u = synth.prefill_directions(cfg.seed, l, Hkv, d, device="cuda")
+        for st in range(steps):
+            qd, kr, vr = synth.decode_step(cfg.seed, l, st, 1, Hq, Hkv, d, u, cfg.gamma, cfg.dtype,
+                                           device="cuda")
+            k[:, :, N0 + st] = kr
+            v[:, :, N0 + st] = vr
+            qs[st][l] = qd
+        layers.append((q, k, v))
+    rule = K.PREFILL_RULE
+    sh = K.make_shape(layers[0][0], layers[0][1], N0)
+    ws_p = K.workspace(K.OP_ANCHOR_PREFILL, sh, 0, rule)
+    T = N0 // rule.tile
+    kmax = K.kascade_topk_for_len(N0, rule)
+    tidx = {a: torch.empty((1, T, Hkv, kmax), dtype=torch.int32, device="cuda") for a in anchors}
+    out_p = torch.empty_like(layers[0][0])
+
+    def prefill(kind=None):
+        for l, (q, k, v) in enumerate(layers):
+            if l in anchors:
+                if kind in (None, "anchor"):
+                    K.check(K.kascade_anchor_prefill(sh, q, k, v, rule, out_p, None, tidx[l], None, ws_p,
+                                                     ws_p.numel()), "anchor_prefill")
+            elif kind in (None, "reuse"):
+                K.check(K.kascade_reuse_prefill(sh, q, k, v, rule, tidx[anchor_of[l]], maps[l], out_p,
+                                                None, 0), "reuse_prefill")
+
+    dec_k = lambda n: K.kascade_topk_for_len(n, K.DECODE_RULE)
+    k_last = dec_k(n_max)
+    sh_max = K.make_shape(qs[0][0], layers[0][1], n_max)
+    ws_a = K.workspace(K.OP_ANCHOR_DECODE, sh_max, k_last)
+    ws_r = K.workspace(K.OP_REUSE_DECODE, sh_max, k_last)
+    didx = {a: torch.empty((1, Hkv, k_last), dtype=torch.int32, device="cuda") for a in anchors}
+    out_d = torch.empty_like(qs[0][0])
+
+    def decode(st, kind=None):
+        n_cur = N0 + st + 1
+        kk = dec_k(n_cur)
+        for l, (_, k, v) in enumerate(layers):
+            shd = K.make_shape(qs[st][l], k, n_cur)
+            if l in anchors:
+                if kind in (None, "anchor"):
+                    K.check(K.kascade_anchor_decode(shd, qs[st][l], k, v, kk, out_d, None, didx[l], None,
+                                                    ws_a, ws_a.numel()), "anchor_decode")
+            elif kind in (None, "reuse"):
+                K.check(K.kascade_reuse_decode(shd, qs[st][l], k, v, kk, didx[anchor_of[l]], maps[l],
+                                               out_d, ws_r, ws_r.numel()), "reuse_decode")
+
+    reuse_layers = [l for l in range(L) if l not in anchors]
+
+    def reuse_flops():
+        return prefill_reuse_flops(torch, K, tidx, anchor_of, maps, reuse_layers, N0, Hkv, G, d)
+
+    return dict(cfg=cfg, anchors=anchors, S=S, prefill=prefill, decode=decode, steps=steps, N0=N0,
+                n_anchor=len(anchors), n_reuse=L - len(anchors), reuse_flops=reuse_flops, dec_k=dec_k)
 
 
 # ---------------------------------------------------------------------------
-# CPU oracle baseline on a bounded sample of the 32K decode workload
+# CPU oracle baseline on bounded samples (decode, prefill, anchor DP)
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(dec, torch):
-    import oracle
+def host_info():
+    """Host CPU model, the CPUs this process may run on and the BLAS threads."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = 1
+        blas = 1
+    return model, affinity, blas
+
+
+def cpu_baseline(dec, pre, torch):
+    """The oracle, as it stands, on bounded samples of the workloads.
+
+    value: 32K decode us/layer from one anchor and one reuse layer (weighted
+    by the layer counts).  Also: the 32K prefill on 16 sampled tiles of one
+    KV head (tiles 0, 1, 20, the last and 12 seeded others) of one anchor and
+    one reuse layer, extrapolated to every tile and KV head (labelled
+    extrapolated), and the anchor DP over the 36-layer similarity matrix."""
+    import oracle
+    model, affinity, blas = host_info()
     cfg = dec["cfg"]
     a = cfg.anchors[0]
     r = a + 1
@@ -189,7 +299,7 @@ def cpu_baseline(dec, torch):
     while True:
         _, _, _, ridx = oracle.anchor_decode(qa, ka, va, cfg.topk)
         reps_a += 1
-        if time.perf_counter() - t0 > 6.0:
+        if time.perf_counter() - t0 > 3.0:
             break
     t_anchor = (time.perf_counter() - t0) / reps_a
     t1 = time.perf_counter()
@@ -197,17 +307,76 @@ def cpu_baseline(dec, torch):
     while True:
         oracle.reuse_decode(qr, kr, vr, ridx, dec["maps"][r])
         reps_r += 1
-        if time.perf_counter() - t1 > 4.0:
+        if time.perf_counter() - t1 > 2.0:
             break
     t_reuse = (time.perf_counter() - t1) / reps_r
     L = cfg.n_layers
     per_layer = (dec["n_anchor"] * t_anchor + dec["n_reuse"] * t_reuse) / L
-    return {"value": per_layer * 1e6, "unit": "us/layer", "cores": int(threads), "kind": "oracle",
+    line = {"value": per_layer * 1e6, "unit": "us/layer", "cores": int(min(blas, affinity)),
+            "kind": "oracle",
             "sample": "32K-context decode: one anchor layer (%d reps) and one reuse layer (%d reps), "
-                      "weighted %d anchor : %d reuse layers; host %s, %d logical cpus" % (
-                          reps_a, reps_r, dec["n_anchor"], dec["n_reuse"], platform.processor() or
-                          platform.machine(), os.cpu_count() or 0),
+                      "weighted %d anchor : %d reuse layers" % (reps_a, reps_r, dec["n_anchor"],
+                                                                 dec["n_reuse"]),
+            "cpu_model": model, "affinity_cpus": affinity, "blas_threads": blas,
             "anchor_s": t_anchor, "reuse_s": t_reuse}
+    if pre is not None:
+        line["prefill32k"] = cpu_prefill_sample(pre, oracle)
+    S = pre["qwen3_S"] if pre is not None and "qwen3_S" in pre else None
+    if S is not None:
+        t2 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t2 < 0.5:
+            oracle.dp_select_anchors(S, 6)
+            reps += 1
+        line["anchor_dp_ms"] = (time.perf_counter() - t2) / reps * 1e3
+        line["anchor_dp_sample"] = "36-layer seeded similarity matrix, 6 anchors (%d reps)" % reps
+    return line
+
+
+def cpu_prefill_sample(pre, oracle):
+    cfg = pre["cfg"]
+    N, Hkv, G, tile = cfg.ctx_len, cfg.n_kv_heads, cfg.group, 128
+    T = N // tile
+    rng = np.random.default_rng(cfg.seed)
+    tiles = sorted(set([0, 1, 20, T - 1]) | set(int(x) for x in rng.choice(np.arange(2, T - 1), 12,
+                                                                            replace=False)))
+    a, r = cfg.anchors[0], cfg.anchors[0] + 1
+    g = 0
+    f64 = lambda t: t.float().cpu().numpy()
+    qa, ka, va = (f64(x[:, g * G:(g + 1) * G] if i == 0 else x[:, g:g + 1])
+                  for i, x in enumerate(pre["layers"][a]))
+    qr, kr, vr = (f64(x[:, g * G:(g + 1) * G] if i == 0 else x[:, g:g + 1])
+                  for i, x in enumerate(pre["layers"][r]))
+    lists = {}
+    t0 = time.perf_counter()
+    for t in tiles:
+        rows = range(tile * t, tile * (t + 1))
+        for hh in range(G):
+            oracle.dense_prefill_rows(qa, ka, va, 0, hh, rows)
+        pooled = oracle.tile_pool_one(qa, ka, 0, t, 0)
+        P, kt = oracle.prefill_tile_k(t, N)
+        lists[t] = oracle.topk_full_sort(pooled, kt)
+    t_anchor = time.perf_counter() - t0
+    kmax = oracle.prefill_tile_k(T - 1, N)[1]
+    idx = -np.ones((1, T, 1, kmax), dtype=np.int64)
+    for t in tiles:
+        idx[0, t, 0, :len(lists[t])] = lists[t]
+    t1 = time.perf_counter()
+    for t in tiles:
+        rows = range(tile * t, tile * (t + 1))
+        for hh in range(G):
+            oracle.sparse_prefill_rows(qr, kr, vr, idx, [0], 0, hh, rows)
+    t_reuse = time.perf_counter() - t1
+    scale = T * Hkv / len(tiles)
+    L = cfg.n_layers
+    na = len(cfg.anchors)
+    ms = (na * t_anchor * scale + (L - na) * t_reuse * scale) * 1e3
+    return {"value": ms, "unit": "ms (32 layers, extrapolated)", "kind": "oracle",
+            "extrapolated": True,
+            "sample": "%d tiles (%s) of KV head 0 of one anchor and one reuse layer, x %d tiles x %d "
+                      "KV heads / %d sampled" % (len(tiles), ",".join(map(str, tiles)), T, Hkv,
+                                                 len(tiles)),
+            "anchor_layer_s": t_anchor * scale, "reuse_layer_s": t_reuse * scale}
 
 
 # ---------------------------------------------------------------------------
@@ -217,7 +386,7 @@ def cpu_baseline(dec, torch):
 def kernel_source_hash(kernel):
     """sha256 over the sources a kernel is built from (its .hip and the shared headers)."""
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel], "common.h", "kernels.h"):
+    for f in (KERNEL_SOURCES[kernel], "common.h", "kernels.h", "paged.h"):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -499,14 +668,143 @@ def paged_prefill_row(torch, K, synth, configs, args):
 
 # ---------------------------------------------------------------------------
 
+def capture_graph(torch, fn):
+    """fn() (library calls on torch's current stream) captured as one HIP graph.
+    One eager run on the capture stream comes first, so the library's
+    once-per-device set-up happens outside the capture."""
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        fn()
+        with torch.cuda.graph(g, stream=st):
+            fn()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    return g
+
+
+def event_reps(torch, fn, reps):
+    """Milliseconds of each of `reps` runs of fn(), each bracketed by HIP events
+    on the current stream and followed by a synchronisation."""
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return np.asarray(ts)
+
+
+def pct(ts, scale=1.0):
+    """median, p10 and p90 of a sample, times `scale`."""
+    return {"median": float(np.median(ts)) * scale, "p10": float(np.percentile(ts, 10)) * scale,
+            "p90": float(np.percentile(ts, 90)) * scale, "n": int(len(ts))}
+
+
+def stream_copy_gbps(torch, nbytes=4 << 30, reps=10):
+    """Measured HBM copy bandwidth (bytes read + written per second) of torch's
+    device copy over a buffer far larger than the last-level cache."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ts = event_reps(torch, lambda: dst.copy_(src), reps)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * nbytes / (np.median(ts) * 1e-3) / 1e9
+
+
+def qwen3_bench(torch, K, synth, configs, args, reps):
+    """Config-5 figures: the 36-layer 64K prefill (eager; per kind over the
+    layers of that kind) and the 512 decode steps, each step one HIP graph,
+    replayed back to back; per-kind decode figures from graphs of the last
+    step's anchor or reuse layers."""
+    w = build_qwen3(torch, K, synth, configs, args.dtype)
+    cfg = w["cfg"]
+    L, Hq, Hkv, d = cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    N0, steps = w["N0"], w["steps"]
+    na, nr = w["n_anchor"], w["n_reuse"]
+    log("qwen3: anchors", w["anchors"])
+    w["prefill"]()
+    torch.cuda.synchronize()
+    pre = {}
+    for kind in (None, "anchor", "reuse"):
+        pre[kind] = event_reps(torch, lambda: w["prefill"](kind), 3)
+    rf = w["reuse_flops"]()
+    fl_anchor = 6.0 * d * Hq * N0 * (N0 + 1) / 2
+    anchor_ms = float(np.median(pre["anchor"])) / na
+    reuse_ms = float(np.median(pre["reuse"])) / nr
+    log("qwen3: prefill done, capturing %d decode steps" % steps)
+    graphs = [capture_graph(torch, lambda st=st: w["decode"](st)) for st in range(steps)]
+    for g in graphs[:8]:
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    passes = []
+    per_step = []
+    for _ in range(3):
+        ev[0].record()
+        for st, g in enumerate(graphs):
+            g.replay()
+            ev[st + 1].record()
+        torch.cuda.synchronize()
+        passes.append(ev[0].elapsed_time(ev[steps]))
+        per_step += [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    del graphs
+    last = steps - 1
+    n_last = N0 + steps
+    kind_us = {}
+    for kind, n in (("anchor", na), ("reuse", nr)):
+        g = capture_graph(torch, lambda kind=kind: w["decode"](last, kind))
+        kind_us[kind] = pct(event_reps(torch, g.replay, reps), 1e3 / n)
+        del g
+    k_last = w["dec_k"](n_last)
+    io = Hq * d * 2 * 2 + Hkv * k_last * 4
+    by_anchor = 2 * Hkv * n_last * d * 2 + io
+    by_reuse = 2 * Hkv * k_last * d * 2 + io
+    torch.cuda.synchronize()
+    res = {
+        "workload": "Qwen3-8B-shaped: 36 layers, 32q/8kv heads, d=128, %s; DP anchors %s; prefill %d tokens "
+                    "(tile 128, k_t min 256), then %d decode steps (k %d -> %d)" % (
+                        args.dtype, w["anchors"], N0, steps, w["dec_k"](N0 + 1), k_last),
+        "prefill_ms": float(np.median(pre[None])), "prefill_ms_runs": [float(x) for x in pre[None]],
+        "prefill_anchor_ms_per_layer": anchor_ms, "prefill_reuse_ms_per_layer": reuse_ms,
+        "prefill_anchor_TFLOPs": fl_anchor / (anchor_ms * 1e-3) / 1e12,
+        "prefill_anchor_mfma_frac": fl_anchor / (anchor_ms * 1e-3) / 1e12 / MFMA16_PEAK_TFLOPS,
+        "prefill_anchor_ideal_ms": fl_anchor / (MFMA16_PEAK_TFLOPS * 1e12) * 1e3,
+        "prefill_reuse_TFLOPs": rf / nr / (reuse_ms * 1e-3) / 1e12,
+        "prefill_reuse_mfma_frac": rf / nr / (reuse_ms * 1e-3) / 1e12 / MFMA16_PEAK_TFLOPS,
+        "prefill_reuse_ideal_ms": rf / nr / (MFMA16_PEAK_TFLOPS * 1e12) * 1e3,
+        "decode_ms_512_steps": float(np.median(passes)),
+        "decode_us_per_layer": pct(np.asarray(per_step), 1e3 / L),
+        "decode_anchor_us_last_step": kind_us["anchor"], "decode_reuse_us_last_step": kind_us["reuse"],
+        "decode_anchor_ideal_us": by_anchor / (HBM_PEAK_GBS * 1e9) * 1e6,
+        "decode_reuse_ideal_us": by_reuse / (HBM_PEAK_GBS * 1e9) * 1e6,
+        "decode_anchor_hbm_frac": by_anchor / (kind_us["anchor"]["median"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "decode_reuse_hbm_frac": by_reuse / (kind_us["reuse"]["median"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+    }
+    S = w["S"]
+    del w
+    torch.cuda.empty_cache()
+    return res, S
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--reps", type=int, default=50,
+                    help="repetitions of each section and kind for the median/p10/p90 figures")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode32k", "decode128k", "prefill"], default=None,
+    ap.add_argument("--no-qwen3", action="store_true",
+                    help="skip the Qwen3-shaped 64K prefill + 512-step decode component")
+    ap.add_argument("--only", choices=["decode32k", "decode128k", "prefill", "qwen3"], default=None,
                     help="run one section only (profiling)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the decode sections eagerly instead of replaying HIP graphs")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="one launch of each kernel plus a calibration copy, for rocprofv3 --pmc")
     ap.add_argument("--calibration", action="store_true",
@@ -539,6 +837,12 @@ def main():
     if args.paged:
         paged_bench(torch, K, synth, configs, args)
         return
+    reps = max(args.reps, 1)
+    if args.only == "qwen3":
+        res, _ = qwen3_bench(torch, K, synth, configs, args, reps)
+        print(json.dumps({"metric": METRIC, "config": {"workload": res["workload"]}, "qwen3_e2e": res}),
+              flush=True)
+        return
 
     sections = ["decode32k", "decode128k", "prefill"] if args.only is None else [args.only]
     log("building workloads", sections)
@@ -548,10 +852,30 @@ def main():
         work["decode32k"] = build_decode(configs.LLAMA_DECODE_32K, torch, K, synth, configs, args.dtype)
     if "decode128k" in sections:
         work["decode128k"] = build_decode(configs.LLAMA_DECODE_128K, torch, K, synth, configs, args.dtype)
-    if "prefill" in sections:
+    if "prefill" in sections or not args.no_cpu_baseline:
         work["prefill"] = build_prefill(torch, K, synth, configs, args.dtype)
     torch.cuda.synchronize()
     log("built in %.1f s" % (time.perf_counter() - t_build))
+
+    # decode sections run as HIP graphs of their 32 layers (one per kind as
+    # well), so their time is the GPU's and not the host's launch rate
+    graphs = {}
+    for s in ("decode32k", "decode128k"):
+        if s in sections:
+            w = work[s]
+            if args.eager:
+                graphs[s] = {kind: (lambda kind=kind, w=w: w["run"](kind))
+                             for kind in (None, "anchor", "reuse", "dense")}
+            else:
+                graphs[s] = {kind: capture_graph(torch, lambda kind=kind, w=w: w["run"](kind)).replay
+                             for kind in (None, "anchor", "reuse", "dense")}
+    log("decode graphs captured" if not args.eager else "eager decode")
+
+    def run_section(s):
+        if s == "prefill":
+            work["prefill"]["run"]()
+        else:
+            graphs[s][None]()
 
     def step():
         marks = {}
@@ -559,20 +883,23 @@ def main():
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
-            work[s]["run"]()
+            run_section(s)
             e1.record()
             marks[s] = (e0, e1)
+        torch.cuda.synchronize()   # step boundary
         return marks
 
     for i in range(args.warmup):
         step()
-        torch.cuda.synchronize()
         log("warmup step %d done" % i)
 
-    # pick the kernel with the largest share of one step, then time it live
+    # pick the kernel with the largest share of one eager step, then time it
+    # live with the library's events during the timed steps (prefill kernels
+    # run eagerly there; a decode kernel is timed over eager passes after them)
     for kid in range(8):
         K.kascade_kernel_timer_enable(kid, True)
-    step()
+    for s in sections:
+        work[s]["run"]()
     torch.cuda.synchronize()
     shares = {kid: K.kascade_kernel_timer_read(kid) for kid in range(8)}
     for kid in range(8):
@@ -586,11 +913,16 @@ def main():
     all_marks = [step() for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if dom < 5 and not args.eager:
+        dsec = "decode128k" if "decode128k" in sections else "decode32k"
+        for _ in range(max(1, min(args.steps, 10))):
+            work[dsec]["run"]()
+        torch.cuda.synchronize()
     dom_ms, dom_n = K.kascade_kernel_timer_read(dom)
     K.kascade_kernel_timer_enable(dom, False)
     log("timed %d steps in %.3f s" % (args.steps, wall))
 
-    sec_ms = {s: float(np.mean([m[s][0].elapsed_time(m[s][1]) for m in all_marks])) for s in sections}
+    sec_ms = {s: np.asarray([m[s][0].elapsed_time(m[s][1]) for m in all_marks]) for s in sections}
 
     comps = {}
     for s in ("decode32k", "decode128k"):
@@ -599,52 +931,53 @@ def main():
         w = work[s]
         L = w["cfg"].n_layers
         by = w["n_anchor"] * w["bytes_anchor"] + w["n_reuse"] * w["bytes_reuse"]
-        # per-kind breakdown outside the timed steps
-        per = {}
+        us_layer = float(np.median(sec_ms[s])) * 1e3 / L
+        # each section and kind again, `reps` times, one synchronised replay each
+        rep = {None: pct(event_reps(torch, graphs[s][None], reps), 1e3 / L)}
         for kind, n in (("anchor", w["n_anchor"]), ("reuse", w["n_reuse"]), ("dense", L)):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = 5
-            e0.record()
-            for _ in range(reps):
-                w["run"](kind)
-            e1.record()
-            torch.cuda.synchronize()
-            per[kind] = e0.elapsed_time(e1) / reps / n * 1e3
+            rep[kind] = pct(event_reps(torch, graphs[s][kind], reps), 1e3 / n)
+        per = {k: rep[k]["median"] for k in ("anchor", "reuse", "dense")}
         comps[s] = {
-            "us_per_layer": sec_ms[s] * 1e3 / L,
-            "GBps": by / (sec_ms[s] * 1e-3) / 1e9,
-            "hbm_frac": by / (sec_ms[s] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "us_per_layer": us_layer,
+            "us_per_layer_steps": pct(sec_ms[s], 1e3 / L),
+            "us_per_layer_reps": rep[None],
+            "GBps": by / (us_layer * L * 1e-6) / 1e9,
+            "hbm_frac": by / (us_layer * L * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "anchor_us": per["anchor"], "reuse_us": per["reuse"],
+            "anchor_us_reps": rep["anchor"], "reuse_us_reps": rep["reuse"],
             "anchor_GBps": w["bytes_anchor"] / (per["anchor"] * 1e-6) / 1e9,
             "reuse_GBps": w["bytes_reuse"] / (per["reuse"] * 1e-6) / 1e9,
-            "dense_us_per_layer": per["dense"],
+            "reuse_hbm_frac": w["bytes_reuse"] / (per["reuse"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "dense_us_per_layer": per["dense"], "dense_us_reps": rep["dense"],
             "dense_GBps": w["bytes_dense"] / (per["dense"] * 1e-6) / 1e9,
-            "speedup_vs_dense": per["dense"] / (sec_ms[s] * 1e3 / L),
+            "speedup_vs_dense": per["dense"] / us_layer,
             "context": w["cfg"].ctx_len, "batch": w["cfg"].batch, "topk": w["cfg"].topk,
+            "timing": "eager launches" if args.eager else "HIP graph replay of the section's layers",
         }
     if "prefill" in sections:
         w = work["prefill"]
         rf = w["reuse_flops"]()
         fl = w["n_anchor"] * (w["flops_flash"] + w["flops_pool"]) + rf
+        prep = max(3, min(reps, 10))
         per = {}
+        rep = {}
         for kind, n in (("anchor", w["n_anchor"]), ("reuse", w["n_reuse"]), ("dense", 1)):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            w["run"](kind)
-            e1.record()
-            torch.cuda.synchronize()
-            per[kind] = e0.elapsed_time(e1) / n
+            rep[kind] = pct(event_reps(torch, lambda kind=kind: w["run"](kind), prep), 1.0 / n)
+            per[kind] = rep[kind]["median"]
+        ms = float(np.median(sec_ms["prefill"]))
         comps["prefill32k"] = {
-            "ms": sec_ms["prefill"], "TFLOPs": fl / (sec_ms["prefill"] * 1e-3) / 1e12,
+            "ms": ms, "ms_steps": pct(sec_ms["prefill"]), "TFLOPs": fl / (ms * 1e-3) / 1e12,
             "anchor_ms": per["anchor"], "reuse_ms": per["reuse"],
+            "anchor_ms_reps": rep["anchor"], "reuse_ms_reps": rep["reuse"],
             "anchor_TFLOPs": (w["flops_flash"] + w["flops_pool"]) / (per["anchor"] * 1e-3) / 1e12,
             "reuse_TFLOPs": rf / w["n_reuse"] / (per["reuse"] * 1e-3) / 1e12,
-            "mfma_frac": fl / (sec_ms["prefill"] * 1e-3) / 1e12 / MFMA16_PEAK_TFLOPS,
+            "mfma_frac": fl / (ms * 1e-3) / 1e12 / MFMA16_PEAK_TFLOPS,
             "anchor_mfma_frac": (w["flops_flash"] + w["flops_pool"]) / (per["anchor"] * 1e-3) / 1e12
             / MFMA16_PEAK_TFLOPS,
+            "reuse_mfma_frac": rf / w["n_reuse"] / (per["reuse"] * 1e-3) / 1e12 / MFMA16_PEAK_TFLOPS,
             "dense_ms_per_layer": per["dense"],
             "dense_TFLOPs": w["flops_flash"] / (per["dense"] * 1e-3) / 1e12,
-            "speedup_vs_dense": per["dense"] * w["cfg"].n_layers / sec_ms["prefill"],
+            "speedup_vs_dense": per["dense"] * w["cfg"].n_layers / ms,
         }
 
     # roofline of the dominant kernel
@@ -674,6 +1007,23 @@ def main():
                      "frac": ach / HBM_PEAK_GBS, "algorithmic_per_launch": per_launch,
                      "traffic": stored_traffic(names[dom], s)})
 
+    # the decode sections' bandwidth against a measured copy as well
+    copy_gbps = stream_copy_gbps(torch)
+    for s in ("decode32k", "decode128k"):
+        if s in comps:
+            comps[s]["stream_copy_GBps"] = copy_gbps
+            comps[s]["reuse_frac_of_copy"] = comps[s]["reuse_GBps"] / copy_gbps
+            comps[s]["anchor_frac_of_copy"] = comps[s]["anchor_GBps"] / copy_gbps
+
+    qwen3_S = None
+    if args.only is None and not args.no_qwen3:
+        for s in ("decode32k", "decode128k"):
+            graphs.pop(s, None)
+        for s in ("decode128k",):
+            work.pop(s, None)
+        torch.cuda.empty_cache()
+        comps["qwen3_e2e"], qwen3_S = qwen3_bench(torch, K, synth, configs, args, reps)
+
     ms_per_step = wall * 1e3 / args.steps
     value = comps.get("decode32k", {}).get("us_per_layer")
     line = {
@@ -683,12 +1033,17 @@ def main():
         "config": {"workload": "Llama-3.1-8B-shaped attention, 32 layers, 32q/8kv heads, d=128, "
                                "anchors [0,2,8,13,14]: decode 32K ctx B=1 k=3264 + decode 128K ctx "
                                "B=4 k=13120 + prefill 32K tokens (tile 128, k_t min 256)",
-                   "sections": sections},
+                   "sections": sections,
+                   "value": "median over the timed steps of the 32K decode section (32 layers, one "
+                            "HIP graph replay) per layer"},
         "components": comps, "roofline": roof,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
-        line["cpu_baseline"] = cpu_baseline(work["decode32k"], torch)
+        pre = work.get("prefill")
+        if pre is not None and qwen3_S is not None:
+            pre["qwen3_S"] = qwen3_S
+        line["cpu_baseline"] = cpu_baseline(work["decode32k"], pre, torch)
     print(json.dumps(line), flush=True)
 
 
