@@ -155,6 +155,26 @@ int kascade_reuse_prefill(const kascade_shape* shape, const void* q, const void*
                           void* out, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
+/* Allocation-free reuse decode, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): kascade_reuse_decode without a workspace argument, same
+ * kernels and the same results.  Its scratch (split partials [B*Hq, S, d+2]
+ * then log2-lse [B*Hq], fp32, each part rounded up to 256 bytes; S = the
+ * split count the library plans for topk keys, at most 2048) lives in a
+ * static 8 MiB device array inside the library, one per GPU, held until the
+ * process ends; the call allocates and frees nothing.  Calls whose scratch
+ * would exceed 8 MiB return KASCADE_ERR_WORKSPACE before any launch (with
+ * the default planning a call needs about B*Hq*min(topk/128, 512/(B*Hkv)+1)
+ * * 520 bytes: 0.4 MB for 32 heads at k 3264, 1 MB for 4 x 32 heads at
+ * k 13120).  Every call on a GPU shares that GPU's array: calls that overlap
+ * on one GPU (other streams, other threads) race and give undefined results;
+ * calls ordered on one stream are fine.  Nothing in the array needs to start
+ * at zero.  Other arguments, errors and stream behaviour as for
+ * kascade_reuse_decode. */
+int kascade_reuse_decode_noalloc(const kascade_shape* shape, const void* q, const void* k,
+                                 const void* v, int32_t topk, const int32_t* anchor_topk_idx,
+                                 const int32_t* head_map, void* out, hipStream_t stream);
+
 /* ---- paged KV caches (block tables) -------------------------------------- */
 
 /* A paged K or V cache: key j of batch b lives in physical block

@@ -18,8 +18,18 @@ thread_local int g_last_hip_error = 0;
 
 
 constexpr int kMaxDevices = 64;
+
+// Scratch of the allocation-free reuse decode (kascade_reuse_decode_noalloc):
+// split partials and per-head log2-lse live in this file-scope device array,
+// one copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel: the device address comes from hipGetSymbolAddress
+// (DeviceInfo::scratch, taken once per device at set-up).
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 struct DeviceInfo {
   bool init = false;
+  void* scratch = nullptr;   // device address of this GPU's scratch array
   int select_cache_cap = 0;
   int cus = 0;
   size_t lds_per_cu = 0;
@@ -74,6 +84,14 @@ int device_setup(DeviceInfo** out) {
       g_last_hip_error = (int)e;
       return KASCADE_ERR_HIP;
     }
+    // this device's copy of the scratch array (the device is current here)
+    void* sp = nullptr;
+    e = hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || sp == nullptr) {
+      g_last_hip_error = (int)(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return KASCADE_ERR_HIP;
+    }
+    d.scratch = sp;
     d.init = true;
   }
   *out = &d;
@@ -614,10 +632,12 @@ static int anchor_decode_impl(const kascade_shape* s, const kascade_paged_kv* pg
   return hip_status(e);
 }
 
+// use_scratch: the partials and lse go to this GPU's scratch array (laid out
+// for the planned split count) instead of the caller's workspace.
 static int reuse_decode_impl(const kascade_shape* s, const kascade_paged_kv* pg, const void* q,
                       const void* k, const void* v, int32_t topk, const int32_t* idx,
                       const int32_t* head_map, void* out, void* ws, size_t ws_bytes,
-                      hipStream_t stream) {
+                      hipStream_t stream, bool use_scratch = false) {
   int st = check_shape(s, false, pg != nullptr);
   if (st) return st;
   if ((st = check_paged(s, pg))) return st;
@@ -626,12 +646,22 @@ static int reuse_decode_impl(const kascade_shape* s, const kascade_paged_kv* pg,
   if (topk < 1 || topk > s->ctx_len) return KASCADE_ERR_TOPK;
   HeadMap hm;
   if ((st = check_head_map(head_map, s->n_kv_heads, &hm))) return st;
-  if (!ws || ws_bytes < plan_decode(s, topk, false, false, 0).total) return KASCADE_ERR_WORKSPACE;
+  if (!use_scratch && (!ws || ws_bytes < plan_decode(s, topk, false, false, 0).total))
+    return KASCADE_ERR_WORKSPACE;
   DeviceInfo* dev = nullptr;
   if ((st = device_setup(&dev))) return st;
   DecodePlan p;
   if ((st = plan_decode_dev(dev, s, topk, true, false, false, pg != nullptr, &p))) return st;
   if (p.kps > kMaxGatherKeys) return KASCADE_ERR_SHAPE;
+  if (use_scratch) {
+    // partials [B*Hq, splits, d+2] then log2-lse [B*Hq], all fp32
+    const size_t BH = (size_t)s->batch * s->n_q_heads;
+    p.off_part = 0;
+    p.off_lse2 = align256(BH * (size_t)p.splits * (size_t)(s->head_dim + 2) * 4);
+    p.total = p.off_lse2 + align256(BH * 4);
+    if (p.total > kScratchBytes) return KASCADE_ERR_WORKSPACE;
+    ws = dev->scratch;
+  }
   char* w = reinterpret_cast<char*>(ws);
   DecodeArgs a = decode_args(s, q, k, v, topk, p, w);
   set_paged(a, s, pg);
@@ -660,6 +690,12 @@ int kascade_reuse_decode(const kascade_shape* s, const void* q, const void* k, c
                          int32_t topk, const int32_t* idx, const int32_t* head_map, void* out,
                          void* ws, size_t ws_bytes, hipStream_t stream) {
   return reuse_decode_impl(s, nullptr, q, k, v, topk, idx, head_map, out, ws, ws_bytes, stream);
+}
+
+int kascade_reuse_decode_noalloc(const kascade_shape* s, const void* q, const void* k,
+                                 const void* v, int32_t topk, const int32_t* idx,
+                                 const int32_t* head_map, void* out, hipStream_t stream) {
+  return reuse_decode_impl(s, nullptr, q, k, v, topk, idx, head_map, out, nullptr, 0, stream, true);
 }
 
 int kascade_anchor_decode_paged(const kascade_shape* s, const kascade_paged_kv* paged,

@@ -20,6 +20,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkascade.so")
 
 KASCADE_F32, KASCADE_BF16, KASCADE_F16 = 0, 1, 2
+KASCADE_OK, KASCADE_ERR_NULL, KASCADE_ERR_SHAPE, KASCADE_ERR_DTYPE = 0, -1, -2, -3
+KASCADE_ERR_TOPK, KASCADE_ERR_HEADMAP, KASCADE_ERR_WORKSPACE, KASCADE_ERR_HIP = -4, -5, -6, -7
+KASCADE_ERR_ARG = -8
 OP_ANCHOR_DECODE, OP_REUSE_DECODE, OP_ANCHOR_PREFILL, OP_REUSE_PREFILL = 0, 1, 2, 3
 OP_DENSE_DECODE, OP_DENSE_PREFILL = 4, 5
 K_DECODE_SPLITK, K_DECODE_COMBINE, K_DECODE_POOL, K_TOPK_SELECT = 0, 1, 2, 3
@@ -34,6 +37,7 @@ EXPORTS = [
     "kascade_anchor_decode_paged", "kascade_reuse_decode_paged", "kascade_reuse_prefill_paged",
     "kascade_calib_head_similarity", "kascade_layer_weight", "kascade_layer_weight_workspace_bytes",
     "kascade_weighted_similarity", "kascade_select_anchors", "kascade_head_maps",
+    "kascade_reuse_decode_noalloc",
 ]
 
 
@@ -77,6 +81,7 @@ _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c
 _SIGS = {
     "kascade_anchor_decode": (_i32, [ctypes.POINTER(Shape), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kascade_reuse_decode": (_i32, [ctypes.POINTER(Shape), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kascade_reuse_decode_noalloc": (_i32, [ctypes.POINTER(Shape), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp]),
     "kascade_anchor_prefill": (_i32, [ctypes.POINTER(Shape), _vp, _vp, _vp, ctypes.POINTER(TopkRule), _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kascade_reuse_prefill": (_i32, [ctypes.POINTER(Shape), _vp, _vp, _vp, ctypes.POINTER(TopkRule), _vp, _vp, _vp, _vp, _sz, _vp]),
     "kascade_workspace_bytes": (_sz, [_i32, ctypes.POINTER(Shape), _i32, ctypes.POINTER(TopkRule)]),
@@ -148,6 +153,14 @@ def kascade_reuse_decode(shape, q, k, v, topk, anchor_topk_idx, head_map, out, w
     return lib().kascade_reuse_decode(ctypes.byref(shape), _p(q), _p(k), _p(v), topk,
                                       _p(anchor_topk_idx), ctypes.cast(hm, _vp) if hm is not None else None,
                                       _p(out), _p(workspace), workspace_bytes, _stream(stream))
+
+
+def kascade_reuse_decode_noalloc(shape, q, k, v, topk, anchor_topk_idx, head_map, out, stream=None) -> int:
+    hm = (ctypes.c_int32 * len(head_map))(*[int(x) for x in head_map]) if head_map is not None else None
+    return lib().kascade_reuse_decode_noalloc(ctypes.byref(shape), _p(q), _p(k), _p(v), topk,
+                                              _p(anchor_topk_idx),
+                                              ctypes.cast(hm, _vp) if hm is not None else None,
+                                              _p(out), _stream(stream))
 
 
 def kascade_anchor_prefill(shape, q, k, v, rule, out, lse_out, tile_topk_idx, pooled_out,
