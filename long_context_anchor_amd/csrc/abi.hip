@@ -320,8 +320,11 @@ int decode_splits(int64_t n_keys, int64_t rows, int slots, int64_t max_kps, int*
 // Passes without a score spill (reuse gather, dense): about two workgroups
 // per CU, i.e. fewer and longer splits than the resident slots allow, which
 // measured 3-6% faster (dense 128K: 16 splits of 8192 keys per row; the
-// split merge reads fewer partials); a small gather keeps at least 128 keys
-// per workgroup.  Splits are capped at max_kps keys.
+// split merge reads fewer partials); a small gather keeps at least 64 keys
+// per workgroup (one load step per wave: at 32K x 1, k 3264, 408 workgroups
+// measured 10.1 us per reuse layer against 11.1 with 128 keys and 184
+// workgroups; 48 or 32 keys were slower again).  Splits are capped at
+// max_kps keys.
 int decode_splits_target(int64_t n_keys, int64_t rows, int64_t target, int64_t max_kps,
                          int* kps_out) {
   int64_t S = target / rows;
@@ -395,7 +398,7 @@ int plan_decode_dev(DeviceInfo* d, const kascade_shape* s, int n_keys, bool gath
   if (!spill) {
     const int64_t total = (int64_t)n_keys * s->batch * s->n_kv_heads;
     int64_t target = 2 * (int64_t)(d->cus > 0 ? d->cus : 1);
-    if (gather) target = total / 128 < target ? (total / 128 > 0 ? total / 128 : 1) : target;
+    if (gather) target = total / 64 < target ? (total / 64 > 0 ? total / 64 : 1) : target;
     *p = plan_decode(s, n_keys, spill, pooled_ws, 0, target,
                      (gather || paged) ? kMaxGatherKeys : (int64_t)1 << 30);
     return KASCADE_OK;
