@@ -586,18 +586,26 @@ static int anchor_decode_impl(const kascade_shape* s, const kascade_paged_kv* pg
     a.hist1 = reinterpret_cast<uint32_t*>(w + p.off_hist1);
     a.ncand = reinterpret_cast<uint32_t*>(w + p.off_ncand);
   }
-  float* lse2 = reinterpret_cast<float*>(w + p.off_lse2);
   float* pooled = pooled_out ? pooled_out : reinterpret_cast<float*>(w + p.off_pooled);
   hipError_t e = timed(KASCADE_K_DECODE_SPLITK, stream,
                        [&] { return launch_decode_splitk(a, s->dtype, false, stream); });
   if (e != hipSuccess) return hip_status(e);
-  CombineArgs c = {a.part, p.splits, s->batch * s->n_q_heads, out, lse2, lse_out};
-  e = timed(KASCADE_K_DECODE_COMBINE, stream,
-            [&] { return launch_decode_combine(c, s->dtype, stream); });
-  if (e != hipSuccess) return hip_status(e);
-  PoolDecodeArgs pa = {a.scores, lse2, pooled, a.hist0, s->batch, s->n_q_heads, s->n_kv_heads,
-                       s->ctx_len};
-  e = timed(KASCADE_K_DECODE_POOL, stream, [&] { return launch_decode_pool(pa, stream); });
+  // one launch pools the row (its lse from the splits' (m, l)) and merges the
+  // splits into out / lse_out
+  PoolDecodeArgs pa;
+  memset(&pa, 0, sizeof(pa));
+  pa.scores = a.scores;
+  pa.part = a.part;
+  pa.n_splits = p.splits;
+  pa.pooled = pooled;
+  pa.hist0 = a.hist0;
+  pa.out = out;
+  pa.lse_out = lse_out;
+  pa.B = s->batch;
+  pa.Hq = s->n_q_heads;
+  pa.Hkv = s->n_kv_heads;
+  pa.N = s->ctx_len;
+  e = timed(KASCADE_K_DECODE_POOL, stream, [&] { return launch_decode_pool(pa, s->dtype, stream); });
   if (e != hipSuccess) return hip_status(e);
   if (p.wide_chunks) {
     WideSelectArgs wa;

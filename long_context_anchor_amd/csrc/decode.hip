@@ -616,26 +616,22 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
   }
 }
 
-// One workgroup per (batch, query head): merge the splits.  Thread
-// (part, dd) folds splits part, part + PARTS, ... into a running
-// (max, sum, output column dd) with all of its loads issued up front, then
-// the PARTS partial states of each column meet once in LDS.
-constexpr int kCombineThreads = 1024;
-constexpr int kMaxSplits = 2048;
-
-template <typename T>
-__global__ __launch_bounds__(kCombineThreads) void k_decode_combine(const CombineArgs a) {
+// Merge the splits of query head bh with NT threads: thread (part, dd) folds
+// splits part, part + PARTS, ... into a running (max, sum, output column dd)
+// with kBatch splits' loads issued up front, then the PARTS partial states of
+// each column meet once in LDS (sm, sl, so hold NT floats each) and threads
+// < D write the normalised column; thread 0 writes the lse.
+template <typename T, int NT, int kBatch>
+KC_INLINE void merge_splits(const float* part, int S, int64_t bh, void* out, float* lse2,
+                            float* lse_out, float* sm, float* sl, float* so) {
   constexpr int D = Elem<T>::D;
-  constexpr int PARTS = kCombineThreads / D;
-  constexpr int kBatch = 8;   // splits whose loads are in flight together
-  __shared__ float sm[PARTS][D], sl[PARTS][D], so[PARTS][D];
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const int dd = tid % D, part = tid / D;
-  const int S = a.n_splits;
-  const float* p = a.part + (int64_t)bh * S * (D + 2);
+  constexpr int PARTS = NT / D;
+  const int tid = threadIdx.x;
+  const int dd = tid % D, prt = tid / D;
+  const float* p = part + bh * S * (D + 2);
 
   float M = kNegInf, L = 0.f, O = 0.f;
-  for (int s0 = part; s0 < S; s0 += PARTS * kBatch) {
+  for (int s0 = prt; s0 < S; s0 += PARTS * kBatch) {
     float mv[kBatch], lv[kBatch], ov[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -655,60 +651,110 @@ __global__ __launch_bounds__(kCombineThreads) void k_decode_combine(const Combin
       M = mn;
     }
   }
-  sm[part][dd] = M;
-  sl[part][dd] = L;
-  so[part][dd] = O;
+  sm[prt * D + dd] = M;
+  sl[prt * D + dd] = L;
+  so[prt * D + dd] = O;
   __syncthreads();
   if (tid < D) {
     float Mt = kNegInf;
 #pragma unroll
-    for (int q = 0; q < PARTS; ++q) Mt = fmaxf(Mt, sm[q][tid]);
+    for (int q = 0; q < PARTS; ++q) Mt = fmaxf(Mt, sm[q * D + tid]);
     float Lt = 0.f, Ot = 0.f;
     if (Mt != kNegInf) {
 #pragma unroll
       for (int q = 0; q < PARTS; ++q) {
-        const float w = exp2f_fast(sm[q][tid] - Mt);
-        Lt = fmaf(sl[q][tid], w, Lt);
-        Ot = fmaf(so[q][tid], w, Ot);
+        const float w = exp2f_fast(sm[q * D + tid] - Mt);
+        Lt = fmaf(sl[q * D + tid], w, Lt);
+        Ot = fmaf(so[q * D + tid], w, Ot);
       }
     }
     const float r = Lt > 0.f ? Ot / Lt : 0.f;
     if constexpr (std::is_same<T, _Float16>::value) {
-      reinterpret_cast<_Float16*>(a.out)[(int64_t)bh * D + tid] = (_Float16)r;
+      reinterpret_cast<_Float16*>(out)[bh * D + tid] = (_Float16)r;
     } else if constexpr (sizeof(T) == 2) {
-      reinterpret_cast<uint16_t*>(a.out)[(int64_t)bh * D + tid] = (uint16_t)f32_to_bf16_bits(r);
+      reinterpret_cast<uint16_t*>(out)[bh * D + tid] = (uint16_t)f32_to_bf16_bits(r);
     } else {
-      reinterpret_cast<float*>(a.out)[(int64_t)bh * D + tid] = r;
+      reinterpret_cast<float*>(out)[bh * D + tid] = r;
     }
     if (tid == 0) {
-      const float lse2 = Mt + log2f_fast(Lt);
-      if (a.lse2) a.lse2[bh] = lse2;
-      if (a.lse_out) a.lse_out[bh] = lse2 * kLn2;
+      const float l2 = Mt + log2f_fast(Lt);
+      if (lse2) lse2[bh] = l2;
+      if (lse_out) lse_out[bh] = l2 * kLn2;
     }
   }
 }
 
-template <int G>
+// One workgroup per (batch, query head): merge the splits (reuse and dense
+// passes).
+constexpr int kCombineThreads = 1024;
+constexpr int kMaxSplits = 2048;
+
+template <typename T>
+__global__ __launch_bounds__(kCombineThreads) void k_decode_combine(const CombineArgs a) {
+  __shared__ float sm[kCombineThreads], sl[kCombineThreads], so[kCombineThreads];
+  merge_splits<T, kCombineThreads, 8>(a.part, a.n_splits, blockIdx.x, a.out, a.lse2, a.lse_out, sm,
+                                      sl, so);
+}
+
+// Anchor pooling fused with the anchor pass's split merge (see
+// PoolDecodeArgs).  A pooling workgroup issues its 1024 keys' score loads for
+// the G heads of KV head g, merges the heads' lse from the splits' (m, l)
+// (wave w takes heads w, w + 4) while those loads are in flight, then writes
+// pooled[j] = sum_h 2^(s_hj - lse_h) and the digit-0 histogram of the row.
+template <typename T, int G>
 __global__ __launch_bounds__(256) void k_decode_pool(const PoolDecodeArgs a) {
+  constexpr int D = Elem<T>::D;
   __shared__ uint32_t sh[2048];
+  __shared__ float s_lse[G];
+  __shared__ float sm[256], sl[256], so[256];
   const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int chunks = (a.N + 1023) / 1024;
+  if ((int)blockIdx.x >= chunks) {   // merge workgroup of query head g*G + (x - chunks)
+    const int64_t bh = (int64_t)b * a.Hq + g * G + ((int)blockIdx.x - chunks);
+    merge_splits<T, 256, 16>(a.part, a.n_splits, bh, a.out, nullptr, a.lse_out, sm, sl, so);
+    return;
+  }
   for (int i = tid; i < 2048; i += 256) sh[i] = 0u;
-  __syncthreads();
   const int j = (blockIdx.x * 256 + tid) * 4;
-  float lse[G];
   const float* sp[G];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const int64_t bh = (int64_t)b * a.Hq + g * G + hh;
-    lse[hh] = a.lse2[bh];
-    sp[hh] = a.scores + bh * a.N;
+  for (int hh = 0; hh < G; ++hh) sp[hh] = a.scores + ((int64_t)b * a.Hq + g * G + hh) * a.N;
+  const bool vec = j + 4 <= a.N && (a.N & 3) == 0;
+  float4 s4[G];
+  if (vec) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) s4[hh] = *reinterpret_cast<const float4*>(sp[hh] + j);
   }
+  {
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int hh = wave; hh < G; hh += 4) {
+      const float* p = a.part + ((int64_t)b * a.Hq + g * G + hh) * a.n_splits * (D + 2);
+      float M = kNegInf, L = 0.f;
+      for (int s = lane; s < a.n_splits; s += 64) {
+        const float m = p[(int64_t)s * (D + 2)], l = p[(int64_t)s * (D + 2) + 1];
+        const float mn = fmaxf(M, m);
+        if (mn != kNegInf) {
+          L = fmaf(L, exp2f_fast(M - mn), l * exp2f_fast(m - mn));
+          M = mn;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float Mo = __shfl_xor(M, o, 64), Lo = __shfl_xor(L, o, 64);
+        const float mn = fmaxf(M, Mo);
+        L = mn == kNegInf ? 0.f : fmaf(L, exp2f_fast(M - mn), Lo * exp2f_fast(Mo - mn));
+        M = mn;
+      }
+      if (lane == 0) s_lse[hh] = M + log2f_fast(L);
+    }
+  }
+  __syncthreads();
+  float lse[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) lse[hh] = s_lse[hh];
   float* out = a.pooled + ((int64_t)b * a.Hkv + g) * a.N;
   if (j < a.N) {
-    if (j + 4 <= a.N && (a.N & 3) == 0) {
-      float4 s4[G];
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) s4[hh] = *reinterpret_cast<const float4*>(sp[hh] + j);
+    if (vec) {
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
@@ -891,16 +937,23 @@ hipError_t launch_decode_combine(const CombineArgs& a, int dtype, hipStream_t s)
   return hipGetLastError();
 }
 
-hipError_t launch_decode_pool(const PoolDecodeArgs& a, hipStream_t s) {
-  dim3 grid((a.N + 1023) / 1024, a.Hkv, a.B);
+template <typename T>
+hipError_t launch_pool_t(const PoolDecodeArgs& a, hipStream_t s) {
+  dim3 grid((a.N + 1023) / 1024 + a.Hq / a.Hkv, a.Hkv, a.B);
   switch (a.Hq / a.Hkv) {
-    case 1: hipLaunchKernelGGL(k_decode_pool<1>, grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(k_decode_pool<2>, grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(k_decode_pool<4>, grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(k_decode_pool<8>, grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_decode_pool<T, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_decode_pool<T, 2>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_decode_pool<T, 4>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_decode_pool<T, 8>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_decode_pool(const PoolDecodeArgs& a, int dtype, hipStream_t s) {
+  if (a.n_splits > kMaxSplits || a.n_splits < 1) return hipErrorInvalidValue;
+  if (dtype == 2) return launch_pool_t<_Float16>(a, s);
+  return dtype == 1 ? launch_pool_t<uint16_t>(a, s) : launch_pool_t<float>(a, s);
 }
 
 }  // namespace kc

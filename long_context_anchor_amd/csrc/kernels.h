@@ -47,11 +47,18 @@ struct CombineArgs {
   float* lse_out;                // [B*Hq] natural-log lse, may be null
 };
 
+// Pooling of the anchor pass, fused with its split merge: workgroups
+// x < ceil(N/1024) pool 1024 keys each (their group's lse comes from the
+// splits' (m, l)); the G workgroups after them merge the splits of one query
+// head each into out and lse_out.
 struct PoolDecodeArgs {
   const float* scores;           // [B,Hq,N]
-  const float* lse2;             // [B,Hq]
+  const float* part;             // [B*Hq, n_splits, D+2] split partials (m, l, o), log2 domain
+  int32_t n_splits;
   float* pooled;                 // [B,Hkv,N]
   uint32_t* hist0;               // [B*Hkv][2048]: counts of key bits 31..21 of pooled
+  void* out;                     // [B*Hq, D] input dtype
+  float* lse_out;                // [B*Hq] natural-log lse, may be null
   int32_t B, Hq, Hkv, N;
 };
 
@@ -138,7 +145,7 @@ size_t decode_splitk_dyn_lds(int dtype, int G, bool gather, bool spill, bool pag
 // paged: a.table is set (bf16 only)
 hipError_t launch_decode_splitk(const DecodeArgs& a, int dtype, bool gather, hipStream_t s);
 hipError_t launch_decode_combine(const CombineArgs& a, int dtype, hipStream_t s);
-hipError_t launch_decode_pool(const PoolDecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_pool(const PoolDecodeArgs& a, int dtype, hipStream_t s);
 hipError_t launch_topk_select(const SelectArgs& a, hipStream_t s);
 
 // Exact Top-k of a few long fp32 rows (decode pooled rows) by chunks of
