@@ -591,16 +591,12 @@ def paged_bench(torch, K, synth, configs, args):
         row = {}
         for kind in ("anchor", "reuse"):
             for paged in (False, True):
+                # the kind's 8 layers as one HIP graph, timed over primed replays
+                g = capture_graph(torch, lambda kind=kind, paged=paged: run(kind, paged))
                 for _ in range(args.warmup):
-                    run(kind, paged)
-                torch.cuda.synchronize()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for _ in range(args.steps):
-                    run(kind, paged)
-                e1.record()
-                torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) * 1e3 / (args.steps * nl)
+                    g.replay()
+                us = float(np.median(event_reps(torch, g.replay, max(args.steps, 10)))) * 1e3 / nl
+                del g
                 by = 2 * B * Hkv * (N if kind == "anchor" else k) * cfg.head_dim * 2
                 row["%s_%s_us" % (kind, "paged" if paged else "contig")] = us
                 row["%s_%s_GBps" % (kind, "paged" if paged else "contig")] = by / (us * 1e-6) / 1e9
@@ -655,13 +651,8 @@ def paged_prefill_row(torch, K, synth, configs, args):
         for _ in range(args.warmup):
             run(paged)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
-            run(paged)
-        e1.record()
-        torch.cuda.synchronize()
-        row["reuse_%s_ms" % ("paged" if paged else "contig")] = e0.elapsed_time(e1) / args.steps
+        ts = event_reps(torch, lambda: run(paged), max(args.steps, 5), prime=False)
+        row["reuse_%s_ms" % ("paged" if paged else "contig")] = float(np.median(ts))
     row["identical"] = bool(torch.equal(outs[False].view(torch.int16), outs[True].view(torch.int16)))
     return row
 
