@@ -55,6 +55,30 @@ def log(*a):
 # workload construction (synthetic, seeded)
 # ---------------------------------------------------------------------------
 
+def decode_bytes(cfg):
+    """Algorithmic HBM bytes of one decode layer (16-bit K/V and queries):
+    (anchor, reuse, dense).  Anchor: every K and V row of the cache, the
+    queries read and the output written, the list written; reuse: the listed
+    K and V rows, the list read, queries and output; dense: cache, queries,
+    output."""
+    e = 2
+    io = cfg.batch * cfg.n_q_heads * cfg.head_dim * e * 2 + cfg.batch * cfg.n_kv_heads * cfg.topk * 4
+    anchor = 2 * cfg.batch * cfg.n_kv_heads * cfg.ctx_len * cfg.head_dim * e + io
+    reuse = 2 * cfg.batch * cfg.n_kv_heads * cfg.topk * cfg.head_dim * e + io
+    dense = 2 * cfg.batch * cfg.n_kv_heads * cfg.ctx_len * cfg.head_dim * e + \
+        cfg.batch * cfg.n_q_heads * cfg.head_dim * e * 2
+    return anchor, reuse, dense
+
+
+def prefill_flops(cfg):
+    """Algorithmic FLOPs of one causal prefill layer: (flash pass, pooling
+    pass).  The flash pass does Q K^T and P V over the causal triangle
+    (4 d Hq N (N+1) / 2), the pooling pass recomputes Q K^T (half of that);
+    the waste of the diagonal blocks is not counted."""
+    d, Hq, N = cfg.head_dim, cfg.n_q_heads, cfg.ctx_len
+    return 4.0 * d * Hq * N * (N + 1) / 2, 2.0 * d * Hq * N * (N + 1) / 2
+
+
 def build_decode(workload, torch, K, synth, configs, dtype="bf16"):
     cfg = dataclasses.replace(workload, dtype=dtype)
     N, L = cfg.ctx_len, cfg.n_layers
@@ -91,26 +115,23 @@ def build_decode(workload, torch, K, synth, configs, dtype="bf16"):
                 K.check(K.kascade_reuse_decode(sh, q, k, v, cfg.topk, idx[anchor_of[l]], maps[l], out,
                                                ws_r, ws_r.numel()), "reuse_decode")
 
-    e = 2
     n_anchor = len(cfg.anchors)
     n_reuse = L - n_anchor
-    io = cfg.batch * cfg.n_q_heads * cfg.head_dim * e * 2 + cfg.batch * cfg.n_kv_heads * cfg.topk * 4
-    bytes_anchor = 2 * cfg.batch * cfg.n_kv_heads * N * cfg.head_dim * e + io
-    bytes_reuse = 2 * cfg.batch * cfg.n_kv_heads * cfg.topk * cfg.head_dim * e + io
-    bytes_dense = 2 * cfg.batch * cfg.n_kv_heads * N * cfg.head_dim * e + \
-        cfg.batch * cfg.n_q_heads * cfg.head_dim * e * 2
+    bytes_anchor, bytes_reuse, bytes_dense = decode_bytes(cfg)
     return dict(cfg=cfg, run=run, n_anchor=n_anchor, n_reuse=n_reuse, bytes_anchor=bytes_anchor,
                 bytes_reuse=bytes_reuse, bytes_dense=bytes_dense, layers=layers, maps=maps)
 
 
 def prefill_reuse_flops(torch, K, idx_by_anchor, anchor_of, maps, layers_reuse, N, n_kv, group, d):
-    """4*d*sum_{h,r} |J_{h,r}| over the reuse layers, counted from the anchors' tile lists."""
+    """4*d*sum_{h,r} |J_{h,r}| over the reuse layers, counted from the anchors' tile lists
+    (J_{h,r} = the listed positions j <= r of row r's tile for KV head head_map[h // group])."""
     rule = K.PREFILL_RULE
     T = N // rule.tile
-    rows = torch.arange(N, device="cuda", dtype=torch.int64).view(T, rule.tile)
+    dev = next(iter(idx_by_anchor.values())).device
+    rows = torch.arange(N, device=dev, dtype=torch.int64).view(T, rule.tile)
     per_anchor = {}
     for a, ix in idx_by_anchor.items():
-        cnt = torch.zeros(n_kv, dtype=torch.float64, device="cuda")
+        cnt = torch.zeros(n_kv, dtype=torch.float64, device=dev)
         for t in range(T):
             kt = K.kascade_topk_for_len(min(N, rule.tile * (t + 1)), rule)
             lst = ix[0, t, :, :kt].to(torch.int64).contiguous()        # [Hkv, kt]
@@ -160,9 +181,8 @@ def build_prefill(torch, K, synth, configs, dtype="bf16"):
                 K.check(K.kascade_reuse_prefill(sh, q, k, v, rule, idx[anchor_of[l]], maps[l], out,
                                                 None, 0), "reuse_prefill")
 
-    d, Hq = cfg.head_dim, cfg.n_q_heads
-    flops_flash = 4.0 * d * Hq * N * (N + 1) / 2
-    flops_pool = 2.0 * d * Hq * N * (N + 1) / 2
+    d = cfg.head_dim
+    flops_flash, flops_pool = prefill_flops(cfg)
     reuse_layers = [l for l in range(L) if l not in cfg.anchors]
 
     def reuse_flops():
@@ -729,7 +749,7 @@ def qwen3_bench(torch, K, synth, configs, args, reps):
     for kind in (None, "anchor", "reuse"):
         pre[kind] = event_reps(torch, lambda: w["prefill"](kind), 3, prime=False)
     rf = w["reuse_flops"]()
-    fl_anchor = 6.0 * d * Hq * N0 * (N0 + 1) / 2
+    fl_anchor = sum(prefill_flops(cfg))
     anchor_ms = float(np.median(pre["anchor"])) / na
     reuse_ms = float(np.median(pre["reuse"])) / nr
     log("qwen3: prefill done, capturing %d decode steps" % steps)
@@ -757,9 +777,7 @@ def qwen3_bench(torch, K, synth, configs, args, reps):
         kind_us[kind] = pct(event_reps(torch, g.replay, reps), 1e3 / n)
         del g
     k_last = w["dec_k"](n_last)
-    io = Hq * d * 2 * 2 + Hkv * k_last * 4
-    by_anchor = 2 * Hkv * n_last * d * 2 + io
-    by_reuse = 2 * Hkv * k_last * d * 2 + io
+    by_anchor, by_reuse, _ = decode_bytes(dataclasses.replace(cfg, ctx_len=n_last, topk=k_last, batch=1))
     torch.cuda.synchronize()
     res = {
         "workload": "Qwen3-8B-shaped: 36 layers, 32q/8kv heads, d=128, %s; DP anchors %s; prefill %d tokens "
