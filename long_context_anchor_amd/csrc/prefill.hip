@@ -12,7 +12,9 @@
 //   k_prefill_attn<false>  causal flash attention, writes O and the log2 lse
 //   k_prefill_attn<true>   the same over a gathered key list (reuse layer)
 //   k_prefill_pool<G>      recomputes S = Q K^T per (tile, KV head) and sums
-//                          2^(S*c - lse2) over the G heads x 128 rows
+//                          2^(S*c - lse2) over the G heads x 128 rows; the
+//                          tile's queries stay in LDS, each wave owns whole
+//                          64-key slices (no barrier in the key loop)
 //
 // MFMA mapping (v_mfma_f32_32x32x16_bf16, or _f16 for fp16 inputs; wave64).  Operand A is 32x16 with
 // lane l holding row l%32, k = 8*(l/32)..+7; operand B is 16x32 with lane l
@@ -25,8 +27,9 @@
 //     each 16-key chunk; V stays [key][d] in LDS and its A operand is read
 //     with the gfx950 transposing LDS load (ds_read_b64_tr_b16) in that
 //     order.
-//   pooling: S = Q K^T (A = Q registers, B = K from LDS), so each lane owns
-//     one key column and the pooled column sum is an in-lane sum.
+//   pooling: S = Q K^T (A = Q fragments from LDS, B = K^T fragments held in
+//     registers for a 64-key slice), so each lane owns one key column and
+//     the pooled column sum is an in-lane sum.
 #include "common.h"
 #include "kernels.h"
 #include "paged.h"
@@ -424,113 +427,121 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void k_prefill_attn(const Pr
   }
 }
 
-// One workgroup = one (query tile, KV head, batch): 4*WH waves; wave w takes
-// the 32-row slice w%4 of the tile for heads (w/4) + WH*i of the group, one
-// head at a time (i outer), so a wave holds one head's queries.
+// Pooling with the tile's queries resident in LDS: one workgroup = one
+// (query tile, KV head, batch) holds the 128 rows of HQ heads of the group
+// (HQ*34 KiB) and the rows' -lse2/c; each wave owns whole 64-key slices of
+// the causal prefix, keeps their K^T fragments in registers, and runs every
+// held query row against them, so a key's pooled sum over the heads and
+// rows stays in its lane and is written once.  No barrier inside the key
+// loop: waves proceed independently.  Each Q fragment read from LDS feeds
+// two MFMAs (the slice's two 32-key halves).
 template <int G, bool HALF>
-__global__ __launch_bounds__(256 * (G < 4 ? G : 4)) void k_prefill_pool(const PrefillArgs a) {
-  typedef Fmt16<HALF> F;   // bf16 or fp16 elements
-  constexpr int WH = G < 4 ? G : 4;          // head lanes of waves
-  constexpr int HPW = G / WH;                // heads per wave
-  constexpr int NT = 256 * WH;
-  constexpr int NW = NT / 64;
-  // key blocks and column sums double-buffered: one barrier per block
-  __shared__ __align__(16) uint16_t sk[2][kKB * kKStride];
-  __shared__ float red[2][NW][kKB];
+__global__ __launch_bounds__(1024) void k_prefill_pool(const PrefillArgs a) {
+  typedef Fmt16<HALF> F;
+  typedef typename F::v8 v8;
+  constexpr int HQ = G < 4 ? G : 4;      // heads held per pass
+  constexpr int PASSES = G / HQ;
+  constexpr int NT = 1024, NW = NT / 64;
+  extern __shared__ __align__(16) uint16_t dyn[];
+  uint16_t* const sq = dyn;                                            // [HQ][128][kKStride]
+  float* const nlse = reinterpret_cast<float*>(dyn + HQ * kTileQ * kKStride);   // [HQ][128]
 
   int t, g, b;
   if (!xcd_work_item(a.T * a.Hkv * a.B, 1, a.T, a.Hkv, t, g, b)) return;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
-  const int slice = wave & 3, hw = wave >> 2;
   const int N = a.N;
-  const int row0 = t * kTileQ + slice * 32;
   const float c = a.scale_log2;
+  const float inv_c = 1.0f / c;
   const int P = min(N, kTileQ * (t + 1));
+  const int nsl = (P + kKB - 1) / kKB;
   const int64_t row_bytes = a.kv_sn * 2;
   const char* kbase = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh) * 2;
   float* prow = a.pooled + (int64_t)b * a.packed_per_batch + packed_row_offset(t, g, a.Hkv, kTileQ, N);
 
-  for (int hi = 0; hi < HPW; ++hi) {
-    typename F::v8 qf[8];
-    float lse[16];
-    {
-      const int h = g * G + hw + WH * hi;
-      const int r = row0 + l32;
-      const char* qp = reinterpret_cast<const char*>(a.q) +
-                       ((int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)min(r, N - 1) * a.q_sn) * 2;
-#pragma unroll
-      for (int ds = 0; ds < 8; ++ds) {
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (r < N) u = ld16(qp + (ds * 16 + hf * 8) * 2);
-        qf[ds] = as_v8<HALF>(u);
-      }
-      const float* lp = a.lse2 + ((int64_t)b * a.Hq + h) * N;
-#pragma unroll
-      for (int ri = 0; ri < 16; ++ri) {
-        const int rr = row0 + 8 * (ri >> 2) + 4 * hf + (ri & 3);
-        lse[ri] = rr < N ? lp[rr] : 0.f;
-      }
+  for (int pass = 0; pass < PASSES; ++pass) {
+    if (pass > 0) __syncthreads();   // every wave is done with the previous heads
+    // queries of the pass's heads (rows past the prompt as zeros) and -lse2/c
+    for (int i = tid; i < HQ * kTileQ * 16; i += NT) {
+      const int ch = i & 15, rr = (i >> 4) % kTileQ, hq = i / (16 * kTileQ);
+      const int h = g * G + pass * HQ + hq, r = t * kTileQ + rr;
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (r < N)
+        u = ld16(reinterpret_cast<const char*>(a.q) +
+                 ((int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)r * a.q_sn) * 2 + ch * 16);
+      sts16(sq + (hq * kTileQ + rr) * kKStride + ch * 8, u);
     }
-    RowStager<NT> regs;
-    const int nblk = (P + kKB - 1) / kKB;
-    regs.load_dense(kbase, row_bytes, P);
-    regs.store(sk[0]);
-    if (nblk > 1) regs.load_dense(kbase + (int64_t)kKB * row_bytes, row_bytes, P - kKB);
+    for (int i = tid; i < HQ * kTileQ; i += NT) {
+      const int hq = i / kTileQ, rr = i % kTileQ, r = t * kTileQ + rr;
+      const int h = g * G + pass * HQ + hq;
+      nlse[i] = r < N ? -a.lse2[((int64_t)b * a.Hq + h) * N + r] * inv_c : 0.f;
+    }
     __syncthreads();
-    // column sums of the G heads x 128 rows of block jb - 1 (complete once
-    // the barrier after its step has passed) added into the pooled row
-    auto fold = [&](int jb) {
-      const int kb = jb * kKB;
-      if (tid < kKB && kb + tid < P) {
-        float sum = hi == 0 ? 0.f : prow[kb + tid];
-#pragma unroll
-        for (int w = 0; w < NW; ++w) sum += red[jb & 1][w][tid];
-        prow[kb + tid] = sum;
-      }
-    };
-    for (int jb = 0; jb < nblk; ++jb) {
-      const int kb = jb * kKB;
-      // block jb + 1 goes over block jb - 1, whose readers finished before
-      // the barrier that ended step jb - 1
-      if (jb + 1 < nblk) regs.store(sk[(jb + 1) & 1]);
-      if (jb + 2 < nblk)
-        regs.load_dense(kbase + (int64_t)(kb + 2 * kKB) * row_bytes, row_bytes, P - kb - 2 * kKB);
-      const bool need_mask = (kb + kKB - 1 > row0) || (kb + kKB > P) || (row0 + 32 > N);
-      const uint16_t* skb = sk[jb & 1];
-      f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
-#pragma unroll
-      for (int ds = 0; ds < 8; ++ds) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const auto kf = as_v8<HALF>(lds16(skb + (kt * 32 + l32) * kKStride + ds * 16 + hf * 8));
-          acc[kt] = F::mfma(qf[ds], kf, acc[kt]);
-        }
-      }
+
+    for (int sl = wave; sl < nsl; sl += NW) {
+      const int kb = sl * kKB;
+      // K^T fragments (MFMA B operand): lane holds key kb + 32*kt + l32 and
+      // d = 16*ds + 8*hf .. +7; keys past the prefix load the last one (masked)
+      v8 kf[2][8];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const int j = kb + kt * 32 + l32;
-        float cs = 0.f;
-        if (need_mask) {
+        const int key = min(kb + kt * 32 + l32, P - 1);
+        const char* kp = kbase + (int64_t)key * row_bytes + hf * 16;
 #pragma unroll
-          for (int ri = 0; ri < 16; ++ri) {
-            const int rr = row0 + 8 * (ri >> 2) + 4 * hf + (ri & 3);
-            const float p = exp2f_fast(fmaf(acc[kt][ri], c, -lse[ri]));
-            cs += (j <= rr && rr < N && j < P) ? p : 0.f;
-          }
-        } else {
-#pragma unroll
-          for (int ri = 0; ri < 16; ++ri) cs += exp2f_fast(fmaf(acc[kt][ri], c, -lse[ri]));
-        }
-        cs += __shfl_xor(cs, 32, 64);
-        if (hf == 0) red[jb & 1][wave][kt * 32 + l32] = cs;
+        for (int ds = 0; ds < 8; ++ds) kf[kt][ds] = as_v8<HALF>(ld16(kp + ds * 32));
       }
-      if (jb > 0) fold(jb - 1);
-      __syncthreads();
+      float cs0 = 0.f, cs1 = 0.f;
+      const int j0 = kb + l32, j1 = kb + 32 + l32;
+#pragma unroll 1
+      for (int hq = 0; hq < HQ; ++hq) {
+#pragma unroll 1
+        for (int rs = 0; rs < 4; ++rs) {
+          const int row0 = t * kTileQ + rs * 32;
+          // every key after every row, or rows past the prompt: nothing to add
+          if (kb > row0 + 31 || row0 >= N) continue;
+          const float* nl = nlse + hq * kTileQ + rs * 32 + 4 * hf;
+          f32x16_t acc0, acc1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float4 u = *reinterpret_cast<const float4*>(nl + 8 * i);
+            acc0[4 * i + 0] = u.x; acc0[4 * i + 1] = u.y; acc0[4 * i + 2] = u.z; acc0[4 * i + 3] = u.w;
+          }
+          acc1 = acc0;
+          const uint16_t* qrow = sq + (hq * kTileQ + rs * 32 + l32) * kKStride + hf * 8;
+#pragma unroll
+          for (int ds = 0; ds < 8; ++ds) {
+            const v8 qa = as_v8<HALF>(lds16(qrow + ds * 16));
+            acc0 = F::mfma(qa, kf[0][ds], acc0);
+            acc1 = F::mfma(qa, kf[1][ds], acc1);
+          }
+          const bool need_mask = (kb + kKB - 1 > row0) || (kb + kKB > P) || (row0 + 32 > N);
+          if (need_mask) {
+#pragma unroll
+            for (int ri = 0; ri < 16; ++ri) {
+              const int rr = row0 + 8 * (ri >> 2) + 4 * hf + (ri & 3);
+              const float p0 = exp2f_fast(acc0[ri] * c), p1 = exp2f_fast(acc1[ri] * c);
+              cs0 += (j0 <= rr && rr < N && j0 < P) ? p0 : 0.f;
+              cs1 += (j1 <= rr && rr < N && j1 < P) ? p1 : 0.f;
+            }
+          } else {
+#pragma unroll
+            for (int ri = 0; ri < 16; ++ri) {
+              cs0 += exp2f_fast(acc0[ri] * c);
+              cs1 += exp2f_fast(acc1[ri] * c);
+            }
+          }
+        }
+      }
+      // the two half-waves hold complementary rows of the same keys
+      cs0 += __shfl_xor(cs0, 32, 64);
+      cs1 += __shfl_xor(cs1, 32, 64);
+      const int j = hf ? j1 : j0;
+      if (j < P) {
+        const float v = hf ? cs1 : cs0;
+        prow[j] = pass == 0 ? v : prow[j] + v;
+      }
     }
-    fold(nblk - 1);
-    __syncthreads();   // red and sk are reused by the next head pass
   }
 }
 
@@ -556,17 +567,37 @@ hipError_t sparse_h(const PrefillArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// dynamic LDS of the pooling kernel: the held heads' 128 query rows and their -lse2/c
+constexpr size_t pool_lds_bytes(int G) { return (size_t)(G < 4 ? G : 4) * kTileQ * (kKStride * 2 + 4); }
+
 template <bool HALF>
 hipError_t pool_h(const PrefillArgs& a, hipStream_t s) {
-  dim3 grid(xcd_grid(a.T * a.Hkv * a.B));
-  switch (a.Hq / a.Hkv) {
-    case 1: hipLaunchKernelGGL((k_prefill_pool<1, HALF>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_prefill_pool<2, HALF>), grid, dim3(512), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_prefill_pool<4, HALF>), grid, dim3(1024), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((k_prefill_pool<8, HALF>), grid, dim3(1024), 0, s, a); break;
+  const dim3 grid(xcd_grid(a.T * a.Hkv * a.B)), block(1024);
+  const int G = a.Hq / a.Hkv;
+  const size_t lds = pool_lds_bytes(G);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((k_prefill_pool<1, HALF>), grid, block, lds, s, a); break;
+    case 2: hipLaunchKernelGGL((k_prefill_pool<2, HALF>), grid, block, lds, s, a); break;
+    case 4: hipLaunchKernelGGL((k_prefill_pool<4, HALF>), grid, block, lds, s, a); break;
+    case 8: hipLaunchKernelGGL((k_prefill_pool<8, HALF>), grid, block, lds, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <bool HALF>
+hipError_t set_pool_lds_h() {
+  const void* fs[] = {reinterpret_cast<const void*>(&k_prefill_pool<1, HALF>),
+                      reinterpret_cast<const void*>(&k_prefill_pool<2, HALF>),
+                      reinterpret_cast<const void*>(&k_prefill_pool<4, HALF>),
+                      reinterpret_cast<const void*>(&k_prefill_pool<8, HALF>)};
+  const int gs[] = {1, 2, 4, 8};
+  for (int i = 0; i < 4; ++i) {
+    const hipError_t e =
+        hipFuncSetAttribute(fs[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)pool_lds_bytes(gs[i]));
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <bool HALF, bool PAGED>
@@ -595,6 +626,8 @@ hipError_t prefill_set_max_lds() {
   if (e == hipSuccess) e = set_lds_h<true, false>(bytes);
   if (e == hipSuccess) e = set_lds_h<false, true>(bytes);
   if (e == hipSuccess) e = set_lds_h<true, true>(bytes);
+  if (e == hipSuccess) e = set_pool_lds_h<false>();
+  if (e == hipSuccess) e = set_pool_lds_h<true>();
   return e;
 }
 
