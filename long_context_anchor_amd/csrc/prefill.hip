@@ -81,23 +81,32 @@ struct RowStager {
   }
   // Gathered rows pos[rr] (block-relative rows rr < nvalid); missing rows
   // (-1 or past the list) load cache row 0 and are masked the same way.
+  // nvalid >= 1, so every list read is clamped into the block's entries and
+  // issued unconditionally: the reads go out together and one wait covers
+  // them (a read guarded by rr < nvalid becomes a branch and a wait per row).
   KC_INLINE void load_gather(const char* base, int64_t row_bytes, const int32_t* pos, int nvalid) {
+    int p[U];
 #pragma unroll
     for (int i = 0; i < U; ++i) {
       const int rr = row(i);
-      const int p = rr < nvalid ? pos[rr] : -1;
-      k[i] = ld16(base + (int64_t)(p < 0 ? 0 : p) * row_bytes + chunk(i) * 16);
+      const int v = pos[min(rr, nvalid - 1)];
+      p[i] = rr < nvalid ? v : -1;
     }
+#pragma unroll
+    for (int i = 0; i < U; ++i) k[i] = ld16(base + (int64_t)(p[i] < 0 ? 0 : p[i]) * row_bytes + chunk(i) * 16);
   }
   // Physical rows rows[rr] of a paged cache (block-relative rows rr <
   // nvalid); missing rows load physical row 0 and are masked the same way.
   KC_INLINE void load_rows(const char* base, int64_t row_bytes, const int32_t* rows, int nvalid) {
+    uint32_t p[U];
 #pragma unroll
     for (int i = 0; i < U; ++i) {
       const int rr = row(i);
-      const uint32_t p = rr < nvalid ? (uint32_t)rows[rr] : 0u;
-      k[i] = ld16(base + (uint64_t)p * (uint64_t)row_bytes + chunk(i) * 16);
+      const uint32_t v = (uint32_t)rows[min(rr, nvalid - 1)];
+      p[i] = rr < nvalid ? v : 0u;
     }
+#pragma unroll
+    for (int i = 0; i < U; ++i) k[i] = ld16(base + (uint64_t)p[i] * (uint64_t)row_bytes + chunk(i) * 16);
   }
   // rows as [key][d] (padded rows of STRIDE bf16)
   KC_INLINE void store(uint16_t* sk) const {
