@@ -132,6 +132,37 @@ def test_paged_reuse_prefill(B, Hq, Hkv, N, bs, hm):
             assert np.max(np.abs(on[b, h, rows] - ref)) <= 2e-2, (b, h)
 
 
+def test_paged_reuse_prefill_longest_list():
+    """The longest list the paged reuse prefill stages (12288 keys: positions
+    and physical rows both sit in LDS): k_t the whole prefix (pct 100), so
+    the output is dense causal attention; bitwise the contiguous pass, and
+    against the oracle on sampled rows."""
+    N, Hq, Hkv, bs = 12288, 2, 1, 64
+    say("paged reuse prefill longest list", N, bs)
+    g = torch.Generator(device=DEV).manual_seed(31)
+    q = torch.randn((1, Hq, N, 128), generator=g, device=DEV).bfloat16()
+    k = torch.randn((1, Hkv, N, 128), generator=g, device=DEV).bfloat16()
+    v = torch.randn((1, Hkv, N, 128), generator=g, device=DEV).bfloat16()
+    rule = K.TopkRule(128, 100, 64, 256)
+    kmax = K.kascade_topk_for_len(N, rule)
+    assert kmax == 12288
+    T = N // 128
+    lists = -np.ones((1, T, Hkv, kmax), dtype=np.int32)
+    for t in range(T):
+        lists[0, t, 0, :128 * (t + 1)] = np.arange(128 * (t + 1))
+    idx = torch.as_tensor(lists, device=DEV)
+    kc, vc, table = _paged(k, v, bs, seed=33)
+    out = K.reuse_prefill_paged(q, kc, vc, table, idx, [0], rule)
+    out_c = K.reuse_prefill(q, k, v, idx, [0], rule)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_c.view(torch.int16))
+    qn, kn, vn, on = np64(q), np64(k), np64(v), np64(out)
+    rows = [0, 1, 127, 128, 5000, N - 1]
+    for h in range(Hq):
+        ro, _, _ = oracle.dense_prefill_rows(qn, kn, vn, 0, h, rows)
+        assert np.max(np.abs(on[0, h, rows] - ro)) <= 2e-2, h
+
+
 def test_paged_reuse_prefill_32k():
     """Full-size reuse layer of the 32K-token prompt workload (32 q / 8 KV
     heads, bf16, block size 16, blocks scattered): bit-identical to the

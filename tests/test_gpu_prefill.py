@@ -143,6 +143,33 @@ def test_reuse_prefill_full_lists_equal_dense():
     assert torch.max(torch.abs(sp.float() - dense.float())).item() <= 1e-2
 
 
+def test_reuse_prefill_longest_list():
+    """The longest list the contiguous reuse prefill stages in LDS (24576
+    keys, checked on the host): with k_t the whole prefix (pct 100) the
+    reuse pass is dense causal attention ([Explainer] "アンカーレイヤーと
+    再利用レイヤー": softmax over the listed keys), here against the oracle's
+    fp64 rows and the GPU's own dense pass."""
+    N, Hq, Hkv = 24576, 2, 1
+    say("reuse prefill longest list", N)
+    q, k, v = _rand_layer(1, Hq, Hkv, N, seed=29)
+    rule = K.TopkRule(128, 100, 64, 256)
+    kmax = K.kascade_topk_for_len(N, rule)
+    assert kmax == 24576
+    T = N // 128
+    lists = -np.ones((1, T, Hkv, kmax), dtype=np.int32)
+    for t in range(T):
+        lists[0, t, 0, :128 * (t + 1)] = np.arange(128 * (t + 1))
+    sp = K.reuse_prefill(q, k, v, torch.as_tensor(lists, device=DEV), [0], rule)
+    dense, _ = K.dense_prefill(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.max(torch.abs(sp.float() - dense.float())).item() <= 1e-2
+    qn, kn, vn, sn = np64(q), np64(k), np64(v), np64(sp)
+    rows = [0, 1, 127, 128, 12345, N - 129, N - 1]
+    for h in range(Hq):
+        ro, _, _ = oracle.dense_prefill_rows(qn, kn, vn, 0, h, rows)
+        assert np.max(np.abs(sn[0, h, rows] - ro)) <= 2e-2, h
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_llama_prefill_32k_sampled(dtype):
     """Full-size anchor + reuse layer pair of the 32K-token prefill workload
