@@ -732,6 +732,21 @@ def stream_copy_gbps(torch, nbytes=4 << 30, reps=10):
     return 2.0 * nbytes / (np.median(ts) * 1e-3) / 1e9
 
 
+def stream_read_gbps(torch, K, nbytes=4 << 30, reps=10):
+    """Measured HBM read bandwidth: the library's stream-read reference
+    (kascade_stream_read: every byte read once with the decode passes'
+    16-byte nontemporal loads) over a buffer far larger than the last-level
+    cache."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    run = lambda: K.check(K.kascade_stream_read(src, nbytes, sink), "kascade_stream_read")
+    run()
+    ts = event_reps(torch, run, reps)
+    del src, sink
+    torch.cuda.empty_cache()
+    return nbytes / (np.median(ts) * 1e-3) / 1e9
+
+
 def qwen3_bench(torch, K, synth, configs, args, reps):
     """Config-5 figures: the 36-layer 64K prefill (eager; per kind over the
     layers of that kind) and the 512 decode steps, each step one HIP graph,
@@ -1024,10 +1039,15 @@ def main():
                      "frac": ach / HBM_PEAK_GBS, "algorithmic_per_launch": per_launch,
                      "traffic": stored_traffic(names[dom], s)})
 
-    # the decode sections' bandwidth against a measured copy as well
+    # the decode sections' bandwidth against a measured stream read (and a
+    # device copy) as well
+    read_gbps = stream_read_gbps(torch, K)
     copy_gbps = stream_copy_gbps(torch)
     for s in ("decode32k", "decode128k"):
         if s in comps:
+            comps[s]["stream_read_GBps"] = read_gbps
+            comps[s]["reuse_frac_of_read"] = comps[s]["reuse_GBps"] / read_gbps
+            comps[s]["anchor_frac_of_read"] = comps[s]["anchor_GBps"] / read_gbps
             comps[s]["stream_copy_GBps"] = copy_gbps
             comps[s]["reuse_frac_of_copy"] = comps[s]["reuse_GBps"] / copy_gbps
             comps[s]["anchor_frac_of_copy"] = comps[s]["anchor_GBps"] / copy_gbps

@@ -291,6 +291,14 @@ int kascade_topk_select_f32(const float* scores, int64_t row_stride, int32_t row
                             int32_t n, int32_t k, int32_t* idx, int64_t idx_stride,
                             hipStream_t stream);
 
+/* Stream-read reference for measurement (not part of the method): reads the
+ * `bytes` bytes at src (device, 16-byte aligned, bytes a positive multiple of
+ * 16) once with the 16-byte nontemporal loads of the decode passes and sets
+ * *sink ^= XOR of all its 32-bit words (sink: device, 4-byte aligned; the
+ * caller zeroes it if it wants the plain XOR).  Asynchronous on `stream`;
+ * KASCADE_ERR_NULL / KASCADE_ERR_ARG on bad arguments, nothing launched. */
+int kascade_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 /* Dense baselines with the same kernels and layouts: decode = anchor decode
  * without pooling/selection; prefill = the causal flash pass alone. */
 int kascade_dense_decode(const kascade_shape* shape, const void* q, const void* k,

@@ -12,6 +12,12 @@
 
 using namespace kc;
 
+// stream.hip: the stream-read reference (a measurement helper, not part of
+// the method, so it stays out of the kernels' shared header)
+namespace kc {
+hipError_t launch_stream_read(const void* src, int64_t n16, uint32_t* sink, int grid, hipStream_t s);
+}
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -875,6 +881,17 @@ int kascade_head_maps(int32_t L, int32_t n_kv_heads, const float* sim, const int
     }
   }
   return KASCADE_OK;
+}
+
+int kascade_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!src || !sink) return KASCADE_ERR_NULL;
+  if (bytes < 16 || bytes % 16 != 0 || !aligned16(src) || ((uintptr_t)sink & 3u) != 0) return KASCADE_ERR_ARG;
+  DeviceInfo* dev = nullptr;
+  int st = device_setup(&dev);
+  if (st) return st;
+  // one 1024-thread workgroup per CU, each streaming a contiguous range
+  const int grid = dev->cus > 0 ? dev->cus : 1;
+  return hip_status(launch_stream_read(src, (int64_t)(bytes / 16), sink, grid, stream));
 }
 
 int kascade_topk_select_f32(const float* scores, int64_t row_stride, int32_t rows, int32_t n,

@@ -37,7 +37,7 @@ EXPORTS = [
     "kascade_anchor_decode_paged", "kascade_reuse_decode_paged", "kascade_reuse_prefill_paged",
     "kascade_calib_head_similarity", "kascade_layer_weight", "kascade_layer_weight_workspace_bytes",
     "kascade_weighted_similarity", "kascade_select_anchors", "kascade_head_maps",
-    "kascade_reuse_decode_noalloc",
+    "kascade_reuse_decode_noalloc", "kascade_stream_read",
 ]
 
 
@@ -103,6 +103,7 @@ _SIGS = {
     "kascade_weighted_similarity": (_i32, [_i32, _i32, _vp, _vp, _vp]),
     "kascade_select_anchors": (_i32, [_i32, _i32, _vp, _vp, _vp]),
     "kascade_head_maps": (_i32, [_i32, _i32, _vp, _vp, _i32, _vp]),
+    "kascade_stream_read": (_i32, [_vp, _sz, _vp, _vp]),
 }
 
 
@@ -186,6 +187,10 @@ def kascade_workspace_bytes(op, shape, topk=0, rule=None) -> int:
 
 def kascade_topk_for_len(n, rule) -> int:
     return lib().kascade_topk_for_len(n, ctypes.byref(rule))
+
+
+def kascade_stream_read(src, nbytes, sink, stream=None) -> int:
+    return lib().kascade_stream_read(_p(src), nbytes, _p(sink), _stream(stream))
 
 
 def kascade_topk_select_f32(scores, row_stride, rows, n, k, idx, idx_stride, stream=None) -> int:

@@ -129,6 +129,15 @@ def test_select_validation():
     assert K.kascade_topk_select_f32(FAKE, 10, 0, 10, 3, FAKE, 3, 0) == 0   # nothing to do
 
 
+def test_stream_read_validation():
+    assert K.kascade_stream_read(None, 64, FAKE, 0) == -1
+    assert K.kascade_stream_read(FAKE, 64, None, 0) == -1
+    assert K.kascade_stream_read(FAKE, 0, FAKE, 0) == -8          # empty
+    assert K.kascade_stream_read(FAKE, 24, FAKE, 0) == -8         # not whole 16-byte words
+    assert K.kascade_stream_read(FAKE + 8, 64, FAKE, 0) == -8     # source not 16-byte aligned
+    assert K.kascade_stream_read(FAKE, 64, FAKE + 2, 0) == -8     # sink not 4-byte aligned
+
+
 def test_timer_api_bounds():
     assert K.lib().kascade_kernel_timer_enable(99, 1) == -8
 
