@@ -378,7 +378,7 @@ DecodePlan plan_decode(const kascade_shape* s, int n_keys, bool spill, bool pool
   if (pooled_ws) off += align256((size_t)rows * s->ctx_len * 4);
   p.wide_chunks = 0;
   p.off_hist1 = p.off_ncand = p.off_cand = p.off_chunk = p.off_thr = 0;
-  const int chunks = (s->ctx_len + kWideChunk - 1) / kWideChunk;
+  const int chunks = (s->ctx_len + wide_chunk(s->ctx_len) - 1) / wide_chunk(s->ctx_len);
   if (spill && s->ctx_len >= kWideMinKeys && chunks <= kWideMaxChunks) {
     p.wide_chunks = chunks;
     p.off_hist1 = off;

@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const SelectArgs a)
 // ---- wide select: few long rows, many workgroups per row ------------------
 //
 // The same radix select (digits of 11, 11 and 10 bits) and index-ordered
-// compaction as k_topk_select, spread over chunks of kWideChunk keys:
+// compaction as k_topk_select, spread over chunks of CH keys (wide_chunk(n)):
 //   pass A (chunks x rows): every chunk finds digit 0's bin from the complete
 //     histogram, counts digit 1 of its keys in that bin (LDS, then integer
 //     atomics into hist1) and appends those keys to the row's candidates;
@@ -340,7 +340,6 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const SelectArgs a)
 
 constexpr int kWideThreads = 256;
 constexpr int kWideWaves = kWideThreads / 64;
-constexpr int kPerThread = kWideChunk / kWideThreads;   // 8 consecutive keys
 
 // Exclusive prefix sum over the 256-thread block; `sh` holds >= 5 words.
 KC_INLINE uint32_t scan256(uint32_t x, uint32_t* sh, uint32_t& total) {
@@ -406,11 +405,13 @@ KC_INLINE uint32_t find_bin256(const uint32_t* hist, uint32_t need, uint32_t* sh
   return bin;
 }
 
-// The thread's 8 consecutive keys of chunk c (keys past n read as 0; every
-// use checks the position against n).
-KC_INLINE void chunk_keys(const WideSelectArgs& a, const float* src, int c, uint32_t (&key)[kPerThread],
-                          int& j0) {
-  j0 = c * kWideChunk + threadIdx.x * kPerThread;
+// The thread's CH/256 consecutive keys of chunk c (keys past n read as 0;
+// every use checks the position against n).
+template <int CH, int PT = CH / kWideThreads>
+KC_INLINE void chunk_keys(const WideSelectArgs& a, const float* src, int c, uint32_t (&key)[PT], int& j0) {
+  static_assert(PT % 4 == 0, "whole 16-byte loads");
+  constexpr int kPerThread = PT;
+  j0 = c * CH + threadIdx.x * kPerThread;
   const bool vec = (a.row_stride & 3) == 0 && ((reinterpret_cast<uintptr_t>(a.src) & 15) == 0);
   if (vec && j0 + kPerThread <= a.n) {
 #pragma unroll
@@ -427,7 +428,9 @@ KC_INLINE void chunk_keys(const WideSelectArgs& a, const float* src, int c, uint
   }
 }
 
+template <int CH>
 __global__ __launch_bounds__(kWideThreads) void k_select_wide_a(const WideSelectArgs a) {
+  constexpr int kPerThread = CH / kWideThreads;
   __shared__ uint32_t hist[kHistBins];
   __shared__ uint32_t sh[8], s_sel[2], s_base;
   const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
@@ -438,7 +441,7 @@ __global__ __launch_bounds__(kWideThreads) void k_select_wide_a(const WideSelect
   for (int i = tid; i < kHistBins; i += kWideThreads) hist[i] = 0u;
   uint32_t key[kPerThread];
   int j0;
-  chunk_keys(a, src, c, key, j0);
+  chunk_keys<CH>(a, src, c, key, j0);
   __syncthreads();
   uint32_t cnt = 0;
 #pragma unroll
@@ -463,7 +466,9 @@ __global__ __launch_bounds__(kWideThreads) void k_select_wide_a(const WideSelect
   }
 }
 
+template <int CH>
 __global__ __launch_bounds__(kWideThreads) void k_select_wide_b(const WideSelectArgs a) {
+  constexpr int kPerThread = CH / kWideThreads;
   __shared__ uint32_t hist[1024];
   __shared__ uint32_t sh[8], s_sel[2];
   const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
@@ -488,7 +493,7 @@ __global__ __launch_bounds__(kWideThreads) void k_select_wide_b(const WideSelect
   const uint32_t T = (p01 << 10) | b2;   // the k-th largest key; `need` keys == T are taken
   uint32_t key[kPerThread];
   int j0;
-  chunk_keys(a, src, c, key, j0);
+  chunk_keys<CH>(a, src, c, key, j0);
   uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
@@ -509,7 +514,9 @@ __global__ __launch_bounds__(kWideThreads) void k_select_wide_b(const WideSelect
   }
 }
 
+template <int CH>
 __global__ __launch_bounds__(kWideThreads) void k_select_wide_c(const WideSelectArgs a) {
+  constexpr int kPerThread = CH / kWideThreads;
   __shared__ uint32_t sh[8];
   const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
   const float* src = a.src + (int64_t)row * a.row_stride;
@@ -527,7 +534,7 @@ __global__ __launch_bounds__(kWideThreads) void k_select_wide_c(const WideSelect
   scan256(eqb, sh, eq_before);
   uint32_t key[kPerThread];
   int j0;
-  chunk_keys(a, src, c, key, j0);
+  chunk_keys<CH>(a, src, c, key, j0);
   uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
@@ -554,18 +561,24 @@ __global__ __launch_bounds__(kWideThreads) void k_select_wide_c(const WideSelect
   }
 }
 
-hipError_t launch_topk_select_wide(const WideSelectArgs& a, hipStream_t s) {
-  if (a.rows <= 0) return hipSuccess;
-  if (a.chunks != (a.n + kWideChunk - 1) / kWideChunk || a.chunks > 65535) return hipErrorInvalidValue;
+template <int CH>
+hipError_t launch_wide_ch(const WideSelectArgs& a, hipStream_t s) {
   const dim3 grid(a.chunks, a.rows);
-  hipLaunchKernelGGL(k_select_wide_a, grid, dim3(kWideThreads), 0, s, a);
+  hipLaunchKernelGGL(k_select_wide_a<CH>, grid, dim3(kWideThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_select_wide_b, grid, dim3(kWideThreads), 0, s, a);
+  hipLaunchKernelGGL(k_select_wide_b<CH>, grid, dim3(kWideThreads), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_select_wide_c, grid, dim3(kWideThreads), 0, s, a);
+  hipLaunchKernelGGL(k_select_wide_c<CH>, grid, dim3(kWideThreads), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_topk_select_wide(const WideSelectArgs& a, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  const int ch = wide_chunk(a.n);
+  if (a.chunks != (a.n + ch - 1) / ch || a.chunks > 65535) return hipErrorInvalidValue;
+  return ch == kWideChunkShort ? launch_wide_ch<kWideChunkShort>(a, s) : launch_wide_ch<kWideChunk>(a, s);
 }
 
 size_t topk_select_lds_bytes(int cache_cap) {
