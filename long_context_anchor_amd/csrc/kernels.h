@@ -151,12 +151,13 @@ hipError_t launch_topk_select(const SelectArgs& a, hipStream_t s);
 // Exact Top-k of a few long fp32 rows (decode pooled rows) by chunks of
 // wide_chunk(n) keys over many workgroups, in three passes.  hist0 is
 // complete (the pooling pass), hist1 and ncand are zero on entry.  Rows up to
-// 64K keys use 1024-key chunks (twice the workgroups: 32K anchor layer 45.3
-// -> 44.5 us), longer rows 2048-key chunks (fewer chunk counts for the
-// prefix of pass C: 128K x 4 anchor layer 383.8 against 390.7 us with 1024).
+// 96K keys use 1024-key chunks (twice the workgroups: 32K anchor layer 45.3
+// -> 44.5 us, 66K-key rows 72.5 -> 71.7 us), longer rows 2048-key chunks
+// (fewer chunk counts for the prefix of pass C: 128K x 4 anchor layer 383.8
+// against 390.7 us with 1024).
 constexpr int kWideChunk = 2048;
 constexpr int kWideChunkShort = 1024;
-constexpr int kWideShortMaxKeys = 65536;
+constexpr int kWideShortMaxKeys = 98304;
 inline int wide_chunk(int n) { return n <= kWideShortMaxKeys ? kWideChunkShort : kWideChunk; }
 struct WideSelectArgs {
   const float* src;              // [rows][row_stride]
