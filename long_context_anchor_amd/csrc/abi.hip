@@ -287,7 +287,7 @@ struct DecodePlan {
   int kps, splits;
   int wide_chunks;   // > 0: the anchor's select runs over chunks of many workgroups
   size_t off_hist, off_scores, off_part, off_lse2, off_pooled, total;
-  size_t off_hist1, off_ncand, off_cand, off_chunk, off_thr;
+  size_t off_hist1, off_cand, off_chunk;
 };
 
 // Rows this long or longer are selected by the many-workgroup path.
@@ -377,20 +377,16 @@ DecodePlan plan_decode(const kascade_shape* s, int n_keys, bool spill, bool pool
   p.off_pooled = off;
   if (pooled_ws) off += align256((size_t)rows * s->ctx_len * 4);
   p.wide_chunks = 0;
-  p.off_hist1 = p.off_ncand = p.off_cand = p.off_chunk = p.off_thr = 0;
+  p.off_hist1 = p.off_cand = p.off_chunk = 0;
   const int chunks = (s->ctx_len + wide_chunk(s->ctx_len) - 1) / wide_chunk(s->ctx_len);
   if (spill && s->ctx_len >= kWideMinKeys && chunks <= kWideMaxChunks) {
     p.wide_chunks = chunks;
     p.off_hist1 = off;
     off += align256((size_t)rows * 2048 * 4);
-    p.off_ncand = off;
-    off += align256((size_t)rows * 4);
     p.off_cand = off;
     off += align256((size_t)rows * s->ctx_len * 4);
     p.off_chunk = off;
     off += align256((size_t)rows * chunks * 2 * 4);
-    p.off_thr = off;
-    off += align256((size_t)rows * 2 * 4);
   }
   p.total = off;
   return p;
@@ -590,7 +586,6 @@ static int anchor_decode_impl(const kascade_shape* s, const kascade_paged_kv* pg
   a.hist0 = reinterpret_cast<uint32_t*>(w + p.off_hist);
   if (p.wide_chunks) {
     a.hist1 = reinterpret_cast<uint32_t*>(w + p.off_hist1);
-    a.ncand = reinterpret_cast<uint32_t*>(w + p.off_ncand);
   }
   float* pooled = pooled_out ? pooled_out : reinterpret_cast<float*>(w + p.off_pooled);
   hipError_t e = timed(KASCADE_K_DECODE_SPLITK, stream,
@@ -626,10 +621,8 @@ static int anchor_decode_impl(const kascade_shape* s, const kascade_paged_kv* pg
     wa.idx_stride = topk;
     wa.hist0 = a.hist0;
     wa.hist1 = a.hist1;
-    wa.ncand = a.ncand;
     wa.cand = reinterpret_cast<uint32_t*>(w + p.off_cand);
     wa.chunk_cnt = reinterpret_cast<uint32_t*>(w + p.off_chunk);
-    wa.thr = reinterpret_cast<uint32_t*>(w + p.off_thr);
     e = timed(KASCADE_K_TOPK_SELECT, stream, [&] { return launch_topk_select_wide(wa, stream); });
     return hip_status(e);
   }

@@ -90,7 +90,6 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk(const DecodeArgs a) 
     if (a.hist1) {
       uint32_t* h1 = a.hist1 + row * 2048;
       for (int i = tid; i < 2048; i += kThreads) h1[i] = 0u;
-      if (tid == 0) a.ncand[row] = 0u;
     }
   }
   if (GATHER) {
@@ -353,7 +352,6 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
     if (a.hist1) {
       uint32_t* h1 = a.hist1 + row * 2048;
       for (int i = tid; i < 2048; i += kThreads) h1[i] = 0u;
-      if (tid == 0) a.ncand[row] = 0u;
     }
   }
   if (LIST) {

@@ -30,7 +30,6 @@ struct DecodeArgs {
   HeadMap hm;
   uint32_t* hist0;               // [B*Hkv][2048] zeroed here for the pooling kernel, or null
   uint32_t* hist1;               // [B*Hkv][2048] zeroed here for the wide select, or null
-  uint32_t* ncand;               // [B*Hkv] zeroed here for the wide select, or null
   // paged caches: key j of batch b is row (j & (bs-1)) of physical block
   // table[b * table_stride + (j >> blk_shift)]; physical row number
   // R = block * blk_rows + row, address = base + g*kv_sh + R*kv_sn (elements)
@@ -150,7 +149,7 @@ hipError_t launch_topk_select(const SelectArgs& a, hipStream_t s);
 
 // Exact Top-k of a few long fp32 rows (decode pooled rows) by chunks of
 // wide_chunk(n) keys over many workgroups, in three passes.  hist0 is
-// complete (the pooling pass), hist1 and ncand are zero on entry.  Rows up to
+// complete (the pooling pass), hist1 is zero on entry.  Rows up to
 // 96K keys use 1024-key chunks (twice the workgroups: 32K anchor layer 45.3
 // -> 44.5 us, 66K-key rows 72.5 -> 71.7 us), longer rows 2048-key chunks
 // (fewer chunk counts for the prefix of pass C: 128K x 4 anchor layer 383.8
@@ -167,10 +166,8 @@ struct WideSelectArgs {
   int64_t idx_stride;
   const uint32_t* hist0;         // [rows][2048]
   uint32_t* hist1;               // [rows][2048]
-  uint32_t* cand;                // [rows][n] keys of the digit-0 bin
-  uint32_t* ncand;               // [rows]
-  uint32_t* chunk_cnt;           // [rows][chunks][2] (greater, equal) per chunk
-  uint32_t* thr;                 // [rows][2] the k-th key and how many equal keys to take
+  uint32_t* cand;                // [rows][n] keys of the digit-0 bin, chunk c's at offset c*CH
+  uint32_t* chunk_cnt;           // [rows][chunks][2] (keys above the digit-0 bin, candidates)
 };
 hipError_t launch_topk_select_wide(const WideSelectArgs& a, hipStream_t s);
 size_t topk_select_lds_bytes(int cache_cap);

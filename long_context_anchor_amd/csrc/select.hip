@@ -324,19 +324,23 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(const SelectArgs a)
 // ---- wide select: few long rows, many workgroups per row ------------------
 //
 // The same radix select (digits of 11, 11 and 10 bits) and index-ordered
-// compaction as k_topk_select, spread over chunks of CH keys (wide_chunk(n)):
-//   pass A (chunks x rows): every chunk finds digit 0's bin from the complete
-//     histogram, counts digit 1 of its keys in that bin (LDS, then integer
-//     atomics into hist1) and appends those keys to the row's candidates;
+// compaction as k_topk_select, spread over chunks of CH keys (wide_chunk(n)),
+// in two passes after the pooling pass that built digit 0's histogram:
+//   pass A (chunks x rows): every chunk finds digit 0's bin b0 from the
+//     complete histogram, counts its keys above b0 (all selected), and
+//     histograms digit 1 of its keys in b0 (the candidates: LDS, then integer
+//     atomics into hist1) and stores them in index order at its own offset
+//     of the row's candidate buffer;
 //   pass B (chunks x rows): every chunk resolves digits 1 and 2 (digit 2 over
-//     the candidates), which fixes the k-th largest key T and how many keys
-//     equal to T are taken, and counts its keys > T and == T;
-//   pass C (chunks x rows): every chunk sums the counts of the chunks before
-//     it and writes its selected indices in index order.
+//     the row's candidates), which fixes the k-th largest key T and how many
+//     keys equal to T are taken, counts the keys > T and == T of the chunks
+//     before it (their keys above b0 plus their candidates compared with T),
+//     and writes its own selected indices in index order.
 // Every workgroup repeats the small histogram scans instead of waiting for
-// another; kernel boundaries order the passes.  Histograms are integer
-// atomics and candidate order is only ever counted, so the output is
-// deterministic.
+// another; the kernel boundary orders the passes.  Histograms are integer
+// atomics and candidates sit at fixed per-chunk offsets, so the output is
+// deterministic.  (A third pass that summed per-chunk counts written by pass
+// B measured 1.5 us slower per 32K anchor layer.)
 
 constexpr int kWideThreads = 256;
 constexpr int kWideWaves = kWideThreads / 64;
@@ -428,11 +432,16 @@ KC_INLINE void chunk_keys(const WideSelectArgs& a, const float* src, int c, uint
   }
 }
 
+// Pass A (chunks x rows): digit 0's bin b0 from the complete histogram; the
+// chunk's keys above b0 are counted (all selected), its keys in b0 (the
+// candidates) are counted, histogrammed on digit 1 (LDS, then integer atomics
+// into hist1) and stored in index order at the chunk's own offset of the
+// row's candidate buffer.  chunk_cnt[row][c] = {keys above b0, candidates}.
 template <int CH>
 __global__ __launch_bounds__(kWideThreads) void k_select_wide_a(const WideSelectArgs a) {
   constexpr int kPerThread = CH / kWideThreads;
   __shared__ uint32_t hist[kHistBins];
-  __shared__ uint32_t sh[8], s_sel[2], s_base;
+  __shared__ uint32_t sh[8], s_sel[2];
   const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
   const float* src = a.src + (int64_t)row * a.row_stride;
   uint32_t above;
@@ -443,21 +452,27 @@ __global__ __launch_bounds__(kWideThreads) void k_select_wide_a(const WideSelect
   int j0;
   chunk_keys<CH>(a, src, c, key, j0);
   __syncthreads();
-  uint32_t cnt = 0;
+  uint32_t cnt = 0, hi = 0;
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
-    const bool m = j0 + q < a.n && (key[q] >> 21) == b0;
+    const bool in = j0 + q < a.n;
+    const uint32_t d0 = key[q] >> 21;
+    const bool m = in && d0 == b0;
     if (m) atomicAdd(&hist[(key[q] >> 10) & 2047u], 1u);
     cnt += m ? 1u : 0u;
+    hi += (in && d0 > b0) ? 1u : 0u;
   }
   uint32_t tot;
-  const uint32_t off = scan256(cnt, sh, tot);
-  if (tid == 0) s_base = tot ? atomicAdd(a.ncand + row, tot) : 0u;
-  __syncthreads();
-  uint32_t* cand = a.cand + (int64_t)row * a.n + s_base + off;
+  const uint32_t off = scan256((cnt << 16) | hi, sh, tot);
+  uint32_t* cand = a.cand + (int64_t)row * a.n + (int64_t)c * CH + (off >> 16);
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
     if (j0 + q < a.n && (key[q] >> 21) == b0) *cand++ = key[q];
+  }
+  if (tid == 0) {
+    uint32_t* cc = a.chunk_cnt + ((int64_t)row * a.chunks + c) * 2;
+    cc[0] = tot & 0xFFFFu;
+    cc[1] = tot >> 16;
   }
   uint32_t* h1 = a.hist1 + (int64_t)row * kHistBins;
   for (int i = tid; i < kHistBins; i += kWideThreads) {
@@ -466,12 +481,34 @@ __global__ __launch_bounds__(kWideThreads) void k_select_wide_a(const WideSelect
   }
 }
 
+// Candidate f of the row in chunk order: its chunk (by binary search over the
+// exclusive prefix `cpre` of the chunks' candidate counts) and its key.
+KC_INLINE uint32_t flat_cand(const WideSelectArgs& a, int row, int CH, const uint32_t* cpre, int chunks,
+                             uint32_t f, int& cc) {
+  int lo = 0, hi = chunks - 1;   // last chunk whose prefix is <= f
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cpre[mid] <= f) lo = mid;
+    else hi = mid - 1;
+  }
+  cc = lo;
+  return a.cand[(int64_t)row * a.n + (int64_t)lo * CH + (f - cpre[lo])];
+}
+
+// Pass B (chunks x rows): every chunk resolves digits 1 and 2 (digit 2 over
+// the row's candidates), which fixes the k-th largest key T and how many keys
+// equal to T are taken; it counts the keys > T and == T of the chunks before
+// it (their keys above b0 plus their candidates compared with T) and writes
+// its own selected indices in index order.
 template <int CH>
 __global__ __launch_bounds__(kWideThreads) void k_select_wide_b(const WideSelectArgs a) {
   constexpr int kPerThread = CH / kWideThreads;
+  constexpr int kMaxCh = 1024;   // chunks per row on this path
   __shared__ uint32_t hist[1024];
+  __shared__ uint32_t cpre[kMaxCh];
   __shared__ uint32_t sh[8], s_sel[2];
   const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  const int chunks = a.chunks;
   const float* src = a.src + (int64_t)row * a.row_stride;
   uint32_t need = (uint32_t)a.k, above;
   const uint32_t b0 = find_bin256<kHistBins>(a.hist0 + (int64_t)row * kHistBins, need, sh, s_sel, above);
@@ -479,59 +516,51 @@ __global__ __launch_bounds__(kWideThreads) void k_select_wide_b(const WideSelect
   const uint32_t b1 = find_bin256<kHistBins>(a.hist1 + (int64_t)row * kHistBins, need, sh, s_sel, above);
   need -= above;
   const uint32_t p01 = (b0 << 11) | b1;
+  // the chunks' counts: keys above b0 of the chunks before this one, and the
+  // exclusive prefix of the candidate counts (flattened candidate index)
+  const uint32_t* ccnt = a.chunk_cnt + (int64_t)row * chunks * 2;
+  uint32_t nc[kMaxCh / kWideThreads], abv = 0, csum = 0;
+#pragma unroll
+  for (int u = 0; u < kMaxCh / kWideThreads; ++u) {
+    const int i = tid * (kMaxCh / kWideThreads) + u;
+    nc[u] = i < chunks ? ccnt[2 * i + 1] : 0u;
+    abv += (i < chunks && i < c) ? ccnt[2 * i] : 0u;
+    csum += nc[u];
+  }
+  uint32_t ncand;
+  uint32_t run = scan256(csum, sh, ncand);
+#pragma unroll
+  for (int u = 0; u < kMaxCh / kWideThreads; ++u) {
+    const int i = tid * (kMaxCh / kWideThreads) + u;
+    if (i < kMaxCh) cpre[i] = run;
+    run += nc[u];
+  }
+  uint32_t above_before;
+  scan256(abv, sh, above_before);   // total over the block: keys above b0 before chunk c
   for (int i = tid; i < 1024; i += kWideThreads) hist[i] = 0u;
   __syncthreads();
-  const uint32_t nc = a.ncand[row];
-  const uint32_t* cand = a.cand + (int64_t)row * a.n;
-  for (uint32_t i = tid; i < nc; i += kWideThreads) {
-    const uint32_t key = cand[i];
+  for (uint32_t f = tid; f < ncand; f += kWideThreads) {
+    int cc;
+    const uint32_t key = flat_cand(a, row, CH, cpre, chunks, f, cc);
     if ((key >> 10) == p01) atomicAdd(&hist[key & 1023u], 1u);
   }
   __syncthreads();
   const uint32_t b2 = find_bin256<1024>(hist, need, sh, s_sel, above);
   need -= above;
   const uint32_t T = (p01 << 10) | b2;   // the k-th largest key; `need` keys == T are taken
-  uint32_t key[kPerThread];
-  int j0;
-  chunk_keys<CH>(a, src, c, key, j0);
-  uint32_t gt = 0, eq = 0;
-#pragma unroll
-  for (int q = 0; q < kPerThread; ++q) {
-    const bool in = j0 + q < a.n;
-    gt += (in && key[q] > T) ? 1u : 0u;
-    eq += (in && key[q] == T) ? 1u : 0u;
-  }
-  uint32_t tot;
-  scan256((gt << 16) | eq, sh, tot);
-  if (tid == 0) {
-    uint32_t* cc = a.chunk_cnt + ((int64_t)row * a.chunks + c) * 2;
-    cc[0] = tot >> 16;
-    cc[1] = tot & 0xFFFFu;
-    if (c == 0) {
-      a.thr[row * 2] = T;
-      a.thr[row * 2 + 1] = need;
-    }
-  }
-}
-
-template <int CH>
-__global__ __launch_bounds__(kWideThreads) void k_select_wide_c(const WideSelectArgs a) {
-  constexpr int kPerThread = CH / kWideThreads;
-  __shared__ uint32_t sh[8];
-  const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
-  const float* src = a.src + (int64_t)row * a.row_stride;
-  const uint32_t T = a.thr[row * 2], need = a.thr[row * 2 + 1];
-  // counts of the chunks before this one (chunk counts fit 16 bits each;
-  // their sums are kept in 32-bit halves separately)
-  uint32_t gtb = 0, eqb = 0;
-  const uint32_t* cc = a.chunk_cnt + (int64_t)row * a.chunks * 2;
-  for (int i = tid; i < c; i += kWideThreads) {
-    gtb += cc[2 * i];
-    eqb += cc[2 * i + 1];
+  // candidates of the chunks before this one: > T and == T
+  const uint32_t fend = c < chunks ? cpre[c] : ncand;
+  uint32_t gtc = 0, eqc = 0;
+  for (uint32_t f = tid; f < fend; f += kWideThreads) {
+    int cc;
+    const uint32_t key = flat_cand(a, row, CH, cpre, chunks, f, cc);
+    gtc += key > T ? 1u : 0u;
+    eqc += key == T ? 1u : 0u;
   }
   uint32_t gt_before, eq_before;
-  scan256(gtb, sh, gt_before);
-  scan256(eqb, sh, eq_before);
+  scan256(gtc, sh, gt_before);
+  scan256(eqc, sh, eq_before);
+  gt_before += above_before;
   uint32_t key[kPerThread];
   int j0;
   chunk_keys<CH>(a, src, c, key, j0);
@@ -568,16 +597,13 @@ hipError_t launch_wide_ch(const WideSelectArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_select_wide_b<CH>, grid, dim3(kWideThreads), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_select_wide_c<CH>, grid, dim3(kWideThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_select_wide(const WideSelectArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
   const int ch = wide_chunk(a.n);
-  if (a.chunks != (a.n + ch - 1) / ch || a.chunks > 65535) return hipErrorInvalidValue;
+  if (a.chunks != (a.n + ch - 1) / ch || a.chunks > 1024) return hipErrorInvalidValue;
   return ch == kWideChunkShort ? launch_wide_ch<kWideChunkShort>(a, s) : launch_wide_ch<kWideChunk>(a, s);
 }
 
