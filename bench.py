@@ -42,8 +42,7 @@ KERNEL_SOURCES = {"prefill_flash": "prefill.hip", "prefill_pool": "prefill.hip",
                   "prefill_sparse": "prefill.hip", "decode_splitk": "decode.hip",
                   "decode_combine": "decode.hip", "decode_pool": "decode.hip",
                   "reuse_decode": "decode.hip", "topk_select": "select.hip",
-                  "topk_select_wide_a": "select.hip", "topk_select_wide_b": "select.hip",
-                  "topk_select_wide_c": "select.hip"}
+                  "topk_select_wide_a": "select.hip", "topk_select_wide_b": "select.hip"}
 COPY_BYTES = 1 << 30  # the calibration copy reads and writes this many bytes
 
 
