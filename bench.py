@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode attn µs/layer + HBM GB/s at 32k/128k ctx; prefill attn TFLOP/s"
 HBM_PEAK_GBS = 8000.0
+FUSED_ANCHOR = False   # --anchor-decode fused: the sections' anchor layers use the one-launch kernel
 MFMA16_PEAK_TFLOPS = 2500.0  # dense bf16 and fp16 MFMA peak
 # HBM traffic of the kernels, read by rocprofv3 counters and stored as text
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_kernels_llama8b.md")
@@ -42,7 +43,8 @@ KERNEL_SOURCES = {"prefill_flash": "prefill.hip", "prefill_pool": "prefill.hip",
                   "prefill_sparse": "prefill.hip", "decode_splitk": "decode.hip",
                   "decode_combine": "decode.hip", "decode_pool": "decode.hip",
                   "reuse_decode": "decode.hip", "topk_select": "select.hip",
-                  "topk_select_wide_a": "select.hip", "topk_select_wide_b": "select.hip"}
+                  "topk_select_wide_a": "select.hip", "topk_select_wide_b": "select.hip",
+                  "anchor_fused": "decode.hip"}
 COPY_BYTES = 1 << 30  # the calibration copy reads and writes this many bytes
 
 
@@ -99,17 +101,33 @@ def build_decode(workload, torch, K, synth, configs, dtype="bf16"):
 
     ws_d = K.workspace(K.OP_DENSE_DECODE, sh)
     lse = torch.empty(layers[0][0].shape[:2], dtype=torch.float32, device="cuda")
+    # the one-launch anchor decode, where its workgroups fit on the GPU at once
+    ws_f = K.workspace(K.OP_ANCHOR_DECODE_FUSED, sh, cfg.topk)
+    a0 = cfg.anchors[0]
+    st = K.kascade_anchor_decode_fused(sh, *layers[a0], cfg.topk, out, None, idx[a0], None, 0, ws_f,
+                                       ws_f.numel())
+    if st not in (K.KASCADE_OK, K.KASCADE_ERR_SHAPE):
+        K.check(st, "anchor_decode_fused")
+    fused_ok = st == K.KASCADE_OK
+
+    def anchor(l, q, k, v, fused):
+        if fused:
+            K.check(K.kascade_anchor_decode_fused(sh, q, k, v, cfg.topk, out, None, idx[l], None, 0, ws_f,
+                                                  ws_f.numel()), "anchor_decode_fused")
+        else:
+            K.check(K.kascade_anchor_decode(sh, q, k, v, cfg.topk, out, None, idx[l], None,
+                                            ws_a, ws_a.numel()), "anchor_decode")
 
     def run(kind=None):
         if kind == "dense":   # the GPU's own dense decode on every layer (comparison)
             for q, k, v in layers:
                 K.check(K.kascade_dense_decode(sh, q, k, v, out, lse, ws_d, ws_d.numel()), "dense_decode")
             return
+        fused = kind == "anchor_fused" or (kind in (None, "anchor") and FUSED_ANCHOR and fused_ok)
         for l, (q, k, v) in enumerate(layers):
             if l in cfg.anchors:
-                if kind in (None, "anchor"):
-                    K.check(K.kascade_anchor_decode(sh, q, k, v, cfg.topk, out, None, idx[l], None,
-                                                    ws_a, ws_a.numel()), "anchor_decode")
+                if kind in (None, "anchor", "anchor_fused"):
+                    anchor(l, q, k, v, fused)
             elif kind in (None, "reuse"):
                 K.check(K.kascade_reuse_decode(sh, q, k, v, cfg.topk, idx[anchor_of[l]], maps[l], out,
                                                ws_r, ws_r.numel()), "reuse_decode")
@@ -118,7 +136,7 @@ def build_decode(workload, torch, K, synth, configs, dtype="bf16"):
     n_reuse = L - n_anchor
     bytes_anchor, bytes_reuse, bytes_dense = decode_bytes(cfg)
     return dict(cfg=cfg, run=run, n_anchor=n_anchor, n_reuse=n_reuse, bytes_anchor=bytes_anchor,
-                bytes_reuse=bytes_reuse, bytes_dense=bytes_dense, layers=layers, maps=maps)
+                bytes_reuse=bytes_reuse, bytes_dense=bytes_dense, layers=layers, maps=maps, fused_ok=fused_ok)
 
 
 def prefill_reuse_flops(torch, K, idx_by_anchor, anchor_of, maps, layers_reuse, N, n_kv, group, d):
@@ -246,16 +264,27 @@ def build_qwen3(torch, K, synth, configs, dtype="bf16"):
     sh_max = K.make_shape(qs[0][0], layers[0][1], n_max)
     ws_a = K.workspace(K.OP_ANCHOR_DECODE, sh_max, k_last)
     ws_r = K.workspace(K.OP_REUSE_DECODE, sh_max, k_last)
+    ws_f = K.workspace(K.OP_ANCHOR_DECODE_FUSED, sh_max, k_last)
     didx = {a: torch.empty((1, Hkv, k_last), dtype=torch.int32, device="cuda") for a in anchors}
     out_d = torch.empty_like(qs[0][0])
+    a0 = anchors[0]
+    st0 = K.kascade_anchor_decode_fused(sh_max, qs[steps - 1][a0], layers[a0][1], layers[a0][2], k_last, out_d,
+                                        None, didx[a0], None, 0, ws_f, ws_f.numel())
+    if st0 not in (K.KASCADE_OK, K.KASCADE_ERR_SHAPE):
+        K.check(st0, "anchor_decode_fused")
+    fused_ok = st0 == K.KASCADE_OK
 
     def decode(st, kind=None):
         n_cur = N0 + st + 1
         kk = dec_k(n_cur)
+        fused = kind == "anchor_fused" or (kind in (None, "anchor") and FUSED_ANCHOR and fused_ok)
         for l, (_, k, v) in enumerate(layers):
             shd = K.make_shape(qs[st][l], k, n_cur)
             if l in anchors:
-                if kind in (None, "anchor"):
+                if kind in (None, "anchor", "anchor_fused") and fused:
+                    K.check(K.kascade_anchor_decode_fused(shd, qs[st][l], k, v, kk, out_d, None, didx[l], None,
+                                                          0, ws_f, ws_f.numel()), "anchor_decode_fused")
+                elif kind in (None, "anchor"):
                     K.check(K.kascade_anchor_decode(shd, qs[st][l], k, v, kk, out_d, None, didx[l], None,
                                                     ws_a, ws_a.numel()), "anchor_decode")
             elif kind in (None, "reuse"):
@@ -268,7 +297,8 @@ def build_qwen3(torch, K, synth, configs, dtype="bf16"):
         return prefill_reuse_flops(torch, K, tidx, anchor_of, maps, reuse_layers, N0, Hkv, G, d)
 
     return dict(cfg=cfg, anchors=anchors, S=S, prefill=prefill, decode=decode, steps=steps, N0=N0,
-                n_anchor=len(anchors), n_reuse=L - len(anchors), reuse_flops=reuse_flops, dec_k=dec_k)
+                n_anchor=len(anchors), n_reuse=L - len(anchors), reuse_flops=reuse_flops, dec_k=dec_k,
+                fused_ok=fused_ok)
 
 
 # ---------------------------------------------------------------------------
@@ -405,7 +435,7 @@ def cpu_prefill_sample(pre, oracle):
 def kernel_source_hash(kernel):
     """sha256 over the sources a kernel is built from (its .hip and the shared headers)."""
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel], "common.h", "kernels.h", "paged.h"):
+    for f in (KERNEL_SOURCES[kernel], "common.h", "kernels.h", "paged.h", "radix.h"):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -478,7 +508,24 @@ def traffic_probe(torch, K, synth, configs):
     K.check(K.kascade_reuse_decode(sh, *lay[1], cfg.topk, idx, maps[1], out, ws_r, ws_r.numel()),
             "reuse_decode")
     torch.cuda.synchronize()
+    del lay, out, ws_a, ws_r, idx
     log("decode done")
+    # the one-launch anchor decode: one layer at 32K context, batch 1
+    cfg = configs.LLAMA_DECODE_32K
+    N = cfg.ctx_len
+    lin = synth.heavy_lineages(cfg.seed, cfg.n_layers, cfg.n_kv_heads, N, cfg.heavy, cfg.drift)
+    maps = synth.head_maps(cfg.seed, cfg.n_layers, cfg.anchors, cfg.n_kv_heads, cfg.head_map_kind)
+    lay = synth.decode_layer(cfg.seed, 0, cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, N,
+                             synth.layer_heavy_sets(lin, 0, cfg.anchors, maps), cfg.alpha, cfg.dtype,
+                             device="cuda")
+    sh = K.make_shape(lay[0], lay[1], N)
+    ws_f = K.workspace(K.OP_ANCHOR_DECODE_FUSED, sh, cfg.topk)
+    idx = torch.empty((cfg.batch, cfg.n_kv_heads, cfg.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(lay[0])
+    K.check(K.kascade_anchor_decode_fused(sh, *lay, cfg.topk, out, None, idx, None, 0, ws_f, ws_f.numel()),
+            "anchor_decode_fused")
+    torch.cuda.synchronize()
+    log("fused decode done")
     print(json.dumps({"probe": "traffic", "copy_bytes": COPY_BYTES,
                       "hashes": {k: kernel_source_hash(k) for k in KERNEL_SOURCES}}), flush=True)
 
@@ -786,7 +833,8 @@ def qwen3_bench(torch, K, synth, configs, args, reps):
     last = steps - 1
     n_last = N0 + steps
     kind_us = {}
-    for kind, n in (("anchor", na), ("reuse", nr)):
+    kinds = (("anchor", na), ("reuse", nr)) + ((("anchor_fused", na),) if w["fused_ok"] else ())
+    for kind, n in kinds:
         g = capture_graph(torch, lambda kind=kind: w["decode"](last, kind))
         kind_us[kind] = pct(event_reps(torch, g.replay, reps), 1e3 / n)
         del g
@@ -808,6 +856,8 @@ def qwen3_bench(torch, K, synth, configs, args, reps):
         "decode_ms_512_steps": float(np.median(passes)),
         "decode_us_per_layer": pct(np.asarray(per_step), 1e3 / L),
         "decode_anchor_us_last_step": kind_us["anchor"], "decode_reuse_us_last_step": kind_us["reuse"],
+        "decode_anchor_fused_us_last_step": kind_us.get("anchor_fused"),
+        "anchor_decode_path": "fused" if FUSED_ANCHOR and w["fused_ok"] else "split",
         "decode_anchor_ideal_us": by_anchor / (HBM_PEAK_GBS * 1e9) * 1e6,
         "decode_reuse_ideal_us": by_reuse / (HBM_PEAK_GBS * 1e9) * 1e6,
         "decode_anchor_hbm_frac": by_anchor / (kind_us["anchor"]["median"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
@@ -841,7 +891,12 @@ def main():
                     help="element type of q, k, v and outputs (the workloads are defined in bf16)")
     ap.add_argument("--paged", action="store_true",
                     help="time decode and the reuse prefill over paged KV caches against contiguous caches")
+    ap.add_argument("--anchor-decode", choices=["split", "fused"], default="split",
+                    help="anchor decode layers of the timed sections: four launches (split) or the "
+                         "one-launch kernel where it fits (fused); both are timed per kind either way")
     args = ap.parse_args()
+    global FUSED_ANCHOR
+    FUSED_ANCHOR = args.anchor_decode == "fused"
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
@@ -894,12 +949,12 @@ def main():
     for s in ("decode32k", "decode128k"):
         if s in sections:
             w = work[s]
+            kinds = (None, "anchor", "reuse", "dense") + (("anchor_fused",) if w["fused_ok"] else ())
             if args.eager:
-                graphs[s] = {kind: (lambda kind=kind, w=w: w["run"](kind))
-                             for kind in (None, "anchor", "reuse", "dense")}
+                graphs[s] = {kind: (lambda kind=kind, w=w: w["run"](kind)) for kind in kinds}
             else:
                 graphs[s] = {kind: capture_graph(torch, lambda kind=kind, w=w: w["run"](kind)).replay
-                             for kind in (None, "anchor", "reuse", "dense")}
+                             for kind in kinds}
     log("decode graphs captured" if not args.eager else "eager decode")
 
     def run_section(s):
@@ -965,8 +1020,10 @@ def main():
         us_layer = float(np.median(sec_ms[s])) * 1e3 / L
         # each section and kind again, `reps` times, one synchronised replay each
         rep = {None: pct(event_reps(torch, graphs[s][None], reps), 1e3 / L)}
-        for kind, n in (("anchor", w["n_anchor"]), ("reuse", w["n_reuse"]), ("dense", L)):
-            rep[kind] = pct(event_reps(torch, graphs[s][kind], reps), 1e3 / n)
+        for kind, n in (("anchor", w["n_anchor"]), ("reuse", w["n_reuse"]), ("dense", L),
+                        ("anchor_fused", w["n_anchor"])):
+            if kind in graphs[s]:
+                rep[kind] = pct(event_reps(torch, graphs[s][kind], reps), 1e3 / n)
         per = {k: rep[k]["median"] for k in ("anchor", "reuse", "dense")}
         comps[s] = {
             "us_per_layer": us_layer,
@@ -976,6 +1033,11 @@ def main():
             "hbm_frac": by / (us_layer * L * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "anchor_us": per["anchor"], "reuse_us": per["reuse"],
             "anchor_us_reps": rep["anchor"], "reuse_us_reps": rep["reuse"],
+            # the one-launch anchor decode, per anchor layer (null where its
+            # workgroups do not all fit on the GPU at once)
+            "anchor_fused_us": rep["anchor_fused"]["median"] if "anchor_fused" in rep else None,
+            "anchor_fused_us_reps": rep.get("anchor_fused"),
+            "anchor_decode_path": "fused" if FUSED_ANCHOR and w["fused_ok"] else "split",
             "anchor_GBps": w["bytes_anchor"] / (per["anchor"] * 1e-6) / 1e9,
             "reuse_GBps": w["bytes_reuse"] / (per["reuse"] * 1e-6) / 1e9,
             "reuse_hbm_frac": w["bytes_reuse"] / (per["reuse"] * 1e-6) / 1e9 / HBM_PEAK_GBS,

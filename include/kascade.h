@@ -116,6 +116,37 @@ int kascade_anchor_decode(const kascade_shape* shape, const void* q, const void*
                           int32_t* topk_idx, float* pooled_out, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
+/* Anchor-layer decode in ONE launch (the same outputs as
+ * kascade_anchor_decode; [Explainer] "アンカーレイヤーと再利用レイヤー": full
+ * attention, then the exact Top-k of the pooled post-softmax probabilities).
+ * The split-K workgroups keep their scores in LDS and run the pooling and the
+ * exact selection themselves, separated by row-wide barriers, instead of the
+ * four launches of kascade_anchor_decode.  With the same split plan as
+ * kascade_anchor_decode the outputs are bitwise identical to it.
+ *   Arguments as kascade_anchor_decode, plus
+ *   max_polls  polls of each row barrier before the call gives up
+ *              (0 = the default, 2^18: far above any normal wait).
+ * Workspace (kascade_workspace_bytes op 6): unlike the other calls its first
+ * 65792 bytes carry state, at the same offsets for every shape: bytes 0..3
+ * are a status word and bytes 256..65791 row barrier counters, all of which
+ * must be ZERO before the first call on a workspace (e.g. allocate it
+ * zeroed); every call leaves the counters zero, so one workspace serves
+ * calls of any shape it is large enough for.
+ * A call whose barrier gave up sets status bit 0; its outputs are then
+ * undefined (the caller reads the word after synchronising and clears it).
+ * Requirements: BF16 or F16 (else KASCADE_ERR_DTYPE), not paged; all
+ * workgroups of the launch must be resident on the GPU at once:
+ * batch * n_kv_heads * splits <= CUs (one workgroup per CU; splits as in
+ * kascade_anchor_decode, at most 256) and the split's scores must fit in LDS,
+ * else KASCADE_ERR_SHAPE (the 32K and 64K single-sequence decodes of the
+ * benchmark qualify, 128K x 4 does not).  Other work running on the GPU at
+ * the same time delays the launch's workgroups; that is safe (the barriers
+ * wait up to max_polls). */
+int kascade_anchor_decode_fused(const kascade_shape* shape, const void* q, const void* k,
+                                const void* v, int32_t topk, void* out, float* lse_out,
+                                int32_t* topk_idx, float* pooled_out, uint32_t max_polls,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Reuse-layer decode.  [Explainer] "アンカーレイヤーと再利用レイヤー" (attention
  * on the preceding anchor's selected keys only) and "ヘッドリマッピング" (each KV
  * head g of the reuse layer uses the list of anchor KV head head_map[g]).
@@ -274,8 +305,9 @@ int kascade_head_maps(int32_t L, int32_t n_kv_heads, const float* sim, const int
 /* ---- helpers ----------------------------------------------------------- */
 
 /* op: 0 anchor_decode, 1 reuse_decode, 2 anchor_prefill, 3 reuse_prefill,
- * 4 dense_decode, 5 dense_prefill.  Returns the workspace bytes the op
- * needs for this shape (0 if none), or 0 for an invalid op/shape. */
+ * 4 dense_decode, 5 dense_prefill, 6 anchor_decode_fused.  Returns the
+ * workspace bytes the op needs for this shape (0 if none), or 0 for an
+ * invalid op/shape. */
 size_t kascade_workspace_bytes(int op, const kascade_shape* shape, int32_t topk,
                                const kascade_topk_rule* rule);
 
@@ -317,7 +349,8 @@ int kascade_dense_prefill(const kascade_shape* shape, const void* q, const void*
 enum {
   KASCADE_K_DECODE_SPLITK = 0, KASCADE_K_DECODE_COMBINE = 1, KASCADE_K_DECODE_POOL = 2,
   KASCADE_K_TOPK_SELECT = 3, KASCADE_K_REUSE_DECODE = 4, KASCADE_K_PREFILL_FLASH = 5,
-  KASCADE_K_PREFILL_POOL = 6, KASCADE_K_PREFILL_SPARSE = 7, KASCADE_K_COUNT = 8
+  KASCADE_K_PREFILL_POOL = 6, KASCADE_K_PREFILL_SPARSE = 7, KASCADE_K_ANCHOR_FUSED = 8,
+  KASCADE_K_COUNT = 9
 };
 int kascade_kernel_timer_enable(int kernel_id, int enable);
 int kascade_kernel_timer_read(int kernel_id, double* total_ms, int64_t* launches);

@@ -487,6 +487,43 @@ PrefillArgs prefill_args(const kascade_shape* s, const void* q, const void* k, c
 
 }  // namespace
 
+// ---- fused anchor decode workspace ----------------------------------------------
+// [status word, 256 B][row barrier counters of kFusedMaxRows rows][partials
+// for up to kFusedMaxSplits splits][hist0][hist1][candidates][split counts].
+// The state (status word and counters) sits at the same offsets for every
+// shape, so a workspace serves calls of different shapes; it must be zero
+// before the first call and every call leaves the counters zero (a call that
+// gave up waiting sets status bit 0).
+constexpr int kFusedMaxSplits = 256;            // one split per thread of the select phases
+constexpr int kFusedMaxRows = 256;              // rows x splits <= resident workgroups
+constexpr uint32_t kFusedDefaultPolls = 1u << 18;
+
+struct FusedPlan {
+  size_t off_status, off_sync, off_part, off_hist0, off_hist1, off_cand, off_cnt, total;
+};
+
+FusedPlan plan_fused(const kascade_shape* s) {
+  FusedPlan p;
+  const size_t rows = (size_t)s->batch * s->n_kv_heads, BH = (size_t)s->batch * s->n_q_heads;
+  size_t o = 0;
+  p.off_status = o;
+  o += 256;
+  p.off_sync = o;
+  o += align256((size_t)kFusedMaxRows * kFusedSyncWords * 4);
+  p.off_part = o;
+  o += align256(BH * kFusedMaxSplits * (size_t)(s->head_dim + 2) * 4);
+  p.off_hist0 = o;
+  o += align256(rows * 2048 * 4);
+  p.off_hist1 = o;
+  o += align256(rows * 2048 * 4);
+  p.off_cand = o;
+  o += align256(rows * (size_t)s->ctx_len * 4);
+  p.off_cnt = o;
+  o += align256(rows * kFusedMaxSplits * 2 * 4);
+  p.total = o;
+  return p;
+}
+
 extern "C" {
 
 const char* kascade_version(void) { return "kascade-mi355x 0.1"; }
@@ -523,6 +560,7 @@ size_t kascade_workspace_bytes(int op, const kascade_shape* s, int32_t topk,
     case 0: return plan_decode(s, s->ctx_len, true, true, 0).total;
     case 1: return topk >= 1 ? plan_decode(s, topk, false, false, 0).total : 0;
     case 4: return plan_decode(s, s->ctx_len, false, false, 0).total;
+    case 6: return plan_fused(s).total;
     case 2: return check_rule(rule) == KASCADE_OK ? plan_prefill(s, rule, true).total : 0;
     case 3: return 0;
     case 5: return 0;
@@ -694,6 +732,59 @@ int kascade_anchor_decode(const kascade_shape* s, const void* q, const void* k, 
                           float* pooled_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   return anchor_decode_impl(s, nullptr, q, k, v, topk, out, lse_out, topk_idx, pooled_out, ws,
                             ws_bytes, stream);
+}
+
+int kascade_anchor_decode_fused(const kascade_shape* s, const void* q, const void* k,
+                                const void* v, int32_t topk, void* out, float* lse_out,
+                                int32_t* topk_idx, float* pooled_out, uint32_t max_polls, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(s, false);
+  if (st) return st;
+  if (s->dtype == KASCADE_F32) return KASCADE_ERR_DTYPE;
+  if (!q || !k || !v || !out || !topk_idx) return KASCADE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return KASCADE_ERR_ARG;
+  if (topk < 1 || topk > s->ctx_len) return KASCADE_ERR_TOPK;
+  const FusedPlan fp = plan_fused(s);
+  if (!ws || ws_bytes < fp.total) return KASCADE_ERR_WORKSPACE;
+  DeviceInfo* dev = nullptr;
+  if ((st = device_setup(&dev))) return st;
+  // the split plan of the spilling anchor pass (so the two paths split alike)
+  DecodePlan p;
+  if ((st = plan_decode_dev(dev, s, s->ctx_len, false, true, true, false, &p))) return st;
+  if (p.kps > decode_max_kps(s, true, false) || p.splits > kFusedMaxSplits) return KASCADE_ERR_SHAPE;
+  // every workgroup must be resident at once: the row barriers wait for all
+  // of a row's splits
+  const int G = s->n_q_heads / s->n_kv_heads;
+  int blocks = 0;
+  size_t static_lds = 0;
+  hipError_t e = anchor_fused_attrs(s->dtype, G, p.kps, &blocks, &static_lds);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return KASCADE_ERR_HIP;
+  }
+  const int64_t rows = (int64_t)s->batch * s->n_kv_heads;
+  if (rows > kFusedMaxRows || rows * p.splits > (int64_t)dev->cus * blocks) return KASCADE_ERR_SHAPE;
+  if (dev->lds_per_cu > 0 && static_lds + anchor_fused_dyn_lds(G, p.kps) > dev->lds_per_cu)
+    return KASCADE_ERR_SHAPE;
+  char* w = reinterpret_cast<char*>(ws);
+  FusedDecodeArgs f;
+  memset(&f, 0, sizeof(f));
+  f.d = decode_args(s, q, k, v, s->ctx_len, p, w);
+  f.d.part = reinterpret_cast<float*>(w + fp.off_part);
+  f.out = out;
+  f.lse_out = lse_out;
+  f.idx = topk_idx;
+  f.pooled = pooled_out;
+  f.k = topk;
+  f.sync = reinterpret_cast<uint32_t*>(w + fp.off_sync);
+  f.status = reinterpret_cast<uint32_t*>(w + fp.off_status);
+  f.spin_limit = max_polls ? max_polls : kFusedDefaultPolls;
+  f.hist0 = reinterpret_cast<uint32_t*>(w + fp.off_hist0);
+  f.hist1 = reinterpret_cast<uint32_t*>(w + fp.off_hist1);
+  f.cand = reinterpret_cast<uint32_t*>(w + fp.off_cand);
+  f.cnt = reinterpret_cast<uint32_t*>(w + fp.off_cnt);
+  e = timed(KASCADE_K_ANCHOR_FUSED, stream, [&] { return launch_anchor_fused(f, s->dtype, stream); });
+  return hip_status(e);
 }
 
 int kascade_reuse_decode(const kascade_shape* s, const void* q, const void* k, const void* v,

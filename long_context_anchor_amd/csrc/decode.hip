@@ -20,6 +20,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "paged.h"
+#include "radix.h"
 
 namespace kc {
 
@@ -322,21 +323,18 @@ KC_INLINE void slots_from_own(uint32_t own_v, uint32_t (&out)[G]) {
   }
 }
 
-template <int G, bool GATHER, bool SPILL, bool PAGED = false, bool HALF = false, int kRows = 4>
-__global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeArgs a) {
+// The split-K pass of one workgroup up to its four waves' partial states in
+// LDS (s_m, s_l, s_o per wave and head).  KEEP: the split's scores stay in
+// LDS (s_list, after the row list when paged) instead of being written out.
+template <int G, bool GATHER, bool SPILL, bool PAGED, bool HALF, int kRows, bool KEEP>
+KC_INLINE void splitk_slots_core(const DecodeArgs& a, int32_t* s_list, float (&s_m)[4][G],
+                                 float (&s_l)[4][G], float (&s_o)[4][G][128]) {
   typedef Fmt16<HALF> F;   // bf16 or fp16 elements
-  constexpr int D = 128;
   constexpr int LG = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
   static_assert(kRows % 4 == 0, "list entries are read four at a time");
   constexpr int kWaveRows = 4 * kRows;  // rows per wave per step
   // the split's rows go through an LDS list when they are gathered or paged
   constexpr bool LIST = GATHER || PAGED;
-  __shared__ float s_m[4][G];
-  __shared__ float s_l[4][G];
-  __shared__ float s_o[4][G][D];
-  // dynamic LDS: the row list (kps + kListPad entries: cache positions, or
-  // physical row numbers when paged), then the spilled scores
-  extern __shared__ __align__(16) int32_t s_list[];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -521,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
     }
   }
 
-  if (SPILL) {
+  if (SPILL && !KEEP) {
     __syncthreads();
     const int n = k1 - k0;
     for (int hh = 0; hh < G; ++hh) {
@@ -592,6 +590,20 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
       *reinterpret_cast<float2*>(&s_o[wave][k ^ own][li * 8 + e]) = make_float2(v[n], v[n + 1]);
     }
   }
+}
+
+template <int G, bool GATHER, bool SPILL, bool PAGED = false, bool HALF = false, int kRows = 4>
+__global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeArgs a) {
+  constexpr int D = 128;
+  __shared__ float s_m[4][G];
+  __shared__ float s_l[4][G];
+  __shared__ float s_o[4][G][D];
+  // dynamic LDS: the row list (kps + kListPad entries: cache positions, or
+  // physical row numbers when paged), then the spilled scores
+  extern __shared__ __align__(16) int32_t s_list[];
+  splitk_slots_core<G, GATHER, SPILL, PAGED, HALF, kRows, false>(a, s_list, s_m, s_l, s_o);
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
   __syncthreads();
   for (int x = tid; x < G * D; x += kThreads) {
     const int hh = x / D, dd = x % D;
@@ -619,7 +631,27 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
 // with kBatch splits' loads issued up front, then the PARTS partial states of
 // each column meet once in LDS (sm, sl, so hold NT floats each) and threads
 // < D write the normalised column; thread 0 writes the lse.
-template <typename T, int NT, int kBatch>
+// Words exchanged between the workgroups of one launch (the fused anchor
+// decode): relaxed atomics at agent scope, which gfx950 issues as stores
+// written through to the device's coherence point and loads that read it, so
+// a reader needs no cache invalidate and a writer no cache writeback.
+KC_INLINE void st_coh(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+KC_INLINE void st_coh(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+KC_INLINE float ld_coh(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+KC_INLINE uint32_t ld_coh(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <bool COH>
+KC_INLINE float ld_part(const float* p) {
+  if constexpr (COH) return ld_coh(p);
+  else return *p;
+}
+
+template <typename T, int NT, int kBatch, bool COH = false>
 KC_INLINE void merge_splits(const float* part, int S, int64_t bh, void* out, float* lse2,
                             float* lse_out, float* sm, float* sl, float* so) {
   constexpr int D = Elem<T>::D;
@@ -635,9 +667,9 @@ KC_INLINE void merge_splits(const float* part, int S, int64_t bh, void* out, flo
     for (int u = 0; u < kBatch; ++u) {
       const int s = s0 + u * PARTS;
       const float* ps = p + (int64_t)min(s, S - 1) * (D + 2);
-      mv[u] = s < S ? ps[0] : kNegInf;
-      lv[u] = ps[1];
-      ov[u] = ps[2 + dd];
+      mv[u] = s < S ? ld_part<COH>(ps) : kNegInf;
+      lv[u] = ld_part<COH>(ps + 1);
+      ov[u] = ld_part<COH>(ps + 2 + dd);
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -784,6 +816,314 @@ __global__ __launch_bounds__(256) void k_decode_pool(const PoolDecodeArgs a) {
   }
 }
 
+// ---- fused anchor decode --------------------------------------------------
+//
+// One launch per anchor layer: grid (splits, Hkv, B) of workgroups that are
+// all resident at once (the host checks the grid against the GPU's resident
+// slots).  A row = the splits of one (batch, KV head).
+//   phase 1  the split-K pass of the split (scores kept in LDS); its
+//            partial (m, l, o) per head is published; split 0 clears the
+//            row's two histograms;                          -> row barrier 1
+//   phase 2  every workgroup merges the row's (m, l) into each head's lse,
+//            pools its keys' probabilities over the G heads into order keys
+//            (LDS) and adds its digit-0 histogram to the row's; arrives;
+//            split s then merges the splits of query heads s, s + S, ... of
+//            the group into out / lse_out;                  -> row barrier 2
+//   phase 3  digit 0's bin b0 from the row histogram; the split's keys above
+//            b0 are counted and its keys in b0 (the candidates) stored at its
+//            own offset, with their digit-1 histogram added to the row's;
+//                                                           -> row barrier 3
+//   phase 4  digits 1 and 2 fix the k-th largest key T and how many keys
+//            equal to T are taken; the counts of the earlier splits give the
+//            split's output offset; its indices are written in index order.
+// A barrier is a per-row counter: each workgroup adds one after its
+// exchanged stores are complete (vmcnt 0) and thread 0 polls the counter a
+// bounded number of times; a workgroup that gives up sets status bit 0 and
+// skips its remaining phases (it still arrives, so the others are not held
+// longer).  The last workgroup of the row to leave clears the row's counters.
+
+// Thread 0 adds the workgroup to the row's barrier once every thread's
+// exchanged stores have completed.
+KC_INLINE void row_arrive(uint32_t* ctr) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits until the row's counter reaches target; false (uniform over the
+// workgroup) if thread 0 gave up after `limit` polls.
+KC_INLINE bool row_wait(const uint32_t* ctr, uint32_t target, uint32_t limit, uint32_t* status,
+                        uint32_t* s_ok) {
+  if (threadIdx.x == 0) {
+    uint32_t ok = 1u, n = 0;
+    while (ld_coh(ctr) < target) {
+      if (++n > limit) {
+        ok = 0u;
+        atomicOr(status, 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    *s_ok = ok;
+  }
+  __syncthreads();
+  return *s_ok != 0u;
+}
+
+// Candidate f of the row in split order: its split by binary search over the
+// exclusive prefix of the splits' candidate counts, then its key.
+KC_INLINE uint32_t fused_cand(const uint32_t* cand_row, const uint32_t* cpre, int S, int kps, uint32_t f) {
+  int lo = 0, hi = S - 1;   // last split whose prefix is <= f
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cpre[mid] <= f) lo = mid;
+    else hi = mid - 1;
+  }
+  return ld_coh(cand_row + (int64_t)lo * kps + (f - cpre[lo]));
+}
+
+template <int G, bool HALF>
+__global__ __launch_bounds__(kThreads) void k_anchor_fused(const FusedDecodeArgs f) {
+  typedef typename std::conditional<HALF, _Float16, uint16_t>::type T;
+  constexpr int D = 128;
+  constexpr int NB = 2048;
+  __shared__ float s_m[4][G];
+  __shared__ float s_l[4][G];
+  __shared__ float s_o[4][G][D];
+  __shared__ uint32_t s_hist[NB];          // histograms; merge scratch in phase 2
+  __shared__ uint32_t s_cpre[kThreads];    // exclusive prefix of the splits' candidate counts
+  __shared__ uint32_t sh[8], s_sel[2], s_ok;
+  __shared__ float s_lse[G];
+  extern __shared__ __align__(16) int32_t s_list[];   // scores [G][kps + kSpillPad]
+  const DecodeArgs& a = f.d;
+
+  splitk_slots_core<G, false, true, false, HALF, 4, true>(a, s_list, s_m, s_l, s_o);
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int S = a.n_splits, kps = a.keys_per_split, N = a.n_keys;
+  const int k0 = split * kps;
+  const int n = min(N, k0 + kps) - k0;
+  const int64_t row = (int64_t)b * a.Hkv + g;
+  uint32_t* ctr = f.sync + row * kFusedSyncWords;
+  uint32_t* h0 = f.hist0 + row * NB;
+  uint32_t* h1 = f.hist1 + row * NB;
+  uint32_t* cand_row = f.cand + row * N;
+  uint32_t* cnt_row = f.cnt + row * S * 2;
+  float* sc = reinterpret_cast<float*>(s_list);
+  uint32_t* keys = reinterpret_cast<uint32_t*>(s_list);   // order keys over head 0's scores
+  const int sstride = kps + kSpillPad;
+  __syncthreads();
+
+  // phase 1: the split's partial state per head (as the split-K epilogue)
+  for (int x = tid; x < G * D; x += kThreads) {
+    const int hh = x / D, dd = x % D;
+    float M = kNegInf;
+    for (int q = 0; q < 4; ++q) M = fmaxf(M, s_m[q][hh]);
+    float L = 0.f, O = 0.f;
+    if (M != kNegInf) {
+      for (int q = 0; q < 4; ++q) {
+        const float w = exp2f_fast(s_m[q][hh] - M);
+        L = fmaf(s_l[q][hh], w, L);
+        O = fmaf(s_o[q][hh][dd], w, O);
+      }
+    }
+    float* pp = a.part + (((int64_t)b * a.Hq + g * G + hh) * S + split) * (D + 2);
+    st_coh(pp + 2 + dd, O);
+    if (dd == 0) {
+      st_coh(pp, M);
+      st_coh(pp + 1, L);
+    }
+  }
+  if (split == 0) {
+    for (int i = tid; i < NB; i += kThreads) {
+      st_coh(h0 + i, 0u);
+      st_coh(h1 + i, 0u);
+    }
+  }
+  row_arrive(ctr);
+  bool ok = row_wait(ctr, (uint32_t)S, f.spin_limit, f.status, &s_ok);
+
+  // phase 2: lse of the group's heads (wave w: heads w, w + 4), pooled keys
+  // and the digit-0 histogram (the same arithmetic as the pooling kernel)
+  if (ok) {
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int hh = wave; hh < G; hh += 4) {
+      const float* p = a.part + ((int64_t)b * a.Hq + g * G + hh) * S * (D + 2);
+      float M = kNegInf, L = 0.f;
+      for (int s2 = lane; s2 < S; s2 += 64) {
+        const float m = ld_coh(p + (int64_t)s2 * (D + 2)), l = ld_coh(p + (int64_t)s2 * (D + 2) + 1);
+        const float mn = fmaxf(M, m);
+        if (mn != kNegInf) {
+          L = fmaf(L, exp2f_fast(M - mn), l * exp2f_fast(m - mn));
+          M = mn;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float Mo = __shfl_xor(M, o, 64), Lo = __shfl_xor(L, o, 64);
+        const float mn = fmaxf(M, Mo);
+        L = mn == kNegInf ? 0.f : fmaf(L, exp2f_fast(M - mn), Lo * exp2f_fast(Mo - mn));
+        M = mn;
+      }
+      if (lane == 0) s_lse[hh] = M + log2f_fast(L);
+    }
+    for (int i = tid; i < NB; i += kThreads) s_hist[i] = 0u;
+    __syncthreads();
+    float lse[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) lse[hh] = s_lse[hh];
+    float* pooled = f.pooled ? f.pooled + row * N + k0 : nullptr;
+    for (int i = tid; i < n; i += kThreads) {
+      float acc = 0.f;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) acc += exp2f_fast(sc[hh * sstride + i] - lse[hh]);
+      const uint32_t key = f32_order_key(acc);
+      keys[i] = key;   // head 0's score i was read by this thread only
+      if (pooled) pooled[i] = acc;
+      atomicAdd(&s_hist[key >> 21], 1u);
+    }
+    __syncthreads();
+    for (int i = tid; i < NB; i += kThreads) {
+      const uint32_t c = s_hist[i];
+      if (c) atomicAdd(&h0[i], c);
+    }
+  }
+  row_arrive(ctr);
+  if (ok) {
+    // split s merges heads s, s + S, ... of the group (a row may have fewer
+    // splits than heads)
+    float* scratch = reinterpret_cast<float*>(s_hist);
+    for (int hh = split; hh < G; hh += S) {
+      merge_splits<T, kThreads, 16, true>(a.part, S, (int64_t)b * a.Hq + g * G + hh, f.out, nullptr,
+                                          f.lse_out, scratch, scratch + kThreads, scratch + 2 * kThreads);
+      __syncthreads();   // the scratch is rewritten by the next head
+    }
+  }
+  ok = ok && row_wait(ctr, 2u * S, f.spin_limit, f.status, &s_ok);
+
+  // phase 3: digit 0's bin; the split's keys above it and its candidates
+  uint32_t b0 = 0, above0 = 0;
+  const int R = (n + kThreads - 1) / kThreads;   // consecutive keys per thread
+  const int i0 = tid * R;
+  if (ok) {
+    for (int i = tid; i < NB; i += kThreads) s_hist[i] = ld_coh(h0 + i);
+    __syncthreads();
+    b0 = find_bin256<NB>(s_hist, (uint32_t)f.k, sh, s_sel, above0);
+    for (int i = tid; i < NB; i += kThreads) s_hist[i] = 0u;
+    __syncthreads();
+    uint32_t cn = 0, hi = 0;
+    for (int q = 0; q < R; ++q) {
+      const int i = i0 + q;
+      if (i < n) {
+        const uint32_t key = keys[i], d0 = key >> 21;
+        if (d0 == b0) {
+          atomicAdd(&s_hist[(key >> 10) & 2047u], 1u);
+          ++cn;
+        }
+        hi += d0 > b0 ? 1u : 0u;
+      }
+    }
+    uint32_t tot;
+    const uint32_t off = scan256((cn << 16) | hi, sh, tot);
+    uint32_t* cp = cand_row + k0 + (off >> 16);
+    for (int q = 0; q < R; ++q) {
+      const int i = i0 + q;
+      if (i < n && (keys[i] >> 21) == b0) st_coh(cp++, keys[i]);
+    }
+    if (tid == 0) {
+      st_coh(cnt_row + 2 * split, tot & 0xFFFFu);
+      st_coh(cnt_row + 2 * split + 1, tot >> 16);
+    }
+    __syncthreads();
+    for (int i = tid; i < NB; i += kThreads) {
+      const uint32_t c = s_hist[i];
+      if (c) atomicAdd(&h1[i], c);
+    }
+  }
+  row_arrive(ctr);
+  ok = ok && row_wait(ctr, 3u * S, f.spin_limit, f.status, &s_ok);
+
+  // phase 4: the threshold key T and the split's indices
+  if (ok) {
+    uint32_t need = (uint32_t)f.k - above0, above;
+    // the splits' counts (one split per thread; counts clamped to the split),
+    // loaded together with the row's digit-1 histogram
+    uint32_t nc = 0, ab = 0;
+    if (tid < S) {
+      const uint32_t len = (uint32_t)min(kps, N - tid * kps);
+      nc = min(ld_coh(cnt_row + 2 * tid + 1), len);
+      ab = tid < split ? min(ld_coh(cnt_row + 2 * tid), len) : 0u;
+    }
+    for (int i = tid; i < NB; i += kThreads) s_hist[i] = ld_coh(h1 + i);
+    __syncthreads();
+    const uint32_t b1 = find_bin256<NB>(s_hist, need, sh, s_sel, above);
+    need -= above;
+    const uint32_t p01 = (b0 << 11) | b1;
+    uint32_t ncand, above_before;
+    s_cpre[tid] = scan256(nc, sh, ncand);
+    scan256(ab, sh, above_before);
+    for (int i = tid; i < 1024; i += kThreads) s_hist[i] = 0u;
+    __syncthreads();
+    for (uint32_t c = tid; c < ncand; c += kThreads) {
+      const uint32_t key = fused_cand(cand_row, s_cpre, S, kps, c);
+      if ((key >> 10) == p01) atomicAdd(&s_hist[key & 1023u], 1u);
+    }
+    __syncthreads();
+    const uint32_t b2 = find_bin256<1024>(s_hist, need, sh, s_sel, above);
+    need -= above;
+    const uint32_t Tk = (p01 << 10) | b2;   // the k-th largest key; `need` keys == Tk are taken
+    const uint32_t cend = s_cpre[split];
+    uint32_t gtc = 0, eqc = 0;
+    for (uint32_t c = tid; c < cend; c += kThreads) {
+      const uint32_t key = fused_cand(cand_row, s_cpre, S, kps, c);
+      gtc += key > Tk ? 1u : 0u;
+      eqc += key == Tk ? 1u : 0u;
+    }
+    uint32_t gt_before, eq_before;
+    scan256(gtc, sh, gt_before);
+    scan256(eqc, sh, eq_before);
+    gt_before += above_before;
+    uint32_t gt = 0, eq = 0;
+    for (int q = 0; q < R; ++q) {
+      const int i = i0 + q;
+      if (i < n) {
+        gt += keys[i] > Tk ? 1u : 0u;
+        eq += keys[i] == Tk ? 1u : 0u;
+      }
+    }
+    uint32_t tot;
+    const uint32_t ex = scan256((gt << 16) | eq, sh, tot);
+    uint32_t g2 = gt_before + (ex >> 16), e2 = eq_before + (ex & 0xFFFFu);
+    int32_t* out = f.idx + row * f.k;
+    const uint32_t kk = (uint32_t)f.k;
+    for (int q = 0; q < R; ++q) {
+      const int i = i0 + q;
+      if (i < n) {
+        const uint32_t key = keys[i];
+        if (key > Tk) {
+          const uint32_t pos = g2 + min(e2, need);
+          if (pos < kk) out[pos] = k0 + i;
+          ++g2;
+        } else if (key == Tk) {
+          if (e2 < need && g2 + e2 < kk) out[g2 + e2] = k0 + i;
+          ++e2;
+        }
+      }
+    }
+  }
+
+  // leave: the row's last workgroup clears its counters for the next call
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t t = __hip_atomic_fetch_add(ctr + 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t + 1 == (uint32_t)S) {
+      st_coh(ctr, 0u);
+      st_coh(ctr + 32, 0u);
+    }
+  }
+}
+
 // 16-bit caches run the head-slot kernel, fp32 caches the plain one (which
 // has no paged variant: the host rejects paged fp32).
 template <typename T, int G, bool GATHER, bool SPILL, bool PAGED = false>
@@ -880,6 +1220,63 @@ hipError_t launch_splitk_g(const DecodeArgs& a, bool gather, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+template <int G, bool HALF>
+hipError_t fused_launch_gh(const FusedDecodeArgs& f, hipStream_t s) {
+  const size_t lds = anchor_fused_dyn_lds(G, f.d.keys_per_split);
+  hipLaunchKernelGGL((k_anchor_fused<G, HALF>), dim3(f.d.n_splits, f.d.Hkv, f.d.B), dim3(kThreads), lds, s, f);
+  return hipGetLastError();
+}
+
+template <bool HALF>
+hipError_t fused_launch_h(const FusedDecodeArgs& f, hipStream_t s) {
+  switch (f.d.Hq / f.d.Hkv) {
+    case 1: return fused_launch_gh<1, HALF>(f, s);
+    case 2: return fused_launch_gh<2, HALF>(f, s);
+    case 4: return fused_launch_gh<4, HALF>(f, s);
+    case 8: return fused_launch_gh<8, HALF>(f, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int G, bool HALF>
+hipError_t fused_attrs_gh(int kps, int* blocks, size_t* static_lds) {
+  const void* k = reinterpret_cast<const void*>(&k_anchor_fused<G, HALF>);
+  hipFuncAttributes fa;
+  hipError_t e = hipFuncGetAttributes(&fa, k);
+  if (e != hipSuccess) return e;
+  *static_lds = fa.sharedSizeBytes;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k, kThreads, anchor_fused_dyn_lds(G, kps));
+}
+
+template <bool HALF>
+hipError_t fused_attrs_h(int G, int kps, int* blocks, size_t* static_lds) {
+  switch (G) {
+    case 1: return fused_attrs_gh<1, HALF>(kps, blocks, static_lds);
+    case 2: return fused_attrs_gh<2, HALF>(kps, blocks, static_lds);
+    case 4: return fused_attrs_gh<4, HALF>(kps, blocks, static_lds);
+    case 8: return fused_attrs_gh<8, HALF>(kps, blocks, static_lds);
+  }
+  return hipErrorInvalidValue;
+}
+
+// The fused kernel's dynamic LDS may grow to the spill cap or to what its
+// static LDS leaves of the CU's 160 KiB, whichever is smaller.
+template <int G, bool HALF>
+hipError_t fused_set_lds_gh() {
+  const void* k = reinterpret_cast<const void*>(&k_anchor_fused<G, HALF>);
+  hipFuncAttributes fa;
+  hipError_t e = hipFuncGetAttributes(&fa, k);
+  if (e != hipSuccess) return e;
+  const size_t room = fa.sharedSizeBytes < kLdsPerCu ? kLdsPerCu - fa.sharedSizeBytes : 0;
+  return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)(room < kSpillMaxLdsOne ? room : kSpillMaxLdsOne));
+}
+template <int G>
+hipError_t fused_set_lds_g() {
+  hipError_t e = fused_set_lds_gh<G, false>();
+  return e != hipSuccess ? e : fused_set_lds_gh<G, true>();
+}
+
 }  // namespace
 
 size_t spill_lds_bytes(int G, int keys_per_split) {
@@ -898,7 +1295,29 @@ hipError_t decode_set_max_lds() {
   if ((e = spill_set_lds_g<1>()) != hipSuccess) return e;
   if ((e = spill_set_lds_g<2>()) != hipSuccess) return e;
   if ((e = spill_set_lds_g<4>()) != hipSuccess) return e;
-  return spill_set_lds_g<8>();
+  if ((e = spill_set_lds_g<8>()) != hipSuccess) return e;
+  if ((e = fused_set_lds_g<1>()) != hipSuccess) return e;
+  if ((e = fused_set_lds_g<2>()) != hipSuccess) return e;
+  if ((e = fused_set_lds_g<4>()) != hipSuccess) return e;
+  return fused_set_lds_g<8>();
+}
+
+// Dynamic LDS of the fused anchor decode: the split's scores, with the same
+// one-workgroup-per-CU floor as the spilling pass.
+size_t anchor_fused_dyn_lds(int G, int kps) {
+  const size_t b = spill_lds_bytes(G, kps);
+  return b < kSpillMinLds ? kSpillMinLds : b;
+}
+
+hipError_t anchor_fused_attrs(int dtype, int G, int kps, int* blocks, size_t* static_lds) {
+  return dtype == 2 ? fused_attrs_h<true>(G, kps, blocks, static_lds)
+                    : fused_attrs_h<false>(G, kps, blocks, static_lds);
+}
+
+hipError_t launch_anchor_fused(const FusedDecodeArgs& f, int dtype, hipStream_t s) {
+  if (f.d.n_splits < 1 || f.d.n_splits > kThreads || f.d.keys_per_split > kSpillMaxKeysOne)
+    return hipErrorInvalidValue;
+  return dtype == 2 ? fused_launch_h<true>(f, s) : fused_launch_h<false>(f, s);
 }
 
 hipError_t decode_splitk_attrs(int dtype, int G, bool gather, bool spill, bool paged, int* blocks,

@@ -170,6 +170,33 @@ struct WideSelectArgs {
   uint32_t* chunk_cnt;           // [rows][chunks][2] (keys above the digit-0 bin, candidates)
 };
 hipError_t launch_topk_select_wide(const WideSelectArgs& a, hipStream_t s);
+
+// Fused anchor decode: one launch of co-resident workgroups (one per split
+// of each (batch, KV head) row) runs the split-K pass with the scores kept
+// in LDS, then, separated by three row-wide barriers, the lse and pooling,
+// the digit-0 candidates and the exact threshold and index write.  Words the
+// row's workgroups exchange are written and read with device-coherent
+// accesses.
+constexpr size_t kLdsPerCu = 160 * 1024;   // gfx950
+constexpr int kFusedSyncWords = 64;    // per row: barrier count (word 0), departures (word 32)
+struct FusedDecodeArgs {
+  DecodeArgs d;                  // the anchor pass; d.part receives the splits' partials
+  void* out;                     // [B,Hq,D] input dtype
+  float* lse_out;                // [B,Hq] natural-log lse, or null
+  int32_t* idx;                  // [B,Hkv,k] ascending
+  float* pooled;                 // [B,Hkv,N] pooled probabilities, or null
+  int32_t k;
+  uint32_t* sync;                // [rows][kFusedSyncWords]: zero on entry, left zero
+  uint32_t* status;              // bit 0 set when a row barrier gave up waiting
+  uint32_t spin_limit;           // polls of a barrier before giving up
+  uint32_t* hist0;               // [rows][2048]
+  uint32_t* hist1;               // [rows][2048]
+  uint32_t* cand;                // [rows][N] digit-0 candidates, split s's at offset s*kps
+  uint32_t* cnt;                 // [rows][splits][2] (keys above the digit-0 bin, candidates)
+};
+hipError_t launch_anchor_fused(const FusedDecodeArgs& a, int dtype, hipStream_t s);
+hipError_t anchor_fused_attrs(int dtype, int G, int kps, int* blocks, size_t* static_lds);
+size_t anchor_fused_dyn_lds(int G, int kps);
 size_t topk_select_lds_bytes(int cache_cap);
 hipError_t topk_select_set_max_lds(size_t bytes);
 hipError_t launch_prefill_flash(const PrefillArgs& a, hipStream_t s);

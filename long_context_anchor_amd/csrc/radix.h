@@ -1,0 +1,76 @@
+// Block-wide radix helpers of the exact Top-k selection (256-thread
+// workgroups): an exclusive prefix sum and the histogram bin that holds the
+// need-th largest key, scanning from the top bin down.
+#pragma once
+#include "common.h"
+
+namespace kc {
+
+constexpr int kWideThreads = 256;
+constexpr int kWideWaves = kWideThreads / 64;
+
+// Exclusive prefix sum over the 256-thread block; `sh` holds >= 5 words.
+KC_INLINE uint32_t scan256(uint32_t x, uint32_t* sh, uint32_t& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kWideWaves; ++w) {
+    const uint32_t v = sh[w];
+    before += w < wave ? v : 0u;
+    tot += v;
+  }
+  __syncthreads();
+  total = tot;
+  return before + incl - x;
+}
+
+// Bin of a histogram (nb = 2048 or 1024 bins, global or LDS) holding the
+// need-th largest key, scanning from the top bin down; `above` receives the
+// count of keys in higher bins.  Thread t owns nb/256 consecutive bins
+// counted from the top.
+template <int NB>
+KC_INLINE uint32_t find_bin256(const uint32_t* hist, uint32_t need, uint32_t* sh, uint32_t* s_sel,
+                               uint32_t& above) {
+  constexpr int W = NB / kWideThreads;
+  const int tid = threadIdx.x;
+  const int hi = NB - W * tid;   // bins [hi - W, hi)
+  uint32_t h[W], tot = 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    h[i] = hist[hi - 1 - i];
+    tot += h[i];
+  }
+  if (tid == 0) {   // a histogram holding fewer than `need` keys selects bin 0
+    s_sel[0] = 0u;
+    s_sel[1] = 0u;
+  }
+  uint32_t all;
+  const uint32_t before = scan256(tot, sh, all);
+  if (before < need && before + tot >= need) {
+    uint32_t cum = before;
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      if (cum + h[i] >= need) {
+        s_sel[0] = (uint32_t)(hi - 1 - i);
+        s_sel[1] = cum;
+        break;
+      }
+      cum += h[i];
+    }
+  }
+  __syncthreads();
+  const uint32_t bin = s_sel[0];
+  above = s_sel[1];
+  __syncthreads();
+  return bin;
+}
+
+}  // namespace kc

@@ -24,9 +24,10 @@ KASCADE_OK, KASCADE_ERR_NULL, KASCADE_ERR_SHAPE, KASCADE_ERR_DTYPE = 0, -1, -2, 
 KASCADE_ERR_TOPK, KASCADE_ERR_HEADMAP, KASCADE_ERR_WORKSPACE, KASCADE_ERR_HIP = -4, -5, -6, -7
 KASCADE_ERR_ARG = -8
 OP_ANCHOR_DECODE, OP_REUSE_DECODE, OP_ANCHOR_PREFILL, OP_REUSE_PREFILL = 0, 1, 2, 3
-OP_DENSE_DECODE, OP_DENSE_PREFILL = 4, 5
+OP_DENSE_DECODE, OP_DENSE_PREFILL, OP_ANCHOR_DECODE_FUSED = 4, 5, 6
 K_DECODE_SPLITK, K_DECODE_COMBINE, K_DECODE_POOL, K_TOPK_SELECT = 0, 1, 2, 3
 K_REUSE_DECODE, K_PREFILL_FLASH, K_PREFILL_POOL, K_PREFILL_SPARSE = 4, 5, 6, 7
+K_ANCHOR_FUSED = 8
 
 EXPORTS = [
     "kascade_anchor_decode", "kascade_reuse_decode", "kascade_anchor_prefill",
@@ -37,7 +38,7 @@ EXPORTS = [
     "kascade_anchor_decode_paged", "kascade_reuse_decode_paged", "kascade_reuse_prefill_paged",
     "kascade_calib_head_similarity", "kascade_layer_weight", "kascade_layer_weight_workspace_bytes",
     "kascade_weighted_similarity", "kascade_select_anchors", "kascade_head_maps",
-    "kascade_reuse_decode_noalloc", "kascade_stream_read",
+    "kascade_reuse_decode_noalloc", "kascade_stream_read", "kascade_anchor_decode_fused",
 ]
 
 
@@ -80,6 +81,8 @@ _LIB: Optional[ctypes.CDLL] = None
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _SIGS = {
     "kascade_anchor_decode": (_i32, [ctypes.POINTER(Shape), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kascade_anchor_decode_fused": (_i32, [ctypes.POINTER(Shape), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
+                                             ctypes.c_uint32, _vp, _sz, _vp]),
     "kascade_reuse_decode": (_i32, [ctypes.POINTER(Shape), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kascade_reuse_decode_noalloc": (_i32, [ctypes.POINTER(Shape), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp]),
     "kascade_anchor_prefill": (_i32, [ctypes.POINTER(Shape), _vp, _vp, _vp, ctypes.POINTER(TopkRule), _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -146,6 +149,13 @@ def kascade_anchor_decode(shape, q, k, v, topk, out, lse_out, topk_idx, pooled_o
     return lib().kascade_anchor_decode(ctypes.byref(shape), _p(q), _p(k), _p(v), topk, _p(out),
                                        _p(lse_out), _p(topk_idx), _p(pooled_out), _p(workspace),
                                        workspace_bytes, _stream(stream))
+
+
+def kascade_anchor_decode_fused(shape, q, k, v, topk, out, lse_out, topk_idx, pooled_out, max_polls,
+                                workspace, workspace_bytes, stream=None) -> int:
+    return lib().kascade_anchor_decode_fused(ctypes.byref(shape), _p(q), _p(k), _p(v), topk, _p(out),
+                                             _p(lse_out), _p(topk_idx), _p(pooled_out), max_polls,
+                                             _p(workspace), workspace_bytes, _stream(stream))
 
 
 def kascade_reuse_decode(shape, q, k, v, topk, anchor_topk_idx, head_map, out, workspace,
@@ -364,6 +374,30 @@ def anchor_decode(q, k, v, topk: int, ctx_len: Optional[int] = None, want_pooled
     check(kascade_anchor_decode(sh, q, k, v, topk, out, lse, idx, pooled, ws, ws.numel()),
           "kascade_anchor_decode")
     return out, lse, idx, pooled
+
+
+def anchor_decode_fused(q, k, v, topk: int, ctx_len: Optional[int] = None, want_pooled=False, ws=None,
+                        max_polls: int = 0):
+    """anchor_decode in one launch.  `ws` must come from workspace(OP_ANCHOR_DECODE_FUSED, ...)
+    (allocated zeroed: its status word and barrier counters start at zero and
+    every call leaves the counters zero); ws[0:4] holds the status word."""
+    N = ctx_len or k.shape[2]
+    sh = make_shape(q, k, N)
+    B, Hq, d = q.shape
+    Hkv = k.shape[1]
+    out = torch.empty((B, Hq, d), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    idx = torch.empty((B, Hkv, topk), dtype=torch.int32, device=q.device)
+    pooled = torch.empty((B, Hkv, N), dtype=torch.float32, device=q.device) if want_pooled else None
+    ws = ws if ws is not None else workspace(OP_ANCHOR_DECODE_FUSED, sh, topk)
+    check(kascade_anchor_decode_fused(sh, q, k, v, topk, out, lse, idx, pooled, max_polls, ws, ws.numel()),
+          "kascade_anchor_decode_fused")
+    return out, lse, idx, pooled
+
+
+def fused_status(ws) -> int:
+    """The status word of a fused anchor-decode workspace (waits for the stream)."""
+    return int(ws[0:4].view(torch.int32).item())
 
 
 def reuse_decode(q, k, v, anchor_idx, head_map: Sequence[int], ctx_len: Optional[int] = None, ws=None):

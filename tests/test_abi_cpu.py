@@ -86,6 +86,25 @@ def test_anchor_decode_validation():
     assert call(shape=bad) == -2
 
 
+def test_anchor_decode_fused_validation():
+    """The one-launch anchor decode rejects bad arguments before any device call."""
+    sh = _shape(N=4096, d=128, Hq=8, Hkv=2, dtype=K.KASCADE_BF16)
+    ws_n = K.kascade_workspace_bytes(K.OP_ANCHOR_DECODE_FUSED, sh, 128)
+    # status word, counters, partials for 256 splits, two histograms, candidates, counts
+    assert ws_n >= 256 + 256 * 64 * 4 + 8 * 256 * 130 * 4 + 2 * 2 * 2048 * 4 + 2 * 4096 * 4
+    call = lambda **kw: K.kascade_anchor_decode_fused(
+        kw.get("shape", sh), kw.get("q", FAKE), FAKE, FAKE, kw.get("topk", 128), FAKE, None,
+        kw.get("idx", FAKE), None, 0, FAKE, kw.get("ws", ws_n), 0)
+    assert call(q=None) == -1
+    assert call(idx=None) == -1
+    assert call(topk=0) == -4
+    assert call(topk=4097) == -4
+    assert call(ws=ws_n - 1) == -6
+    assert call(shape=_shape(N=4096, d=64, Hq=8, Hkv=2)) == -3      # fp32 caches: not fused
+    assert call(shape=_shape(N=4096, d=128, Hq=12, Hkv=4, dtype=K.KASCADE_BF16)) == -2
+    assert call(q=FAKE + 8) == -8
+
+
 def test_reuse_decode_validation():
     sh = _shape()
     ws_n = K.kascade_workspace_bytes(K.OP_REUSE_DECODE, sh, 128)
