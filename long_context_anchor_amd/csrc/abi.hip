@@ -783,6 +783,7 @@ int kascade_anchor_decode_fused(const kascade_shape* s, const void* q, const voi
   f.hist1 = reinterpret_cast<uint32_t*>(w + fp.off_hist1);
   f.cand = reinterpret_cast<uint32_t*>(w + fp.off_cand);
   f.cnt = reinterpret_cast<uint32_t*>(w + fp.off_cnt);
+  f.cand_cap = (uint32_t)(anchor_fused_dyn_lds(G, p.kps) / sizeof(uint32_t)) - (uint32_t)p.kps;
   e = timed(KASCADE_K_ANCHOR_FUSED, stream, [&] { return launch_anchor_fused(f, s->dtype, stream); });
   return hip_status(e);
 }

@@ -1064,9 +1064,49 @@ __global__ __launch_bounds__(kThreads) void k_anchor_fused(const FusedDecodeArgs
     s_cpre[tid] = scan256(nc, sh, ncand);
     scan256(ab, sh, above_before);
     for (int i = tid; i < 1024; i += kThreads) s_hist[i] = 0u;
+    // The row's candidates, copied into the free part of the LDS score buffer
+    // when they fit (the two passes below then read LDS): thread t copies the
+    // flat range [t*RC, t*RC + RC), eight coherent loads in flight at a time.
+    uint32_t* s_cand = keys + kps;
+    const bool staged = ncand <= f.cand_cap;
+    if (staged) {
+      const uint32_t RC = (ncand + kThreads - 1) / kThreads;
+      const uint32_t c0 = tid * RC, c1 = min(ncand, c0 + RC);
+      if (c0 < c1) {
+        int sp = 0, hi = S - 1;   // last split whose prefix is <= c0
+        while (sp < hi) {
+          const int mid = (sp + hi + 1) >> 1;
+          if (s_cpre[mid] <= c0) sp = mid;
+          else hi = mid - 1;
+        }
+        uint32_t off = c0 - s_cpre[sp];
+        for (uint32_t c = c0; c < c1; c += 8) {
+          uint32_t v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            v[u] = 0u;
+            if (c + u < c1) {
+              // skip splits whose candidates are used up (or that have none)
+              while (sp + 1 < S && s_cpre[sp] + off >= s_cpre[sp + 1]) {
+                ++sp;
+                off = 0;
+              }
+              v[u] = ld_coh(cand_row + (int64_t)sp * kps + off);
+              ++off;
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (c + u < c1) s_cand[c + u] = v[u];
+        }
+      }
+    }
     __syncthreads();
+    auto cand_at = [&](uint32_t c) {
+      return staged ? s_cand[c] : fused_cand(cand_row, s_cpre, S, kps, c);
+    };
     for (uint32_t c = tid; c < ncand; c += kThreads) {
-      const uint32_t key = fused_cand(cand_row, s_cpre, S, kps, c);
+      const uint32_t key = cand_at(c);
       if ((key >> 10) == p01) atomicAdd(&s_hist[key & 1023u], 1u);
     }
     __syncthreads();
@@ -1076,7 +1116,7 @@ __global__ __launch_bounds__(kThreads) void k_anchor_fused(const FusedDecodeArgs
     const uint32_t cend = s_cpre[split];
     uint32_t gtc = 0, eqc = 0;
     for (uint32_t c = tid; c < cend; c += kThreads) {
-      const uint32_t key = fused_cand(cand_row, s_cpre, S, kps, c);
+      const uint32_t key = cand_at(c);
       gtc += key > Tk ? 1u : 0u;
       eqc += key == Tk ? 1u : 0u;
     }

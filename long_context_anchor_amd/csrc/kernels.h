@@ -193,6 +193,7 @@ struct FusedDecodeArgs {
   uint32_t* hist1;               // [rows][2048]
   uint32_t* cand;                // [rows][N] digit-0 candidates, split s's at offset s*kps
   uint32_t* cnt;                 // [rows][splits][2] (keys above the digit-0 bin, candidates)
+  uint32_t cand_cap;             // candidates the LDS score buffer holds after the split's keys
 };
 hipError_t launch_anchor_fused(const FusedDecodeArgs& a, int dtype, hipStream_t s);
 hipError_t anchor_fused_attrs(int dtype, int G, int kps, int* blocks, size_t* static_lds);
