@@ -139,9 +139,14 @@ int kascade_anchor_decode(const kascade_shape* shape, const void* q, const void*
  * batch * n_kv_heads * splits <= CUs (one workgroup per CU; splits as in
  * kascade_anchor_decode, at most 256) and the split's scores must fit in LDS,
  * else KASCADE_ERR_SHAPE (the 32K and 64K single-sequence decodes of the
- * benchmark qualify, 128K x 4 does not).  Other work running on the GPU at
- * the same time delays the launch's workgroups; that is safe (the barriers
- * wait up to max_polls). */
+ * benchmark qualify, 128K x 4 does not).  Work running on the GPU at the
+ * same time (other streams) delays the launch's workgroups, which is safe
+ * while it ends within the barriers' wait (max_polls polls, about a second
+ * by default).  Two fused calls must not run at the same time on one GPU
+ * (calls on one stream are ordered and fine): each launch's resident
+ * workgroups can hold the CUs the other's are waiting for, so both wait out
+ * max_polls and report status bit 0 (nothing hangs, the outputs are
+ * undefined). */
 int kascade_anchor_decode_fused(const kascade_shape* shape, const void* q, const void* k,
                                 const void* v, int32_t topk, void* out, float* lse_out,
                                 int32_t* topk_idx, float* pooled_out, uint32_t max_polls,
