@@ -5,8 +5,9 @@ size, context or prompt length (log-uniform or uniform over a range,
 ragged), Top-k (decode), dtype (fp32 with d 64, bf16 or fp16 with d 128)
 and a random many-to-one head map.
 Anchor layers are checked in full (outputs, lse, pooled values, index
-lists); reuse layers run on the ORACLE's index lists, so both sides consume
-the same lists.  16-bit cases also run over paged caches (random block size,
+lists; 16-bit cases also through the one-launch anchor decode, bit for bit
+against the four-launch call); reuse layers run on the ORACLE's index lists,
+so both sides consume the same lists.  16-bit cases also run over paged caches (random block size,
 blocks scattered): paged decode against the oracle, paged reuse prefill bit
 for bit against the contiguous call.  Tolerances as in the other GPU tests: outputs 1e-4 (fp32) /
 2e-2 (16-bit) max-abs, decode lse 1e-4, prefill lse 1e-3, pooled 1e-4
@@ -93,6 +94,12 @@ def test_random_decode(seed):
             assert np.array_equal(gi[b, g], oracle.topk_full_sort(gp[b, g], topk))
             ok, nd = oracle.index_sets_agree(gi[b, g], ridx[b, g], rpool[b, g])
             assert ok, (b, g, nd)
+    if dtype != "f32":
+        # the one-launch anchor decode: bit for bit the four-launch outputs
+        fo, fl, fi, fpool = K.anchor_decode_fused(q, k, v, topk, want_pooled=True)
+        torch.cuda.synchronize()
+        assert torch.equal(fo.view(torch.int16), out.view(torch.int16))
+        assert torch.equal(fl, lse) and torch.equal(fi, idx) and torch.equal(fpool, pooled)
     # reuse layer on the oracle's lists through a random head map
     q2 = _randn((B, Hq, d), 7 * seed + 1, dtype)
     k2 = _randn((B, Hkv, N, d), 7 * seed + 2, dtype)
