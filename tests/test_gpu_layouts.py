@@ -52,6 +52,11 @@ def test_decode_interleaved_heads_and_padded_rows(B, Hq, Hkv, N, topk):
             assert np.array_equal(gi[b, gg], oracle.topk_full_sort(gp[b, gg], topk))
             ok, nd = oracle.index_sets_agree(gi[b, gg], ridx[b, gg], rpool[b, gg])
             assert ok, (b, gg, nd)
+    # the one-launch anchor decode over the same strided caches: bit for bit
+    fo, fl, fi, fp = K.anchor_decode_fused(q, k, v, topk, want_pooled=True)
+    torch.cuda.synchronize()
+    assert torch.equal(fo.view(torch.int16), out.view(torch.int16))
+    assert torch.equal(fl, lse) and torch.equal(fi, idx) and torch.equal(fp, pooled)
     hm = list(reversed(range(Hkv)))
     out2 = K.reuse_decode(q, k, v, torch.as_tensor(ridx.astype(np.int32), device=DEV), hm)
     torch.cuda.synchronize()
