@@ -632,9 +632,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_splitk_slots(const DecodeAr
 // each column meet once in LDS (sm, sl, so hold NT floats each) and threads
 // < D write the normalised column; thread 0 writes the lse.
 // Words exchanged between the workgroups of one launch (the fused anchor
-// decode): relaxed atomics at agent scope, which gfx950 issues as stores
-// written through to the device's coherence point and loads that read it, so
-// a reader needs no cache invalidate and a writer no cache writeback.
+// decode): relaxed atomics at agent scope, which the compiler issues for
+// gfx950 as global stores and loads with the sc1 (device scope) bit and no
+// cache writeback or invalidate instructions; the hardware keeps such
+// accesses coherent across the device.
 KC_INLINE void st_coh(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 KC_INLINE void st_coh(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
