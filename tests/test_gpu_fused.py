@@ -217,3 +217,31 @@ def test_fused_rejects_launches_that_cannot_be_resident():
     assert st == K.KASCADE_ERR_SHAPE
     torch.cuda.synchronize()
     assert int((idx != -3).sum().item()) == 0
+
+
+def test_fused_many_calls_stay_bitwise_equal():
+    """200 calls on one workspace, alternating two 32K anchor layers, each
+    output compared bit for bit with the four-launch reference: the
+    exchanged words (partials, histograms, candidates, counters) are seen
+    complete in every call, and every call leaves the counters zero."""
+    cfg = configs.LLAMA_DECODE_32K
+    lays = [_layer(cfg, 0), _layer(cfg, 2)]
+    refs = [K.anchor_decode(*x, cfg.topk) for x in lays]
+    sh = K.make_shape(lays[0][0], lays[0][1], cfg.ctx_len)
+    ws = K.workspace(K.OP_ANCHOR_DECODE_FUSED, sh, cfg.topk)
+    out = torch.empty_like(refs[0][0])
+    lse = torch.empty_like(refs[0][1])
+    idx = torch.empty_like(refs[0][2])
+    bad = 0
+    for i in range(200):
+        q, k, v = lays[i % 2]
+        K.check(K.kascade_anchor_decode_fused(sh, q, k, v, cfg.topk, out, lse, idx, None, 0, ws, ws.numel()),
+                "fused")
+        ro, rl, ri, _ = refs[i % 2]
+        ok = torch.equal(_bits(out), _bits(ro)) and torch.equal(lse, rl) and torch.equal(idx, ri)
+        bad += 0 if ok else 1
+    torch.cuda.synchronize()
+    say("mismatching calls", bad, "of 200")
+    assert bad == 0
+    assert K.fused_status(ws) == 0
+    assert int(_sync_words(ws, sh).abs().sum().item()) == 0
