@@ -35,19 +35,25 @@ KC_INLINE uint32_t scan256(uint32_t x, uint32_t* sh, uint32_t& total) {
 // Bin of a histogram (nb = 2048 or 1024 bins, global or LDS) holding the
 // need-th largest key, scanning from the top bin down; `above` receives the
 // count of keys in higher bins.  Thread t owns nb/256 consecutive bins
-// counted from the top.
+// counted from the top: load_bins reads them (so a caller can issue the
+// loads early, beside other independent ones), find_bin256_regs searches.
 template <int NB>
-KC_INLINE uint32_t find_bin256(const uint32_t* hist, uint32_t need, uint32_t* sh, uint32_t* s_sel,
-                               uint32_t& above) {
+KC_INLINE void load_bins(const uint32_t* hist, uint32_t (&h)[NB / kWideThreads]) {
+  constexpr int W = NB / kWideThreads;
+  const int hi = NB - W * (int)threadIdx.x;   // bins [hi - W, hi)
+#pragma unroll
+  for (int i = 0; i < W; ++i) h[i] = hist[hi - 1 - i];
+}
+
+template <int NB>
+KC_INLINE uint32_t find_bin256_regs(const uint32_t (&h)[NB / kWideThreads], uint32_t need, uint32_t* sh,
+                                    uint32_t* s_sel, uint32_t& above) {
   constexpr int W = NB / kWideThreads;
   const int tid = threadIdx.x;
-  const int hi = NB - W * tid;   // bins [hi - W, hi)
-  uint32_t h[W], tot = 0;
+  const int hi = NB - W * tid;
+  uint32_t tot = 0;
 #pragma unroll
-  for (int i = 0; i < W; ++i) {
-    h[i] = hist[hi - 1 - i];
-    tot += h[i];
-  }
+  for (int i = 0; i < W; ++i) tot += h[i];
   if (tid == 0) {   // a histogram holding fewer than `need` keys selects bin 0
     s_sel[0] = 0u;
     s_sel[1] = 0u;
@@ -71,6 +77,14 @@ KC_INLINE uint32_t find_bin256(const uint32_t* hist, uint32_t need, uint32_t* sh
   above = s_sel[1];
   __syncthreads();
   return bin;
+}
+
+template <int NB>
+KC_INLINE uint32_t find_bin256(const uint32_t* hist, uint32_t need, uint32_t* sh, uint32_t* s_sel,
+                               uint32_t& above) {
+  uint32_t h[NB / kWideThreads];
+  load_bins<NB>(hist, h);
+  return find_bin256_regs<NB>(h, need, sh, s_sel, above);
 }
 
 }  // namespace kc

@@ -378,13 +378,16 @@ __global__ __launch_bounds__(kWideThreads) void k_select_wide_a(const WideSelect
   __shared__ uint32_t sh[8], s_sel[2];
   const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
   const float* src = a.src + (int64_t)row * a.row_stride;
-  uint32_t above;
-  const uint32_t b0 = find_bin256<kHistBins>(a.hist0 + (int64_t)row * kHistBins, (uint32_t)a.k, sh,
-                                             s_sel, above);
-  for (int i = tid; i < kHistBins; i += kWideThreads) hist[i] = 0u;
+  // the histogram's bins and the chunk's keys are independent: both loads go
+  // out before either is used
+  uint32_t h0[kHistBins / kWideThreads];
+  load_bins<kHistBins>(a.hist0 + (int64_t)row * kHistBins, h0);
   uint32_t key[kPerThread];
   int j0;
   chunk_keys<CH>(a, src, c, key, j0);
+  uint32_t above;
+  const uint32_t b0 = find_bin256_regs<kHistBins>(h0, (uint32_t)a.k, sh, s_sel, above);
+  for (int i = tid; i < kHistBins; i += kWideThreads) hist[i] = 0u;
   __syncthreads();
   uint32_t cnt = 0, hi = 0;
 #pragma unroll
@@ -444,14 +447,12 @@ __global__ __launch_bounds__(kWideThreads) void k_select_wide_b(const WideSelect
   const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
   const int chunks = a.chunks;
   const float* src = a.src + (int64_t)row * a.row_stride;
-  uint32_t need = (uint32_t)a.k, above;
-  const uint32_t b0 = find_bin256<kHistBins>(a.hist0 + (int64_t)row * kHistBins, need, sh, s_sel, above);
-  need -= above;
-  const uint32_t b1 = find_bin256<kHistBins>(a.hist1 + (int64_t)row * kHistBins, need, sh, s_sel, above);
-  need -= above;
-  const uint32_t p01 = (b0 << 11) | b1;
-  // the chunks' counts: keys above b0 of the chunks before this one, and the
-  // exclusive prefix of the candidate counts (flattened candidate index)
+  // independent loads first, all in flight together: both histograms' bins,
+  // the chunks' counts (keys above b0 of the chunks before this one, and the
+  // candidate counts for the flattened candidate index) and the chunk's keys
+  uint32_t h0[kHistBins / kWideThreads], h1[kHistBins / kWideThreads];
+  load_bins<kHistBins>(a.hist0 + (int64_t)row * kHistBins, h0);
+  load_bins<kHistBins>(a.hist1 + (int64_t)row * kHistBins, h1);
   const uint32_t* ccnt = a.chunk_cnt + (int64_t)row * chunks * 2;
   uint32_t nc[kMaxCh / kWideThreads], abv = 0, csum = 0;
 #pragma unroll
@@ -461,6 +462,15 @@ __global__ __launch_bounds__(kWideThreads) void k_select_wide_b(const WideSelect
     abv += (i < chunks && i < c) ? ccnt[2 * i] : 0u;
     csum += nc[u];
   }
+  uint32_t key[kPerThread];
+  int j0;
+  chunk_keys<CH>(a, src, c, key, j0);
+  uint32_t need = (uint32_t)a.k, above;
+  const uint32_t b0 = find_bin256_regs<kHistBins>(h0, need, sh, s_sel, above);
+  need -= above;
+  const uint32_t b1 = find_bin256_regs<kHistBins>(h1, need, sh, s_sel, above);
+  need -= above;
+  const uint32_t p01 = (b0 << 11) | b1;
   uint32_t ncand;
   uint32_t run = scan256(csum, sh, ncand);
 #pragma unroll
@@ -495,9 +505,6 @@ __global__ __launch_bounds__(kWideThreads) void k_select_wide_b(const WideSelect
   scan256(gtc, sh, gt_before);
   scan256(eqc, sh, eq_before);
   gt_before += above_before;
-  uint32_t key[kPerThread];
-  int j0;
-  chunk_keys<CH>(a, src, c, key, j0);
   uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
