@@ -9,15 +9,24 @@ namespace kc {
 constexpr int kWideThreads = 256;
 constexpr int kWideWaves = kWideThreads / 64;
 
+// Inclusive prefix sum over the 64 lanes of a wave (every lane active) with
+// DPP moves instead of LDS shuffles: shifts by 1, 2, 4 and 8 lanes inside
+// each 16-lane row (a lane with no source adds nothing), then lane 15 of
+// rows 0 and 2 added to rows 1 and 3, then lane 31 added to rows 2 and 3.
+KC_INLINE uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // Exclusive prefix sum over the 256-thread block; `sh` holds >= 5 words.
 KC_INLINE uint32_t scan256(uint32_t x, uint32_t* sh, uint32_t& total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t incl = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
+  const uint32_t incl = wave_incl_scan(x);
   if (lane == 63) sh[wave] = incl;
   __syncthreads();
   uint32_t before = 0, tot = 0;

@@ -69,22 +69,12 @@ KC_INLINE RowGeom row_geom(const SelectArgs& a, int r) {
 // Exclusive prefix sum over the block (1024 threads).  `sh` holds >= 17 words.
 KC_INLINE uint32_t block_excl_scan(uint32_t x, uint32_t* sh, uint32_t& total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t incl = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
+  const uint32_t incl = wave_incl_scan(x);
   if (lane == 63) sh[wave] = incl;
   __syncthreads();
-  if (tid < 64) {
-    uint32_t w = tid < kSelWaves ? sh[tid] : 0u;
-    uint32_t wi = w;
-#pragma unroll
-    for (int o = 1; o < kSelWaves; o <<= 1) {
-      uint32_t y = __shfl_up(wi, o, 64);
-      if (lane >= o) wi += y;
-    }
+  if (tid < 64) {   // the whole first wave: its lanes past kSelWaves scan zeros
+    const uint32_t w = tid < kSelWaves ? sh[tid] : 0u;
+    const uint32_t wi = wave_incl_scan(w);
     if (tid < kSelWaves) sh[tid] = wi - w;          // exclusive wave offsets
     if (tid == kSelWaves - 1) sh[kSelWaves] = wi;   // block total
   }
