@@ -1061,10 +1061,11 @@ __global__ __launch_bounds__(kThreads) void k_anchor_fused(const FusedDecodeArgs
     const uint32_t b1 = find_bin256<NB>(s_hist, need, sh, s_sel, above);
     need -= above;
     const uint32_t p01 = (b0 << 11) | b1;
-    uint32_t ncand, above_before;
-    s_cpre[tid] = scan256(nc, sh, ncand);
-    scan256(ab, sh, above_before);
+    uint32_t ncand, above_before, nc_ex, ab_ex;
+    scan256x2(nc, ab, sh, nc_ex, ab_ex, ncand, above_before);
+    s_cpre[tid] = nc_ex;
     for (int i = tid; i < 1024; i += kThreads) s_hist[i] = 0u;
+    __syncthreads();   // s_cpre is read by every thread below
     // The row's candidates, copied into the free part of the LDS score buffer
     // when they fit (the two passes below then read LDS): thread t copies the
     // flat range [t*RC, t*RC + RC), eight coherent loads in flight at a time.
@@ -1121,9 +1122,8 @@ __global__ __launch_bounds__(kThreads) void k_anchor_fused(const FusedDecodeArgs
       gtc += key > Tk ? 1u : 0u;
       eqc += key == Tk ? 1u : 0u;
     }
-    uint32_t gt_before, eq_before;
-    scan256(gtc, sh, gt_before);
-    scan256(eqc, sh, eq_before);
+    uint32_t gtc_ex, eqc_ex, gt_before, eq_before;
+    scan256x2(gtc, eqc, sh, gtc_ex, eqc_ex, gt_before, eq_before);   // block totals
     gt_before += above_before;
     uint32_t gt = 0, eq = 0;
     for (int q = 0; q < R; ++q) {

@@ -24,6 +24,9 @@ KC_INLINE uint32_t wave_incl_scan(uint32_t x) {
 }
 
 // Exclusive prefix sum over the 256-thread block; `sh` holds >= 5 words.
+// TAIL = false leaves out the closing barrier: the caller then puts a block
+// barrier between this call and the next write of `sh`.
+template <bool TAIL = true>
 KC_INLINE uint32_t scan256(uint32_t x, uint32_t* sh, uint32_t& total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t incl = wave_incl_scan(x);
@@ -36,14 +39,43 @@ KC_INLINE uint32_t scan256(uint32_t x, uint32_t* sh, uint32_t& total) {
     before += w < wave ? v : 0u;
     tot += v;
   }
-  __syncthreads();
+  if (TAIL) __syncthreads();
   total = tot;
   return before + incl - x;
 }
 
+// Two independent exclusive prefix sums over the block behind one pair of
+// barriers; `sh` holds >= 8 words.
+KC_INLINE void scan256x2(uint32_t x, uint32_t y, uint32_t* sh, uint32_t& ex, uint32_t& ey,
+                         uint32_t& tx, uint32_t& ty) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t ix = wave_incl_scan(x), iy = wave_incl_scan(y);
+  if (lane == 63) {
+    sh[wave] = ix;
+    sh[kWideWaves + wave] = iy;
+  }
+  __syncthreads();
+  uint32_t bx = 0, by = 0, sx = 0, sy = 0;
+#pragma unroll
+  for (int w = 0; w < kWideWaves; ++w) {
+    const uint32_t vx = sh[w], vy = sh[kWideWaves + w];
+    bx += w < wave ? vx : 0u;
+    by += w < wave ? vy : 0u;
+    sx += vx;
+    sy += vy;
+  }
+  __syncthreads();
+  ex = bx + ix - x;
+  ey = by + iy - y;
+  tx = sx;
+  ty = sy;
+}
+
 // Bin of a histogram (nb = 2048 or 1024 bins, global or LDS) holding the
 // need-th largest key, scanning from the top bin down; `above` receives the
-// count of keys in higher bins.  Thread t owns nb/256 consecutive bins
+// count of keys in higher bins.  Two block barriers; the histogram (when in
+// LDS) and `sh` may be rewritten after the call, `s_sel` only behind a later
+// barrier.  Thread t owns nb/256 consecutive bins
 // counted from the top: load_bins reads them (so a caller can issue the
 // loads early, beside other independent ones), find_bin256_regs searches.
 template <int NB>
@@ -63,13 +95,13 @@ KC_INLINE uint32_t find_bin256_regs(const uint32_t (&h)[NB / kWideThreads], uint
   uint32_t tot = 0;
 #pragma unroll
   for (int i = 0; i < W; ++i) tot += h[i];
-  if (tid == 0) {   // a histogram holding fewer than `need` keys selects bin 0
-    s_sel[0] = 0u;
-    s_sel[1] = 0u;
-  }
   uint32_t all;
-  const uint32_t before = scan256(tot, sh, all);
-  if (before < need && before + tot >= need) {
+  // the barrier below the search closes the scan: `sh` is read before it
+  const uint32_t before = scan256<false>(tot, sh, all);
+  // need = 0, or a histogram holding fewer than `need` keys: bin 0, nothing
+  // above (no thread finds a bin); else exactly one thread finds it
+  const bool none = need == 0u || all < need;
+  if (!none && before < need && before + tot >= need) {
     uint32_t cum = before;
 #pragma unroll
     for (int i = 0; i < W; ++i) {
@@ -82,10 +114,11 @@ KC_INLINE uint32_t find_bin256_regs(const uint32_t (&h)[NB / kWideThreads], uint
     }
   }
   __syncthreads();
-  const uint32_t bin = s_sel[0];
-  above = s_sel[1];
-  __syncthreads();
-  return bin;
+  // No closing barrier: the next write of `s_sel` (by the next search's
+  // finder) comes after that search's scan barrier, which every thread
+  // reaches only after reading these two words here.
+  above = none ? 0u : s_sel[1];
+  return none ? 0u : s_sel[0];
 }
 
 template <int NB>

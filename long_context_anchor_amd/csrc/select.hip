@@ -461,18 +461,18 @@ __global__ __launch_bounds__(kWideThreads) void k_select_wide_b(const WideSelect
   const uint32_t b1 = find_bin256_regs<kHistBins>(h1, need, sh, s_sel, above);
   need -= above;
   const uint32_t p01 = (b0 << 11) | b1;
-  uint32_t ncand;
-  uint32_t run = scan256(csum, sh, ncand);
+  // the candidate counts' prefix, and the block total of the keys above b0
+  // in the chunks before chunk c
+  uint32_t run, abv_ex, ncand, above_before;
+  scan256x2(csum, abv, sh, run, abv_ex, ncand, above_before);
 #pragma unroll
   for (int u = 0; u < kMaxCh / kWideThreads; ++u) {
     const int i = tid * (kMaxCh / kWideThreads) + u;
     if (i < kMaxCh) cpre[i] = run;
     run += nc[u];
   }
-  uint32_t above_before;
-  scan256(abv, sh, above_before);   // total over the block: keys above b0 before chunk c
   for (int i = tid; i < 1024; i += kWideThreads) hist[i] = 0u;
-  __syncthreads();
+  __syncthreads();   // cpre and the cleared histogram
   for (uint32_t f = tid; f < ncand; f += kWideThreads) {
     int cc;
     const uint32_t key = flat_cand(a, row, CH, cpre, chunks, f, cc);
@@ -491,9 +491,8 @@ __global__ __launch_bounds__(kWideThreads) void k_select_wide_b(const WideSelect
     gtc += key > T ? 1u : 0u;
     eqc += key == T ? 1u : 0u;
   }
-  uint32_t gt_before, eq_before;
-  scan256(gtc, sh, gt_before);
-  scan256(eqc, sh, eq_before);
+  uint32_t gtc_ex, eqc_ex, gt_before, eq_before;
+  scan256x2(gtc, eqc, sh, gtc_ex, eqc_ex, gt_before, eq_before);   // block totals
   gt_before += above_before;
   uint32_t gt = 0, eq = 0;
 #pragma unroll
@@ -506,15 +505,17 @@ __global__ __launch_bounds__(kWideThreads) void k_select_wide_b(const WideSelect
   const uint32_t ex = scan256((gt << 16) | eq, sh, tot);
   uint32_t g2 = gt_before + (ex >> 16), e2 = eq_before + (ex & 0xFFFFu);
   int32_t* out = a.idx + (int64_t)row * a.idx_stride;
+  const uint32_t kk = (uint32_t)a.k;   // positions stay inside the row's k slots
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
     const int j = j0 + q;
     if (j < a.n) {
       if (key[q] > T) {
-        out[g2 + min(e2, need)] = j;
+        const uint32_t pos = g2 + min(e2, need);
+        if (pos < kk) out[pos] = j;
         ++g2;
       } else if (key[q] == T) {
-        if (e2 < need) out[g2 + e2] = j;
+        if (e2 < need && g2 + e2 < kk) out[g2 + e2] = j;
         ++e2;
       }
     }
