@@ -727,6 +727,35 @@ __global__ __launch_bounds__(kCombineThreads) void k_decode_combine(const Combin
                                       sl, so);
 }
 
+// (M, L) += (Mo, Lo) in the log2 domain: the larger maximum, the sums
+// rescaled to it.
+KC_INLINE void lse_merge(float& M, float& L, float Mo, float Lo) {
+  const float mn = fmaxf(M, Mo);
+  L = mn == kNegInf ? 0.f : fmaf(L, exp2f_fast(M - mn), Lo * exp2f_fast(Mo - mn));
+  M = mn;
+}
+
+// The (M, L) pairs of a wave's 64 lanes merged into lane 0 (the other lanes
+// end with partial merges): across the halves and the 16-lane rows with the
+// lane-swap instructions (both lanes of a pair see the lower lane's value
+// first), then inside each row with DPP mirrors and quad permutes.  No LDS.
+KC_INLINE void wave_lse_reduce(float& M, float& L) {
+  const auto m32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(M), __float_as_uint(M), false, false);
+  const auto l32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(L), __float_as_uint(L), false, false);
+  M = __uint_as_float(m32[0]);
+  L = __uint_as_float(l32[0]);
+  lse_merge(M, L, __uint_as_float(m32[1]), __uint_as_float(l32[1]));
+  const auto m16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(M), __float_as_uint(M), false, false);
+  const auto l16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(L), __float_as_uint(L), false, false);
+  M = __uint_as_float(m16[0]);
+  L = __uint_as_float(l16[0]);
+  lse_merge(M, L, __uint_as_float(m16[1]), __uint_as_float(l16[1]));
+  lse_merge(M, L, dpp_f<DPP_MIRROR>(M), dpp_f<DPP_MIRROR>(L));
+  lse_merge(M, L, dpp_f<DPP_HALF_MIRROR>(M), dpp_f<DPP_HALF_MIRROR>(L));
+  lse_merge(M, L, dpp_f<DPP_XOR2>(M), dpp_f<DPP_XOR2>(L));
+  lse_merge(M, L, dpp_f<DPP_XOR1>(M), dpp_f<DPP_XOR1>(L));
+}
+
 // Anchor pooling fused with the anchor pass's split merge (see
 // PoolDecodeArgs).  A pooling workgroup issues its 1024 keys' score loads for
 // the G heads of KV head g, merges the heads' lse from the splits' (m, l)
@@ -769,13 +798,7 @@ __global__ __launch_bounds__(256) void k_decode_pool(const PoolDecodeArgs a) {
           M = mn;
         }
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float Mo = __shfl_xor(M, o, 64), Lo = __shfl_xor(L, o, 64);
-        const float mn = fmaxf(M, Mo);
-        L = mn == kNegInf ? 0.f : fmaf(L, exp2f_fast(M - mn), Lo * exp2f_fast(Mo - mn));
-        M = mn;
-      }
+      wave_lse_reduce(M, L);
       if (lane == 0) s_lse[hh] = M + log2f_fast(L);
     }
   }
@@ -960,13 +983,7 @@ __global__ __launch_bounds__(kThreads) void k_anchor_fused(const FusedDecodeArgs
           M = mn;
         }
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float Mo = __shfl_xor(M, o, 64), Lo = __shfl_xor(L, o, 64);
-        const float mn = fmaxf(M, Mo);
-        L = mn == kNegInf ? 0.f : fmaf(L, exp2f_fast(M - mn), Lo * exp2f_fast(Mo - mn));
-        M = mn;
-      }
+      wave_lse_reduce(M, L);
       if (lane == 0) s_lse[hh] = M + log2f_fast(L);
     }
     for (int i = tid; i < NB; i += kThreads) s_hist[i] = 0u;
