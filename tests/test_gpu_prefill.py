@@ -96,15 +96,16 @@ def _check_anchor_prefill(q, k, v, tiles=None, heads_g=None):
     return out, idx, ref_idx
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,N", [(1, 4, 1, 128), (1, 8, 2, 300), (2, 4, 2, 640),
-                                        (1, 4, 4, 1000), (1, 16, 2, 2049)])
+@pytest.mark.parametrize("B,Hq,Hkv,N", [(1, 4, 1, 1), (2, 4, 2, 37), (1, 4, 1, 128), (1, 8, 2, 300),
+                                        (2, 4, 2, 640), (1, 4, 4, 1000), (1, 16, 2, 2049)])
 def test_anchor_prefill_parity(B, Hq, Hkv, N):
     say("anchor prefill", B, Hq, Hkv, N)
     q, k, v = _rand_layer(B, Hq, Hkv, N, seed=7 * N + Hq, planted=True)
     _check_anchor_prefill(q, k, v)
 
 
-@pytest.mark.parametrize("Hq,Hkv,N,hm", [(4, 1, 300, [0]), (8, 2, 1000, [1, 0]),
+@pytest.mark.parametrize("Hq,Hkv,N,hm", [(4, 2, 1, [1, 1]), (4, 2, 37, [1, 0]), (4, 1, 300, [0]),
+                                         (8, 2, 1000, [1, 0]),
                                          (8, 4, 2049, [2, 2, 0, 1]), (16, 2, 3000, [1, 1])])
 def test_reuse_prefill_parity(Hq, Hkv, N, hm):
     say("reuse prefill", Hq, Hkv, N, hm)
