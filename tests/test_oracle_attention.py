@@ -208,6 +208,49 @@ def test_sparse_prefill_full_lists_equal_dense():
     assert np.max(np.abs(sp - dense)) < 1e-12
 
 
+def test_anchor_and_reuse_prefill_layers_against_library_routines():
+    """One anchor prefill layer and the reuse layer that reads its lists
+    ([Explainer] "アンカーレイヤーと再利用レイヤー", "ヘッドリマッピング", "Top-k設定"
+    eq. k with the query tiles of "実装のポイント"): the anchor's output equals
+    causal torch SDPA and its lse the log of the causal row sums; its pooled
+    rows equal SDPA's probabilities summed over each tile's rows and the
+    group's heads; its lists are the k_t best keys of each pooled row by a
+    stable library sort (ties to the lower index), ascending, then -1 up to
+    k_max; the reuse layer equals SDPA under the boolean mask those lists and
+    the head map define.  Rule {tile 4, pct 50, round_to 2, k_min 4} on a
+    20-token prompt gives, by hand, P_t = 4, 8, 12, 16, 20 and k_t = 4, 4, 6,
+    8, 10 (k_min >= tile, so no reuse row is left without keys)."""
+    B, Hq, Hkv, d, N, tile = 1, 4, 2, 8, 20, 4
+    G = Hq // Hkv
+    want_k = [4, 4, 6, 8, 10]
+    q, k, v = _rand((B, Hq, N, d), 60), _rand((B, Hkv, N, d), 61), _rand((B, Hkv, N, d), 62)
+    out, lse, pooled, idx = oracle.anchor_prefill(q, k, v, tile=tile, pct=50, round_to=2, k_min=4)
+    assert np.max(np.abs(out - _sdpa(q, k, v, G, causal=True))) < 1e-12
+    s = np.einsum("bhnd,bhmd->bhnm", q, np.repeat(k, G, axis=1)) / math.sqrt(d)
+    s = np.where(np.tril(np.ones((N, N), dtype=bool)), s, -np.inf)
+    assert np.max(np.abs(lse - np.log(np.exp(s).sum(-1)))) < 1e-12
+    P = _sdpa(q, k, np.broadcast_to(np.eye(N), (B, Hkv, N, N)), G, causal=True)
+    assert idx.shape == (B, len(want_k), Hkv, want_k[-1])
+    for t, k_t in enumerate(want_k):
+        lo, hi = tile * t, tile * (t + 1)
+        for g in range(Hkv):
+            row = np.asarray(pooled[0][t][g])
+            assert np.max(np.abs(row - P[0, G * g:G * g + G, lo:hi, :hi].sum(axis=(0, 1)))) < 1e-12
+            best = np.argsort(-row, kind="stable")[:k_t]
+            assert idx[0, t, g, :k_t].tolist() == sorted(best.tolist()), (t, g)
+            assert (idx[0, t, g, k_t:] == -1).all(), (t, g)
+    q2, k2, v2 = _rand((B, Hq, N, d), 63), _rand((B, Hkv, N, d), 64), _rand((B, Hkv, N, d), 65)
+    head_map = [1, 0]
+    got = oracle.reuse_prefill(q2, k2, v2, idx, head_map, tile=tile)
+    mask = np.zeros((B, Hq, N, N), dtype=bool)
+    for h in range(Hq):
+        for r in range(N):
+            J = idx[0, r // tile, head_map[h // G]]
+            mask[0, h, r, J[(J >= 0) & (J <= r)]] = True
+    assert mask.any(axis=-1).all()
+    assert np.max(np.abs(got - _sdpa(q2, k2, v2, G, mask=mask))) < 1e-12
+
+
 def test_anchor_prefill_tiles_zero_and_one_are_dense():
     # with the prefill k rule (minimum 256, tile 128) tiles 0 and 1 keep every key
     for t, P in ((0, 128), (1, 256)):

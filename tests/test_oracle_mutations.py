@@ -317,6 +317,33 @@ def test_layer_stack_with_the_anchors_values_is_caught():
     check(STACK_PINS, run_decode_layerstack=_stack_variant(anchor_values=True))
 
 
+LAYER_PINS = [ta.test_anchor_and_reuse_prefill_layers_against_library_routines]
+
+
+def _anchor_prefill_variant(rule_ignored=False, pool_tile=None):
+    """anchor_prefill with one step changed."""
+    def anchor_prefill(q, k, v, tile=128, pct=10, round_to=64, k_min=256, scale=None):
+        out, lse = ko.dense_prefill(q, k, v, scale)
+        pooled = ko.tile_pool(q, k, pool_tile or tile, scale)
+        if rule_ignored:
+            pct, round_to, k_min = 10, 64, 256
+        return out, lse, pooled, ko.tile_topk(pooled, np.asarray(q).shape[2], tile, pct, round_to, k_min)
+    return anchor_prefill
+
+
+def test_anchor_prefill_ignoring_the_rule_is_caught():
+    check(LAYER_PINS, anchor_prefill=_anchor_prefill_variant(rule_ignored=True))
+
+
+def test_anchor_prefill_pooling_single_rows_is_caught():
+    check(LAYER_PINS, anchor_prefill=_anchor_prefill_variant(pool_tile=1))
+
+
+def test_reuse_prefill_ignoring_the_head_map_is_caught():
+    check(LAYER_PINS, reuse_prefill=lambda q, k, v, idx, head_map, tile=128, scale=None:
+          ko.sparse_prefill(q, k, v, idx, None, tile, scale))
+
+
 def test_every_planted_mistake_is_restored():
     for name, fn in ORIG.items():
         assert getattr(ko, name) is fn
