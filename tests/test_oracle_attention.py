@@ -208,6 +208,38 @@ def test_sparse_prefill_full_lists_equal_dense():
     assert np.max(np.abs(sp - dense)) < 1e-12
 
 
+def test_anchor_and_reuse_decode_layers_against_library_routines():
+    """One anchor decode layer and the reuse layer that reads its lists
+    ([Explainer] "アンカーレイヤーと再利用レイヤー", "ヘッドリマッピング"): the
+    anchor's output equals torch SDPA over all keys and its lse the log of the
+    row sums; its pooled row per KV head is SDPA's probabilities summed over
+    the group's heads; its list is the topk best keys of that row by a stable
+    library sort, ascending; the reuse layer equals SDPA under the boolean
+    mask of the remapped lists."""
+    B, Hq, Hkv, d, N, topk = 2, 6, 3, 8, 40, 7
+    G = Hq // Hkv
+    q, k, v = _rand((B, Hq, 1, d), 66), _rand((B, Hkv, N, d), 67), _rand((B, Hkv, N, d), 68)
+    out, lse, pooled, idx = oracle.anchor_decode(q[:, :, 0], k, v, topk)
+    assert np.max(np.abs(out - _sdpa(q, k, v, G)[:, :, 0])) < 1e-12
+    s = np.einsum("bhd,bhmd->bhm", q[:, :, 0], np.repeat(k, G, axis=1)) / math.sqrt(d)
+    assert np.max(np.abs(lse - np.log(np.exp(s).sum(-1)))) < 1e-12
+    P = _sdpa(q, k, np.broadcast_to(np.eye(N), (B, Hkv, N, N)), G)[:, :, 0]
+    assert idx.shape == (B, Hkv, topk)
+    for b in range(B):
+        for g in range(Hkv):
+            assert np.max(np.abs(pooled[b, g] - P[b, G * g:G * g + G].sum(axis=0))) < 1e-12
+            best = np.argsort(-pooled[b, g], kind="stable")[:topk]
+            assert idx[b, g].tolist() == sorted(best.tolist()), (b, g)
+    q2, k2, v2 = _rand((B, Hq, 1, d), 69), _rand((B, Hkv, N, d), 70), _rand((B, Hkv, N, d), 71)
+    head_map = [2, 0, 0]
+    got = oracle.reuse_decode(q2[:, :, 0], k2, v2, idx, head_map)
+    mask = np.zeros((B, Hq, 1, N), dtype=bool)
+    for b in range(B):
+        for h in range(Hq):
+            mask[b, h, 0, idx[b, head_map[h // G]]] = True
+    assert np.max(np.abs(got - _sdpa(q2, k2, v2, G, mask=mask)[:, :, 0])) < 1e-12
+
+
 def test_anchor_and_reuse_prefill_layers_against_library_routines():
     """One anchor prefill layer and the reuse layer that reads its lists
     ([Explainer] "アンカーレイヤーと再利用レイヤー", "ヘッドリマッピング", "Top-k設定"

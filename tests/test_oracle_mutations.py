@@ -318,6 +318,7 @@ def test_layer_stack_with_the_anchors_values_is_caught():
 
 
 LAYER_PINS = [ta.test_anchor_and_reuse_prefill_layers_against_library_routines]
+DECODE_LAYER_PINS = [ta.test_anchor_and_reuse_decode_layers_against_library_routines]
 
 
 def _anchor_prefill_variant(rule_ignored=False, pool_tile=None):
@@ -342,6 +343,11 @@ def test_anchor_prefill_pooling_single_rows_is_caught():
 def test_reuse_prefill_ignoring_the_head_map_is_caught():
     check(LAYER_PINS, reuse_prefill=lambda q, k, v, idx, head_map, tile=128, scale=None:
           ko.sparse_prefill(q, k, v, idx, None, tile, scale))
+
+
+def test_reuse_decode_ignoring_the_head_map_is_caught():
+    check(DECODE_LAYER_PINS, reuse_decode=lambda q, k, v, idx, head_map, scale=None:
+          ko.sparse_decode(q, k, v, idx, None, scale)[0])
 
 
 def test_every_planted_mistake_is_restored():
